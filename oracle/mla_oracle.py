@@ -1,0 +1,281 @@
+"""Plain fp64 CPU oracle for one MLA decode step.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` may import this module.  The HIP library never calls it and it
+shares no code, constants or helpers with ``head_latent_attention_16_amd``.
+
+What it computes, and where the pages say so
+--------------------------------------------
+Page abbreviations used in the citations below:
+
+* [MLA-struct]  "MLA模型结构详解：从公式到推理代码" (gentlecold.top) -- the
+  formal source: equations, data-flow chart, both inference branches and a
+  shape-by-shape worked decode step.
+* [MLA-visual]  "DeepSeek-V2 MLA" visual reading (syt-nju.github.io,
+  files/visual-reading/deepseek-v2-mla) -- method narrative and the per-token
+  cache-size table.
+* [KV-2026]     "MLA latent attention / KV cache" (ai.saiita.com.cn,
+  mla-latent-attention-kv-cache-2026) -- DeepSeek-V3 cache arithmetic.
+* [KV-slim]     "给 KV Cache 瘦身：MQA · GQA · MLA" (bilibili-notes) -- the
+  7B example and the 576-numbers / ~70 KB figure.
+
+The oracle deliberately takes the *un-absorbed* route ([MLA-struct], section
+"MLA 的核心结构"): the content keys and values of every cached token are
+materialised explicitly (k^C = W^UK c^KV, v^C = W^UV c^KV), the per-head query
+and key are the concatenations [q^C; RoPE(q^R)] and [k^C; k^R] with k^R shared
+by all heads ([MLA-struct], section "RoPE 为什么要解耦"), the score is their dot
+product times the softmax scale, the softmax is the textbook two-pass one, and
+the head output is the probability-weighted sum of the explicit values.  The
+absorbed route used by the GPU path is an exact re-association of this
+([MLA-struct], section "为什么矩阵吸收很关键", the two associativity identities),
+so the two must agree up to rounding.
+
+Readings of points the pages leave open (each is listed in the design doc too):
+
+* softmax scale = 1 / sqrt(d_h + d_R) applied to the sum of the content and
+  RoPE scores (the pages write "x scale" without a value);
+* RoPE is rotate-half with base 10000: theta_i = base^(-2 i / d_R), pairs
+  (i, i + d_R/2); angles pos * theta_i are formed in fp64;
+* the cache always holds the already-rotated k^R (the worked example writes the
+  RoPE'd k_pe into pe_cache);
+* no causal mask is applied: a single decode query sits at a position >= every
+  cached row, so the mask passes everything;
+* the latent ``norm(...)`` of the reference code path is not applied (its type
+  and epsilon are not stated; c^KV = W^DKV h_t is the equation's definition);
+* weights are [out, in] row-major: W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c],
+  W_UQ rows head-major with [d_h content | d_R rope] per head, W_O input index
+  h * d_v + v ("flatten head").
+
+Everything is float64.  Inputs given as bf16 bit patterns are widened exactly
+by the caller before they reach this module.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "rope",
+    "softmax_two_pass",
+    "explicit_kv",
+    "attend_explicit",
+    "decode_explicit",
+    "absorb_query",
+    "latent_attention",
+    "append_rows",
+    "query_path",
+    "project_out",
+    "layer_step",
+    "cache_elems_per_token_layer",
+    "cache_bytes_per_token",
+]
+
+
+# ---------------------------------------------------------------------------
+# RoPE on the decoupled positional part.
+# [MLA-visual], section on decoupled RoPE: the query RoPE part is per head,
+# the key RoPE part k^R = RoPE(W^KR h_t) is one vector shared by all heads.
+# Rotation convention (rotate-half, base 10000, fp64 angles) is a reading.
+# ---------------------------------------------------------------------------
+def rope(x: np.ndarray, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotate the last axis of ``x`` (length d_R, even) by position ``pos``.
+
+    x'_i        = x_i cos(pos*theta_i) - x_{i+d/2} sin(pos*theta_i)
+    x'_{i+d/2}  = x_{i+d/2} cos(pos*theta_i) + x_i sin(pos*theta_i)
+    theta_i     = base ** (-2 i / d),  i < d/2.
+    ``pos`` broadcasts against x.shape[:-1].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE dimension must be even")
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * i / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    cos, sin = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * cos - hi * sin, hi * cos + lo * sin], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Softmax: textbook two-pass form over the last axis.
+# [MLA-struct], worked example step 4: score -> (causal mask) -> softmax.
+# ---------------------------------------------------------------------------
+def softmax_two_pass(s: np.ndarray):
+    """Return (p, lse) with p = exp(s - max) / sum exp(s - max)."""
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=-1, keepdims=True)
+    p = e / z
+    lse = (m + np.log(z))[..., 0]
+    return p, lse
+
+
+# ---------------------------------------------------------------------------
+# The un-absorbed ("naive") route.
+# [MLA-struct], section "MLA 的核心结构": k^C_t = W^UK c^KV_t, v^C_t = W^UV c^KV_t;
+# section "RoPE 为什么要解耦": q_{t,i} = [q^C_{t,i}; q^R_{t,i}],
+# k_{t,i} = [k^C_{t,i}; k^R_t] with k^R_t shared by every head i.
+# ---------------------------------------------------------------------------
+def explicit_kv(c: np.ndarray, k_rot: np.ndarray, W_UK_h: np.ndarray, W_UV_h: np.ndarray):
+    """Explicit keys [T, d_h + d_R] and values [T, d_v] of one head."""
+    k_content = c @ W_UK_h.T          # k^C_j = W^UK c_j   -> [T, d_h]
+    v_content = c @ W_UV_h.T          # v^C_j = W^UV c_j   -> [T, d_v]
+    keys = np.concatenate([k_content, k_rot], axis=1)
+    return keys, v_content
+
+
+def attend_explicit(q_C_h, q_R_rot_h, c, k_rot, W_UK_h, W_UV_h, scale):
+    """One head, one query, explicit K/V.
+
+    Returns (o_h [d_v], o_lat_h [d_c], lse_h).  ``o_lat_h`` = sum_j p_j c_j is
+    the latent aggregate that W^UV maps to o_h ([MLA-struct], value identity);
+    it is returned so the GPU's latent output can be compared directly.
+    """
+    keys, values = explicit_kv(c, k_rot, W_UK_h, W_UV_h)
+    q = np.concatenate([q_C_h, q_R_rot_h])           # [d_h + d_R]
+    s = (keys @ q) * scale                            # [T]
+    p, lse = softmax_two_pass(s)
+    o_h = p @ values                                  # sum_j p_j v_j
+    o_lat_h = p @ c                                   # sum_j p_j c_j
+    return o_h, o_lat_h, float(lse)
+
+
+def decode_explicit(q_C, q_R, pos, c, k_rot, W_UK, W_UV, scale, base=10000.0):
+    """All heads of one sequence.
+
+    q_C [n_h, d_h], q_R [n_h, d_R] (not yet rotated), pos = query position,
+    c [T, d_c], k_rot [T, d_R] (rotated keys as cached), W_UK [n_h, d_h, d_c],
+    W_UV [n_h, d_v, d_c].  Returns o [n_h, d_v], o_lat [n_h, d_c], lse [n_h].
+    """
+    c = np.asarray(c, np.float64)
+    k_rot = np.asarray(k_rot, np.float64)
+    q_R_rot = rope(q_R, pos, base)
+    n_h = q_C.shape[0]
+    o = np.empty((n_h, W_UV.shape[1]))
+    o_lat = np.empty((n_h, c.shape[1]))
+    lse = np.empty(n_h)
+    for h in range(n_h):
+        o[h], o_lat[h], lse[h] = attend_explicit(
+            q_C[h], q_R_rot[h], c, k_rot, W_UK[h], W_UV[h], scale)
+    return o, o_lat, lse
+
+
+# ---------------------------------------------------------------------------
+# What the latent-space call computes, stated as its own definition:
+# o_lat[h] = sum_j softmax_j(scale (q_lat[h].c_j + q_pe[h].k^R_j)) c_j.
+# [MLA-struct], worked example steps 4-5 (score_C + score_R, z = A . kv_cache).
+# ---------------------------------------------------------------------------
+def absorb_query(q_C, W_UK):
+    """q_lat[h] = W_UK[h]^T q_C[h]  ([MLA-struct], key identity q.(W c) = (q W).c)."""
+    return np.einsum("hk,hkc->hc", np.asarray(q_C, np.float64), np.asarray(W_UK, np.float64))
+
+
+def latent_attention(q_lat, q_pe, c, k_rot, scale):
+    """o_lat [n_h, d_c] and lse [n_h] from latent queries (q_pe already rotated)."""
+    s = (np.asarray(q_lat, np.float64) @ np.asarray(c, np.float64).T
+         + np.asarray(q_pe, np.float64) @ np.asarray(k_rot, np.float64).T) * scale
+    p, lse = softmax_two_pass(s)
+    return p @ np.asarray(c, np.float64), lse
+
+
+# ---------------------------------------------------------------------------
+# New-token projections and the cache row.
+# [MLA-struct], section "MLA 的核心结构": c^KV_t = W^DKV h_t; c^Q_t = W^DQ h_t,
+# q^C_t = W^UQ c^Q_t; worked example steps 1-3 (q split per head into
+# [128 content | 64 rope]; kv_and_pe split into latent and k_pe; RoPE(k_pe);
+# write at index start_pos).
+# ---------------------------------------------------------------------------
+def append_rows(x, W_DKV, W_KR, pos, base=10000.0):
+    """Cache rows for new tokens: (c_new [n, d_c], k_rot [n, d_R]).
+
+    x [n, d_model] are the new tokens' hidden states, pos [n] their positions.
+    """
+    x = np.asarray(x, np.float64)
+    c_new = x @ np.asarray(W_DKV, np.float64).T
+    k_raw = x @ np.asarray(W_KR, np.float64).T
+    return c_new, rope(k_raw, np.asarray(pos), base)
+
+
+def query_path(h, W_DQ, W_UQ, n_h, d_h, d_r):
+    """q_C [n, n_h, d_h] and q_R [n, n_h, d_R] (un-rotated) from hidden states h [n, d].
+
+    With ``W_DQ`` None the query is projected directly (q = W_UQ h), as in a
+    configuration without query compression.
+    """
+    c_Q = np.asarray(h, np.float64)
+    if W_DQ is not None:
+        c_Q = c_Q @ np.asarray(W_DQ, np.float64).T
+    q = (c_Q @ np.asarray(W_UQ, np.float64).T).reshape(len(c_Q), n_h, d_h + d_r)
+    return q[..., :d_h], q[..., d_h:]
+
+
+# ---------------------------------------------------------------------------
+# Output side.  [MLA-struct], worked example step 5: o = W^UV z per head, then
+# flatten heads and apply the output projection W_O.
+# ---------------------------------------------------------------------------
+def project_out(o_lat, W_UV, W_O=None):
+    """o [B, n_h, d_v] = W_UV[h] o_lat[b, h];  u [B, d_model] = W_O flatten(o[b])."""
+    o_lat = np.asarray(o_lat, np.float64)
+    o = np.einsum("hvc,bhc->bhv", np.asarray(W_UV, np.float64), o_lat)
+    u = None
+    if W_O is not None:
+        u = o.reshape(o.shape[0], -1) @ np.asarray(W_O, np.float64).T
+    return o, u
+
+
+def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None):
+    """One full MLA decode layer step for selected sequences, explicit route.
+
+    h_t [B, d_model]; W: dict with W_DQ, W_UQ, W_DKV, W_KR, W_UK, W_UV, W_O;
+    prior_c[b] [T_b, d_c], prior_k[b] [T_b, d_R] (rotated).  The new token of
+    sequence b sits at position t_b = T_b: its row is appended at that index,
+    and the query uses the same position ([MLA-struct], worked example step 3:
+    write at start_pos, visible length start_pos + 1).
+    Returns dict of per-sequence results keyed by b.
+    """
+    n_h, d_h, d_r = dims["n_h"], dims["d_h"], dims["d_r"]
+    seqs = range(len(h_t)) if seqs is None else seqs
+    out = {}
+    for b in seqs:
+        x = np.asarray(h_t[b:b + 1], np.float64)
+        t = len(prior_c[b])
+        q_C, q_R = query_path(x, W["W_DQ"], W["W_UQ"], n_h, d_h, d_r)
+        c_new, k_new = append_rows(x, W["W_DKV"], W["W_KR"], [t], base)
+        c_all = np.concatenate([np.asarray(prior_c[b], np.float64), c_new])
+        k_all = np.concatenate([np.asarray(prior_k[b], np.float64), k_new])
+        o, o_lat, lse = decode_explicit(q_C[0], q_R[0], t, c_all, k_all,
+                                        W["W_UK"], W["W_UV"], scale, base)
+        u = o.reshape(1, -1) @ np.asarray(W["W_O"], np.float64).T
+        out[b] = dict(o=o, o_lat=o_lat, lse=lse, u=u[0], c_new=c_new[0], k_new=k_new[0],
+                      q_C=q_C[0], q_R=q_R[0])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Cache-size arithmetic.  [MLA-visual], cache-size table: MHA 2 n_h d_h l,
+# GQA 2 n_g d_h l, MQA 2 d_h l, MLA (d_c + d_h^R) l elements per token.
+# ---------------------------------------------------------------------------
+def cache_elems_per_token_layer(kind: str, n_h=None, d_h=None, n_g=None, d_c=None, d_r=None) -> int:
+    if kind == "mha":
+        return 2 * n_h * d_h
+    if kind == "gqa":
+        return 2 * n_g * d_h
+    if kind == "mqa":
+        return 2 * d_h
+    if kind == "mla":
+        return d_c + d_r
+    raise ValueError(kind)
+
+
+def cache_bytes_per_token(kind: str, layers: int, bytes_per_elem: int, **dims) -> int:
+    return layers * bytes_per_elem * cache_elems_per_token_layer(kind, **dims)
+
+
+def scale_for(d_h: int, d_r: int) -> float:
+    """Softmax scale reading: 1 / sqrt(d_h + d_R)."""
+    return 1.0 / math.sqrt(d_h + d_r)
