@@ -1,0 +1,247 @@
+"""Benchmark one MLA decode step on one MI355X through the C ABI.
+
+    python bench.py [--steps K] [--warmup W] [--workload uniform|ragged|long|layer]
+
+A step is one pass of the decode hot path over one batch:
+  attention-only workloads (uniform, ragged, long):
+      mla_absorb_q (q given) -> mla_decode_attn -> mla_project_out (o)
+  layer workload: mla_absorb_q (from h_t) -> mla_append_cache (from h_t)
+      -> mla_decode_attn -> mla_project_out (o and u)
+Inputs are seeded synthetic tensors of the DeepSeek-V3 shapes, resident in
+HBM before timing; several independent copies of all inputs are rotated so
+that consecutive steps do not hit in the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout (progress goes to stderr).  ``value`` is
+cache-tokens/s of the whole step; ``roofline`` is for the mla_decode_attn call
+(its three kernels: length scan, split attention, combine), timed with HIP
+events on the launch stream inside the timed loop.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode cache-tokens/s & HBM GB/s (% roofline), V3 dims, B×T at 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="uniform", choices=["uniform", "ragged", "long", "layer"])
+    p.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic(w):
+    """Bytes and FLOPs of one mla_decode_attn call (cache read once, q in, o_lat out)."""
+    n_h, d_c, d_r = w.dims["n_h"], w.dims["d_c"], w.dims["d_r"]
+    tokens = int(w.total_rows)
+    byts = tokens * (d_c + d_r) * 2 + w.B * n_h * (d_c + d_r) * 2 + w.B * n_h * d_c * 4
+    flops = tokens * 2 * n_h * ((d_c + d_r) + d_c)
+    return tokens, byts, flops
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle (explicit route) on whole sequences until the budget is used."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    d = w.dims
+    scale = O.scale_for(d["d_h"], d["d_r"])
+    W_UK, W_UV = w.f64(w.W["W_UK"]), w.f64(w.W["W_UV"])
+    done_tokens, heads_done, t0 = 0, 0, time.perf_counter()
+    b = 0
+    while time.perf_counter() - t0 < budget_s and b < w.B:
+        rows = w.f64(w.seq_rows(b))
+        c, kr = rows[:, :d["d_c"]], rows[:, d["d_c"]:]
+        if w.q_C is not None:
+            q_C, q_R, pos = w.f64(w.q_C[b]), w.f64(w.q_R[b]), int(w.lens[b])
+        else:
+            q_C, q_R = O.query_path(w.f64(w.h_t[b:b + 1]), w.f64(w.W["W_DQ"]), w.f64(w.W["W_UQ"]),
+                                    d["n_h"], d["d_h"], d["d_r"])
+            q_C, q_R, pos = q_C[0], q_R[0], int(w.lens[b])
+        # all heads of this sequence, one head at a time, stop at the budget
+        for h in range(d["n_h"]):
+            O.decode_explicit(q_C[h:h + 1], q_R[h:h + 1], pos, c, kr, W_UK[h:h + 1], W_UV[h:h + 1], scale)
+            heads_done += 1
+            done_tokens += len(rows)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        b += 1
+    dt = time.perf_counter() - t0
+    per_token_heads = done_tokens / d["n_h"]        # cache-tokens with all heads processed
+    return {"value": per_token_heads / dt, "unit": "cache-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 explicit route, {heads_done} (sequence, head) pairs over "
+                      f"{b} sequence(s) of the same workload in {dt:.1f} s; value = "
+                      f"head-weighted cache tokens / s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from head_latent_attention_16_amd import _lib as L
+    from head_latent_attention_16_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    name = args.workload
+    spare = args.warmup + args.steps + 2
+    log(f"generating workload {name} ...")
+    t0 = time.perf_counter()
+    w = I.layer(spare=spare) if name == "layer" else I.make(name)
+    log(f"  done in {time.perf_counter() - t0:.1f}s: B={w.B} total_rows={w.total_rows}")
+    d = w.dims
+    layer = name == "layer"
+    dims = L.Dims.make(d["n_h"], d["d_c"], d["d_r"], d["d_h"], d["d_v"], d_model=d["d_model"],
+                       d_q=d["d_q"], dtype="bf16")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = {"cache": dev(w.cache), "offsets": dev(w.offsets), "lens": dev(w.lens)}
+    for k, v in w.W.items():
+        base[k] = dev(v)
+    if layer:
+        base["h_t"] = dev(w.h_t)
+    else:
+        base["q"] = dev(np.ascontiguousarray(np.concatenate([w.q_C, w.q_R], -1)))
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    copies = args.copies or max(2, math.ceil(2.5 * MALL_BYTES / per_copy))
+    log(f"  {per_copy / 1e6:.1f} MB of inputs per copy, rotating {copies} copies")
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+
+    B, n_h = w.B, d["n_h"]
+    hint = int(w.total_rows) + (B if layer else 0)
+    q_lat = torch.empty(B, n_h, d["d_c"], dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(B, n_h, d["d_r"], dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty(B, n_h, d["d_c"], dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
+    o = torch.empty(B, n_h, d["d_v"], dtype=torch.float32, device="cuda")
+    u = torch.empty(B, d["d_model"], dtype=torch.float32, device="cuda") if layer else None
+    pos = [s["lens"].clone() for s in sets]
+    ws_dec = torch.empty(L.decode_attn_workspace(dims, B, hint), dtype=torch.uint8, device="cuda")
+    lib = L.lib()
+    import ctypes
+    ws_abs = torch.empty(max(1, lib.mla_absorb_q_workspace(ctypes.byref(dims), B, int(layer))),
+                         dtype=torch.uint8, device="cuda")
+    ws_app = torch.empty(max(1, lib.mla_append_cache_workspace(ctypes.byref(dims), B, 1, 1)),
+                         dtype=torch.uint8, device="cuda")
+    ws_prj = torch.empty(max(1, lib.mla_project_out_workspace(ctypes.byref(dims), B, int(layer))),
+                         dtype=torch.uint8, device="cuda")
+
+    ev = []
+
+    def step(i, timed):
+        s = sets[i % copies]
+        if layer:
+            pos[i % copies].copy_(s["lens"])   # query position = current length
+            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[i % copies], h_t=s["h_t"], W_DQ=s["W_DQ"],
+                       W_UQ=s["W_UQ"], ws=ws_abs)
+            L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
+                           W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
+        else:
+            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["lens"], q=s["q"])
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
+                      total_rows_hint=hint, ws=ws_dec)
+        if timed:
+            b.record()
+            ev.append((a, b))
+        if layer:
+            L.project_out(dims, o_lat, s["W_UV"], o=o, u=u, W_O=s["W_O"], ws=ws_prj)
+        else:
+            L.project_out(dims, o_lat, s["W_UV"], o=o)
+
+    log(f"warmup {args.warmup} steps ...")
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps ...")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    tokens, byts, flops = algorithmic(w)
+    if layer:
+        tokens += B * (args.warmup + args.steps // 2 + 1)     # rows grow by one per step
+    achieved = byts / (dec_ms * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode_attn {dec_ms * 1e3:.1f} us, {achieved:.0f} GB/s, "
+        f"{flops / (dec_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+    wl = {"uniform": f"uniform B={w.B} T={int(w.lens[0])}",
+          "ragged": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows}",
+          "long": f"long-context B={w.B} T={int(w.lens[0])}",
+          "layer": f"full layer step B={w.B} prior T~U[512,8192] sum={w.total_rows}"}[name]
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "cache-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl + " (DeepSeek-V3 dims n_h=128 d_c=512 d_R=64)",
+                   "B": w.B, "cache_tokens": tokens,
+                   "step": "absorb_q+append+decode_attn+project_out(o,u)" if layer
+                   else "absorb_q+decode_attn+project_out(o)",
+                   "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "mla_decode_attn (scan + split attention + combine)",
+                     "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
+                     "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"oracle baseline on the host ({args.cpu_seconds:.0f} s budget) ...")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,321 @@
+// C ABI of libmla.so: argument validation, workspace sizing and dispatch.
+// Every entry point checks its arguments before making any HIP call, so the
+// error paths can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/mla.h"
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+hipError_t g_info_err[kMaxDevices];
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// Host-side validation of the dimension record.  Returns MLA_OK or an error.
+mla_status_t check_dims(const mla_dims_t* d, Shape* s) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->dtype != MLA_DT_BF16 && d->dtype != MLA_DT_F32) return MLA_ERR_DTYPE;
+  if (d->n_h < 1 || d->d_c < 1 || d->d_r < 2 || (d->d_r & 1) || d->d_h < 1 || d->d_v < 1)
+    return MLA_ERR_SHAPE;
+  if (d->d_model < 0 || d->d_q < 0) return MLA_ERR_SHAPE;
+  if (!(d->rope_base > 0.f) || !isfinite(d->rope_base)) return MLA_ERR_SHAPE;
+  if (isnan(d->softmax_scale) || isinf(d->softmax_scale)) return MLA_ERR_SHAPE;
+  // Widths the kernels can hold: the generic decode keeps a row in 20
+  // registers per lane and the latent accumulator in 16.
+  if (d->d_c > 1024 || d->d_c + d->d_r > 1280) return MLA_ERR_SHAPE;
+  if (s) {
+    s->n_h = d->n_h;
+    s->d_c = d->d_c;
+    s->d_r = d->d_r;
+    s->d_h = d->d_h;
+    s->d_v = d->d_v;
+    s->d_model = d->d_model;
+    s->d_q = d->d_q;
+    s->rope_base = (double)d->rope_base;
+    s->scale = d->softmax_scale > 0.f ? d->softmax_scale
+                                      : (float)(1.0 / sqrt((double)(d->d_h + d->d_r)));
+    s->bf16 = d->dtype == MLA_DT_BF16;
+  }
+  return MLA_OK;
+}
+
+size_t elem_bytes(const Shape& s) { return s.bf16 ? 2 : 4; }
+
+mla_status_t device_ready(DeviceInfo* info) {
+  hipError_t e = current_device_info(info);
+  if (e != hipSuccess || !info->gfx950) return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
+mla_status_t launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+bool force_generic() { return env_flag("MLA_FORCE_GENERIC"); }
+
+// Workspace layouts (byte offsets, each region 256-aligned).
+size_t absorb_ws(const Shape& s, int B, bool from_hidden) {
+  if (!from_hidden) return 0;
+  size_t cq = s.d_q > 0 ? align256((size_t)B * s.d_q * sizeof(float)) : 0;
+  size_t q = align256((size_t)B * s.n_h * (s.d_h + s.d_r) * sizeof(float));
+  return cq + q;
+}
+size_t append_ws(const Shape& s, int B, int n_new, bool from_hidden) {
+  if (!from_hidden) return 0;
+  return align256((size_t)B * n_new * (s.d_c + s.d_r) * sizeof(float));
+}
+size_t project_ws(const Shape& s, int B, bool with_u) {
+  if (!with_u) return 0;
+  return align256((size_t)B * s.n_h * s.d_v * sizeof(float));
+}
+size_t decode_ws(const Shape& s, int B, int64_t hint, int num_cu) {
+  if (!force_generic() && decode_v3_supported(s)) return decode_v3_workspace(s, B, hint, num_cu);
+  return 0;
+}
+
+int num_cu_or_default() {
+  DeviceInfo info;
+  if (current_device_info(&info) == hipSuccess && info.num_cu > 0) return info.num_cu;
+  return 256;
+}
+
+}  // namespace
+
+hipError_t current_device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_once[dev], [dev]() {
+    hipDeviceProp_t p;
+    hipError_t err = hipGetDeviceProperties(&p, dev);
+    g_info_err[dev] = err;
+    if (err == hipSuccess) {
+      g_info[dev].device = dev;
+      g_info[dev].num_cu = p.multiProcessorCount;
+      g_info[dev].gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    }
+  });
+  if (g_info_err[dev] != hipSuccess) return g_info_err[dev];
+  *out = g_info[dev];
+  return hipSuccess;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size is out of range or the dims are unsupported";
+    case MLA_ERR_DTYPE: return "unknown element type";
+    case MLA_ERR_WORKSPACE: return "workspace smaller than required";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_DEVICE: return "no usable gfx950 device is current";
+  }
+  return "unknown status";
+}
+
+size_t mla_cache_row_bytes(const mla_dims_t* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK) return 0;
+  return (size_t)(s.d_c + s.d_r) * elem_bytes(s);
+}
+
+size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hidden) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK || B < 0) return 0;
+  return absorb_ws(s, B, from_hidden != 0);
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
+                          const void* W_UQ, const void* q, const void* W_UK, const int32_t* pos,
+                          void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!W_UK || !pos || !q_lat || !q_pe) return MLA_ERR_NULL;
+  const bool from_hidden = h_t != nullptr;
+  if (from_hidden) {
+    if (!W_UQ) return MLA_ERR_NULL;
+    if (s.d_model < 1) return MLA_ERR_SHAPE;
+    if ((s.d_q > 0) != (W_DQ != nullptr)) return s.d_q > 0 ? MLA_ERR_NULL : MLA_ERR_SHAPE;
+  } else if (!q) {
+    return MLA_ERR_NULL;
+  }
+  const size_t need = absorb_ws(s, B, from_hidden);
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  DeviceInfo info;
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+
+  // Inputs given in the storage type are fp32 exactly when the storage is fp32.
+  const bool storage_f32 = !s.bf16;
+  const void* qsrc = q;
+  bool q_f32 = storage_f32;
+  if (from_hidden) {
+    char* w = (char*)ws;
+    const int qw = s.n_h * (s.d_h + s.d_r);
+    const void* x = h_t;
+    bool x_f32 = storage_f32;
+    int K = s.d_model;
+    if (s.d_q > 0) {
+      float* cq = (float*)w;
+      w += align256((size_t)B * s.d_q * sizeof(float));
+      hipError_t e = launch_linear_generic(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, hs);
+      if (e != hipSuccess) return MLA_ERR_LAUNCH;
+      x = cq;
+      x_f32 = true;
+      K = s.d_q;
+    }
+    float* qf = (float*)w;
+    hipError_t e = launch_linear_generic(s, B, qw, K, x, x_f32, W_UQ, qf, hs);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+    qsrc = qf;
+    q_f32 = true;
+  }
+  return launched(launch_absorb_generic(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
+}
+
+size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_new,
+                                  int32_t from_hidden) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK || B < 0 || n_new < 0) return 0;
+  return append_ws(s, B, n_new, from_hidden != 0);
+}
+
+mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                              const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
+                              const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0 || n_new < 0) return MLA_ERR_SHAPE;
+  if (B == 0 || n_new == 0) return MLA_OK;
+  if (!cache || !offsets || !lens) return MLA_ERR_NULL;
+  const bool from_hidden = h_t != nullptr;
+  if (from_hidden) {
+    if (!W_DKV || !W_KR) return MLA_ERR_NULL;
+    if (s.d_model < 1) return MLA_ERR_SHAPE;
+  } else if (!kv_raw) {
+    return MLA_ERR_NULL;
+  }
+  const size_t need = append_ws(s, B, n_new, from_hidden);
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  DeviceInfo info;
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  const size_t D = (size_t)(s.d_c + s.d_r);
+  if (from_hidden) {
+    // c = x W_DKV^T and k = x W_KR^T into fp32 scratch, then rotate + write.
+    float* kc = (float*)ws;
+    const int M = B * n_new;
+    float* kr = kc + (size_t)M * s.d_c;
+    hipError_t e = launch_linear_generic(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, hs);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+    e = launch_linear_generic(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, hs);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+    return launched(launch_append_generic(s, B, n_new, kc, (size_t)s.d_c, kr, (size_t)s.d_r, true,
+                                          cache, offsets, lens, err_flag, hs));
+  }
+  const char* raw = (const char*)kv_raw;
+  // kv_raw is in the storage type: fp32 rows are read as fp32, bf16 rows as bf16.
+  return launched(launch_append_generic(s, B, n_new, raw, D, raw + (size_t)s.d_c * elem_bytes(s), D,
+                                        !s.bf16, cache, offsets, lens, err_flag, hs));
+}
+
+size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK || B < 0) return 0;
+  if (total_rows_hint < 1) total_rows_hint = 1;
+  return decode_ws(s, B, total_rows_hint, num_cu_or_default());
+}
+
+mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                             const void* q_pe, const void* cache, const int32_t* offsets,
+                             const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                             float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
+                             void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (total_rows_hint < 1) return MLA_ERR_SHAPE;
+  if (!q_lat || !q_pe || !cache || !offsets || !lens || !o_lat) return MLA_ERR_NULL;
+  DeviceInfo info;
+  const bool fast = !force_generic() && decode_v3_supported(s);
+  // The workspace requirement depends on the device's CU count; size it
+  // before touching the device only when the fast path needs it.
+  if (fast) {
+    if (!ws) return MLA_ERR_WORKSPACE;
+    if ((st = device_ready(&info)) != MLA_OK) return st;
+    const size_t need = decode_v3_workspace(s, B, total_rows_hint, info.num_cu);
+    if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+    return launched(launch_decode_v3(s, B, q_lat, q_pe, cache, offsets, lens, total_rows_hint,
+                                     o_lat, lse, err_flag, ws, ws_bytes, info.num_cu,
+                                     (hipStream_t)stream));
+  }
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  return launched(launch_decode_generic(s, B, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
+                                        err_flag, (hipStream_t)stream));
+}
+
+size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK || B < 0) return 0;
+  return project_ws(s, B, with_u != 0);
+}
+
+mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_lat,
+                             const void* W_UV, const void* W_O, float* o, float* u, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0) return MLA_ERR_SHAPE;
+  if (B == 0 || (!o && !u)) return MLA_OK;
+  if (!o_lat || !W_UV) return MLA_ERR_NULL;
+  if (u) {
+    if (!W_O) return MLA_ERR_NULL;
+    if (s.d_model < 1) return MLA_ERR_SHAPE;
+  }
+  const size_t need = (u && !o) ? project_ws(s, B, true) : 0;
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  DeviceInfo info;
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* ob = o ? o : (float*)ws;
+  hipError_t e = launch_uv_generic(s, B, o_lat, W_UV, ob, hs);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (u) {
+    e = launch_linear_generic(s, B, s.d_model, s.n_h * s.d_v, ob, true, W_O, u, hs);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

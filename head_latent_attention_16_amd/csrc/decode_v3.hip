@@ -1,0 +1,646 @@
+// Latent-space MLA decode attention for DeepSeek-V3 dims on gfx950.
+//
+// What is computed ("MLA模型结构详解：从公式到推理代码", worked example steps 4-5):
+//   s_j   = scale * (q_lat[h] . c_j + q_pe[h] . kR_j)          per head h, row j
+//   o_lat = sum_j softmax_j(s) c_j,  lse = log sum_j exp(s_j)
+// over the rows [c_j | kR_j] (512 + 64 bf16) of each sequence's cache region.
+//
+// Design (MI355X):
+// * The cache is read exactly once.  A workgroup owns a contiguous range of
+//   cache rows and ALL 128 heads: every 32-row tile is DMA'd from HBM into LDS
+//   once (global_load_lds_dwordx4, 16 B per lane) and then feeds both
+//   contractions of all four waves: S^T = K . Q^T (QK, 576-deep) and
+//   O^T += C^T . P^T (PV, over the tile's 32 rows, first 512 columns).
+// * Wave w owns heads 32w..32w+31.  Q (32 heads x 576 bf16) lives in VGPRs;
+//   the output accumulator O^T (512 cols x 32 heads fp32) lives in 16 MFMA
+//   32x32 tiles (256 accumulation registers per lane).
+// * Both contractions use v_mfma_f32_32x32x16_bf16.  QK reads row-major
+//   16-byte fragments; PV needs 8 rows of one column per lane and gets them
+//   with ds_read_b64_tr_b16 transpose reads from the same row-major tile.
+//   The PV reduction order over rows is permuted to match the accumulator
+//   layout of S, so P goes from the QK result to the PV operand in registers.
+// * LDS rows are 1152 B with 16-byte chunks XOR-swizzled per row so that the
+//   row-strided reads of both contractions are free of bank conflicts.
+// * Four LDS stages (144 KiB): tile i is multiplied by Q while tile i-1 feeds
+//   PV and tiles i+1, i+2 are in flight.  The QK chain of tile i is
+//   interleaved with the PV products of tile i-1, and the softmax of tile i
+//   overlaps the second half of them, so the matrix cores stay busy while
+//   the single wave per SIMD waits on LDS or runs VALU work.
+// * Softmax in base 2 against a per-piece reference max fixed by the piece's
+//   first tile: later scores may exceed it (p up to 2^64 stays far from fp32
+//   overflow), so the accumulator is never rescaled inside the loop -- the
+//   accumulators stay in AGPRs.  The final normalisation uses the same
+//   reference, so the result is exact.  If a later score exceeds the
+//   reference by more than 2^64 the piece is flagged and the combine kernel
+//   recomputes that sequence with a plain online-softmax loop.
+// * Split-T: the sum of all lengths is divided evenly over G workgroups
+//   (one per CU); a workgroup's range may cross sequence boundaries and emits
+//   one partial (O, m, l) per sequence piece; a combine kernel merges the
+//   pieces of each sequence by log-sum-exp.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int NH = 128;
+constexpr int DC = 512;
+constexpr int DR = 64;
+constexpr int DK = DC + DR;            // 576
+constexpr int ROWB = DK * 2;           // 1152 bytes per cache row
+constexpr int CHUNKS = ROWB / 16;      // 72
+constexpr int TILE = 32;               // rows per tile
+constexpr int TILEB = TILE * ROWB;     // 36864 bytes
+constexpr int NSTAGE = 4;
+constexpr int WAVES = 4;
+constexpr int THREADS = WAVES * 64;
+constexpr int DMA_PER_TILE = TILEB / 1024;            // 36 wave-instructions
+constexpr int DMA_PER_WAVE = DMA_PER_TILE / WAVES;    // 9
+constexpr int KSTEPS = DK / 16;                       // 36
+constexpr float OVF_TH = 64.0f;                       // log2 units
+constexpr int MIN_ROWS_PER_WG = 256;
+
+static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
+static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "uneven DMA split");
+
+// Partial record of one (workgroup, sequence) piece.
+struct PartialLayout {
+  size_t o_off;    // float [slots][NH][DC]
+  size_t ml_off;   // float [slots][NH][2]   (m in log2 units, l)
+  size_t pre_off;  // int64 [B + 1] prefix of valid lengths
+  size_t ovf_off;  // int32 [B] sequence needs the fallback recompute
+  size_t bytes;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline PartialLayout partial_layout(int B, int G) {
+  PartialLayout L;
+  size_t slots = (size_t)G + (size_t)B;   // slot = g + b  <  G + B - 1
+  L.pre_off = 0;
+  L.ovf_off = align256(sizeof(int64_t) * (B + 1));
+  L.o_off = L.ovf_off + align256(sizeof(int32_t) * B);
+  L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(float));
+  L.bytes = L.ml_off + align256(slots * NH * 2 * sizeof(float));
+  return L;
+}
+
+__device__ __forceinline__ int64_t range_start(int g, int64_t total, int G) {
+  return (int64_t)((int64_t)g * total) / G;
+}
+
+// Largest g in [0, G) with range_start(g) <= p (p < total).
+__device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
+  int g = (int)((p * (int64_t)G) / total);
+  if (g > G - 1) g = G - 1;
+  while (g + 1 < G && range_start(g + 1, total, G) <= p) ++g;
+  while (g > 0 && range_start(g, total, G) > p) --g;
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// Scheduler: validate lengths, prefix-sum the valid ones (invalid -> 0).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_sched(int B, const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ lens,
+                                                int64_t* __restrict__ prefix,
+                                                int32_t* __restrict__ ovf, int32_t* err_flag) {
+  __shared__ int64_t part[1024];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    int b = base + threadIdx.x;
+    int64_t v = 0;
+    if (b < B) {
+      int len = lens[b];
+      int cap = offsets[b + 1] - offsets[b];
+      if (len >= 1 && len <= cap) {
+        v = len;
+      } else if (err_flag) {
+        atomicOr(err_flag, MLA_DEVERR_LENS);
+      }
+    }
+    if (b < B) ovf[b] = 0;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      int64_t add = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += add;
+      __syncthreads();
+    }
+    int64_t c = carry;
+    if (b < B) prefix[b + 1] = c + part[threadIdx.x];   // inclusive
+    __syncthreads();
+    if (threadIdx.x == 1023) carry = c + part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) prefix[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel.
+// ---------------------------------------------------------------------------
+struct SplitArgs {
+  const __bf16* q_lat;
+  const __bf16* q_pe;
+  const char* cache;
+  const int32_t* offsets;
+  const int64_t* prefix;
+  int32_t* ovf;
+  float* part_o;
+  float* part_ml;
+  int B;
+  int G;
+  float scale_log2;
+};
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const char* base) {
+  // Direct global -> LDS: lane i's 16 bytes land at M0 + 16 i.  Issued from
+  // inline asm so that the compiler does not add a conservative vmcnt(0)
+  // before every LDS read (it cannot see which stage the DMA targets);
+  // completion is tracked by hand with s_waitcnt vmcnt before the barrier.
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier_all_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Bank swizzle of a 1152-byte row in LDS.  gfx950's LDS has 64 four-byte
+// banks; a 16-byte read by 16 lanes or an 8-byte read by 32 lanes is served in
+// one pass when the lanes hit 16 distinct 16-byte bank groups.  Row r starts
+// at bank group 8 r (mod 16), and its 16-byte chunk c is stored at
+// c ^ swz(r), swz = bit-reverse of bits 1..3 of r.  Then (a) 16 consecutive
+// rows at one chunk (the QK fragment read) and (b) 4 aligned rows x 4 aligned
+// chunks (one 32-lane half of a PV transpose read) cover 16 distinct groups.
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+}
+
+// S^T[32 rows x 32 heads] += K[rows, k-step kk] . Q^T[k-step kk, heads]
+#define QK_STEP(T, kk, S) \
+  S = __builtin_amdgcn_mfma_f32_32x32x16_bf16( \
+      *(const MLA_LDS bf16x8*)((T) + qk_off[(kk) & 3] + ((kk) >> 2) * 128), q[kk], S, 0, 0, 0)
+
+// O^T[cols 32cb.., 32 heads] += C^T[cols, rows of half kk2] . P^T[rows, heads]
+#define PV_STEP(T, kk2, cb, P) \
+  do { \
+    const MLA_LDS char* p0_ = (T) + tr_base[0][(cb) & 1] + (kk2) * 16 * ROWB + (cb) * 64; \
+    const MLA_LDS char* p1_ = (T) + tr_base[1][(cb) & 1] + (kk2) * 16 * ROWB + (cb) * 64; \
+    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0_); \
+    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1_); \
+    const bf16x8 cf_ = {lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]}; \
+    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf_, (P)[kk2], O[cb], 0, 0, 0); \
+  } while (0)
+
+__global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
+  // Per-lane DMA source offsets, kept in LDS rather than in 9 VGPRs.
+  __shared__ __attribute__((aligned(16))) uint32_t dma_tab[DMA_PER_WAVE / 4 * 4 + 4][THREADS];
+
+  const int g = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g32 = lane >> 5;          // which half of the wave
+  const int n32 = lane & 31;          // head within the wave's 32 / row within tile
+
+  const int64_t total = a.prefix[a.B];
+  if (total <= 0) return;
+  const int64_t start = range_start(g, total, a.G);
+  const int64_t end = range_start(g + 1, total, a.G);
+  if (start >= end) return;
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
+
+  // DMA mapping for full tiles: wave-instruction j = wave*9 + k covers LDS
+  // chunks [64 j, 64 j + 64); lane i fills chunk p = 64 j + i, which holds
+  // logical chunk (p % 72) ^ swz(row) of row p / 72.
+#pragma unroll
+  for (int k = 0; k < DMA_PER_WAVE; ++k) {
+    const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
+    const int r = p / CHUNKS;
+    const int c = (p % CHUNKS) ^ swz(r);
+    dma_tab[k][threadIdx.x] = (uint32_t)(r * ROWB + c * 16);
+  }
+  // (read back by each wave itself only: no barrier needed)
+
+  // QK fragment addresses: row n32, logical chunk 2kk + g32 stored at
+  // (2kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
+  // (2v + g32) ^ swz(n32); the rest is the constant 8u chunks.
+  uint32_t qk_off[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    qk_off[v] = (uint32_t)(n32 * ROWB + (((2 * v + g32) ^ swz(n32)) << 4));
+
+  // PV transpose-read addresses.  In each 16-lane group G (i = lane % 16),
+  // lane i reads 8 bytes of row 16 kk2 + 8 rd + rr, rr = 4 g32 + i/4, at
+  // columns 32 cb + 16 (G & 1) + 4 (i & 3); after the transpose lane j of the
+  // group holds column 32 cb + 16 (G & 1) + j for four consecutive rows.
+  // Logical chunk 4 cb + e sits at (4 cb + e) ^ swz(8 rd + rr)
+  //   = 4 (cb ^ bb) + (e ^ ff),  bb = bit 2 of swz, ff = its low two bits.
+  uint32_t tr_base[2][2];
+  {
+    const int Gq = lane >> 4;
+    const int i16 = lane & 15;
+    const int rr = 4 * g32 + (i16 >> 2);
+    const int e = 2 * (Gq & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int sw = swz(8 * rd + rr);
+      const int bb = sw >> 2, ff = sw & 3;
+      const uint32_t base = (uint32_t)((8 * rd + rr) * ROWB + ((e ^ ff) << 4) + 8 * (i16 & 1));
+      tr_base[rd][0] = base + (uint32_t)(bb << 6);   // cb even: cb ^ bb = cb + bb
+      tr_base[rd][1] = base - (uint32_t)(bb << 6);   // cb odd:  cb ^ bb = cb - bb
+    }
+  }
+
+  const int head = wave * 32 + n32;
+
+  // Find the first sequence touching [start, end).
+  int b;
+  {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.prefix[mid + 1] > start) hi = mid; else lo = mid + 1;
+    }
+    b = lo;
+  }
+
+  int64_t pos = start;
+  bool first_segment = true;
+  while (pos < end) {
+    while (a.prefix[b + 1] <= pos) ++b;
+    const int64_t seq_begin = a.prefix[b];
+    const int64_t seg_end = end < a.prefix[b + 1] ? end : a.prefix[b + 1];
+    const int t0 = (int)(pos - seq_begin);
+    const int seg_len = (int)(seg_end - pos);
+    const int ntiles = (seg_len + TILE - 1) / TILE;
+    const char* rows = a.cache + ((size_t)a.offsets[b] + (size_t)t0) * ROWB;
+
+    if (!first_segment) barrier_all_lds();   // previous segment's tiles fully consumed
+    first_segment = false;
+
+    // Q fragments for this sequence: B operand of QK (head n32, 8 features).
+    bf16x8 q[KSTEPS];
+    {
+      const bf16x8* ql = (const bf16x8*)(a.q_lat + ((size_t)b * NH + head) * DC);
+      const bf16x8* qp = (const bf16x8*)(a.q_pe + ((size_t)b * NH + head) * DR);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        q[kk] = kk < DC / 16 ? ql[2 * kk + g32] : qp[2 * (kk - DC / 16) + g32];
+    }
+
+    auto issue_tile = [&](int tile) {
+      const uint32_t stage_lds = lds0 + (uint32_t)((tile % NSTAGE) * TILEB);
+      const char* tbase = rows + (size_t)tile * TILEB;
+      const int nvalid = seg_len - tile * TILE;
+      uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+      for (int k = 0; k < DMA_PER_WAVE; ++k) dma_off[k] = dma_tab[k][threadIdx.x];
+      if (nvalid >= TILE) {
+#pragma unroll
+        for (int k = 0; k < DMA_PER_WAVE; ++k)
+          dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), dma_off[k], tbase);
+      } else {
+        // Partial tile (the last of a piece): rows nvalid..31 of the stage are
+        // zeroed (finite, and their scores are masked out), and only lanes
+        // whose chunk lies in a row below nvalid load -- chunk p is in row
+        // p / 72, so the test is the uniform bound p < 72 * nvalid.  No byte
+        // outside the sequence is read.  Such a tile may issue fewer than
+        // DMA_PER_WAVE instructions, so waits that precede it use vmcnt(0).
+        MLA_LDS char* st = (MLA_LDS char*)lds + (tile % NSTAGE) * TILEB;
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (int off = nvalid * ROWB + (int)threadIdx.x * 16; off < TILEB; off += THREADS * 16)
+          *(MLA_LDS floatx4*)(st + off) = zero;
+#pragma unroll
+        for (int k = 0; k < DMA_PER_WAVE; ++k) {
+          const int bound = nvalid * CHUNKS - (wave * DMA_PER_WAVE + k) * 64;
+          if (lane < bound)
+            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), dma_off[k], tbase);
+        }
+      }
+    };
+    const bool last_partial = (seg_len % TILE) != 0;
+    // Wait until tile `it` has landed in LDS (this wave's DMA), then barrier.
+    // Tile it + 1 may still be in flight unless it is a partial tile.
+    auto wait_tile = [&](int it) {
+      if (it + 1 < ntiles && !(it + 1 == ntiles - 1 && last_partial))
+        wait_vm_then_barrier<DMA_PER_WAVE>();
+      else
+        wait_vm_then_barrier<0>();
+    };
+
+    // Tile `it` lives in stage it % NSTAGE.  While tile it is multiplied by
+    // Q, tile it-1 is still needed for its PV product, and tiles it+1 and
+    // it+2 are in flight: four stages.
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+
+    floatx16 O[DC / 32];
+#pragma unroll
+    for (int cb = 0; cb < DC / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
+    float m_ref;               // reference max of scaled scores (log2 units)
+    float l_run = 0.f;         // this lane's share of the sum of weights
+    bf16x8 P[2];               // weights of the previous tile (PV operand)
+
+    // Softmax of one tile's scores into bf16 weights; lane holds head n32 and
+    // rows 8 (i/4) + 4 g32 + i%4.  One separately rounded product per score
+    // feeds both the max and the exponent, so the maximal score gets exactly
+    // exp2(0) = 1; l sums the same bf16-rounded weights that enter PV, so
+    // O / l is an exactly normalised average of the rows.
+    auto softmax = [&](floatx16& S, int nvalid, bf16x8* Pn) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * g32 + (i & 3);
+        const float x = __fmul_rn(S[i], a.scale_log2);
+        S[i] = row < nvalid ? x : -INFINITY;
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(S[i] - m_ref);
+        lsum += (float)pb;
+        Pn[i >> 3][i & 7] = pb;
+      }
+      l_run += lsum;
+    };
+
+    // ---- tile 0: QK, reference max, weights ----
+    {
+      wait_tile(0);
+      if (ntiles > 2) issue_tile(2);
+      const MLA_LDS char* T = (const MLA_LDS char*)lds;
+      floatx16 S;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) QK_STEP(T, kk, S);
+      const int nvalid = seg_len;
+      float smax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * g32 + (i & 3);
+        smax = fmaxf(smax, row < nvalid ? S[i] : -INFINITY);
+      }
+      const float mloc = __fmul_rn(smax, a.scale_log2);
+      m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      softmax(S, nvalid, P);
+    }
+
+    // ---- steady state: QK(it) and the first half of PV(it-1) interleaved,
+    //      then softmax(it) overlapping the second half of PV(it-1) ----
+    for (int it = 1; it < ntiles; ++it) {
+      wait_tile(it);
+      if (it + 2 < ntiles) issue_tile(it + 2);
+      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
+      const MLA_LDS char* Tp = (const MLA_LDS char*)lds + ((it - 1) % NSTAGE) * TILEB;
+      floatx16 S;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] = 0.f;
+      // 36 QK steps against the first 16 PV steps (kk2 = 0: cb 0..15)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        QK_STEP(T, kk, S);
+        if (kk < 32 && (kk & 1) == 0) PV_STEP(Tp, 0, kk >> 1, P);
+      }
+      bf16x8 Pn[2];
+      const int nvalid = seg_len - it * TILE;
+      softmax(S, nvalid, Pn);
+      // second half of PV(it-1): kk2 = 1
+#pragma unroll
+      for (int cb = 0; cb < DC / 32; ++cb) PV_STEP(Tp, 1, cb, P);
+      P[0] = Pn[0];
+      P[1] = Pn[1];
+      // Overflow guard: a score far above the reference max flags the sequence.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      if (__any(mx > m_ref + OVF_TH)) {
+        if (lane == 0) a.ovf[b] = 1;
+      }
+    }
+
+    // ---- PV of the last tile ----
+    {
+      const MLA_LDS char* Tp = (const MLA_LDS char*)lds + ((ntiles - 1) % NSTAGE) * TILEB;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+        for (int cb = 0; cb < DC / 32; ++cb) PV_STEP(Tp, kk2, cb, P);
+    }
+
+    // ---- emit the partial (unnormalised O, m, l) of this piece ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const size_t slot = (size_t)g + (size_t)b;
+    float* po = a.part_o + (slot * NH + head) * DC;
+#pragma unroll
+    for (int cb = 0; cb < DC / 32; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        floatx4 v = {O[cb][4 * q4 + 0], O[cb][4 * q4 + 1], O[cb][4 * q4 + 2], O[cb][4 * q4 + 3]};
+        *(floatx4*)(po + 32 * cb + 8 * q4 + 4 * g32) = v;
+      }
+    if (g32 == 0) {
+      float* pm = a.part_ml + (slot * NH + head) * 2;
+      pm[0] = m_ref;
+      pm[1] = l_tot;
+    }
+    pos = seg_end;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: merge the pieces of each (sequence, head) by log-sum-exp.
+// ---------------------------------------------------------------------------
+struct CombineArgs {
+  const __bf16* q_lat;
+  const __bf16* q_pe;
+  const __bf16* cache;
+  const int32_t* offsets;
+  const int64_t* prefix;
+  const int32_t* ovf;
+  const float* part_o;
+  const float* part_ml;
+  float* o_lat;
+  float* lse;
+  int B;
+  int G;
+  float scale_log2;
+};
+
+// Fallback for a flagged sequence: a plain online softmax over all its rows
+// (two waves, alternate rows, 64 lanes across the 576 features, running max
+// with rescale), then the two wave states are merged.
+__device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
+  __shared__ float st_m[2], st_l[2];
+  __shared__ float st_o[2][DC];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float q[DK / 64];
+#pragma unroll
+  for (int k = 0; k < DK / 64; ++k) {
+    const int f = lane + 64 * k;
+    q[k] = f < DC ? (float)a.q_lat[((size_t)b * NH + h) * DC + f]
+                  : (float)a.q_pe[((size_t)b * NH + h) * DR + (f - DC)];
+  }
+  float acc[DC / 64];
+#pragma unroll
+  for (int k = 0; k < DC / 64; ++k) acc[k] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const __bf16* rows = a.cache + (size_t)a.offsets[b] * DK;
+  for (int j = wave; j < len; j += 2) {
+    const __bf16* r = rows + (size_t)j * DK;
+    float sdot = 0.f;
+#pragma unroll
+    for (int k = 0; k < DK / 64; ++k) sdot += q[k] * (float)r[lane + 64 * k];
+    const float x = wave_sum(sdot) * a.scale_log2;
+    const float mn = fmaxf(m, x);
+    const float al = exp2f(m - mn);
+    const float p = exp2f(x - mn);
+    l = l * al + p;
+#pragma unroll
+    for (int k = 0; k < DC / 64; ++k) acc[k] = acc[k] * al + p * (float)r[lane + 64 * k];
+    m = mn;
+  }
+  if (lane == 0) { st_m[wave] = m; st_l[wave] = l; }
+#pragma unroll
+  for (int k = 0; k < DC / 64; ++k) st_o[wave][lane + 64 * k] = acc[k];
+  __syncthreads();
+  const float M = fmaxf(st_m[0], st_m[1]);
+  const float w0 = st_m[0] == -INFINITY ? 0.f : exp2f(st_m[0] - M);
+  const float w1 = st_m[1] == -INFINITY ? 0.f : exp2f(st_m[1] - M);
+  const float L = st_l[0] * w0 + st_l[1] * w1;
+  float* out = a.o_lat + ((size_t)b * NH + h) * DC;
+  for (int c = threadIdx.x; c < DC; c += blockDim.x) out[c] = (st_o[0][c] * w0 + st_o[1][c] * w1) / L;
+  if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
+}
+
+__global__ void __launch_bounds__(128) k_combine(CombineArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t total = a.prefix[a.B];
+  const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
+  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + h) * DC);
+  if (p1 <= p0) {   // invalid length: NaN result (the error flag is set)
+    const float nan = __builtin_nanf("");
+    out[threadIdx.x] = make_float4(nan, nan, nan, nan);
+    if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = nan;
+    return;
+  }
+  if (a.ovf[b]) {
+    recompute_head(a, b, h, (int)(p1 - p0));
+    return;
+  }
+  const int G = a.G;
+  const int g_lo = wg_of(p0, total, G);
+  const int g_hi = wg_of(p1 - 1, total, G);
+  float M = -INFINITY;
+  for (int g = g_lo; g <= g_hi; ++g) {
+    if (range_start(g, total, G) == range_start(g + 1, total, G)) continue;
+    M = fmaxf(M, a.part_ml[(((size_t)g + b) * NH + h) * 2]);
+  }
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = g_lo; g <= g_hi; ++g) {
+    if (range_start(g, total, G) == range_start(g + 1, total, G)) continue;
+    const size_t slot = (size_t)g + b;
+    const float m = a.part_ml[(slot * NH + h) * 2];
+    const float l = a.part_ml[(slot * NH + h) * 2 + 1];
+    const float w = exp2f(m - M);
+    L += l * w;
+    const float4 v = ((const float4*)(a.part_o + (slot * NH + h) * DC))[threadIdx.x];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = 1.f / L;
+  out[threadIdx.x] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
+}
+
+int choose_groups(int64_t total_rows_hint, int num_cu) {
+  int64_t g = (total_rows_hint + MIN_ROWS_PER_WG - 1) / MIN_ROWS_PER_WG;
+  if (g < 1) g = 1;
+  if (g > num_cu) g = num_cu;
+  return (int)g;
+}
+
+}  // namespace
+
+bool decode_v3_supported(const Shape& s) {
+  return s.bf16 && s.n_h == NH && s.d_c == DC && s.d_r == DR;
+}
+
+size_t decode_v3_workspace(const Shape&, int B, int64_t total_rows_hint, int num_cu) {
+  return partial_layout(B, choose_groups(total_rows_hint, num_cu)).bytes;
+}
+
+hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void* q_pe,
+                            const void* cache, const int32_t* offsets, const int32_t* lens,
+                            int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
+                            void* ws, size_t, int num_cu, hipStream_t st) {
+  const int G = choose_groups(total_rows_hint, num_cu);
+  const PartialLayout L = partial_layout(B, G);
+  char* w = (char*)ws;
+  int64_t* prefix = (int64_t*)(w + L.pre_off);
+  int32_t* ovf = (int32_t*)(w + L.ovf_off);
+  k_sched<<<1, 1024, 0, st>>>(B, offsets, lens, prefix, ovf, err_flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SplitArgs a;
+  a.q_lat = (const __bf16*)q_lat;
+  a.q_pe = (const __bf16*)q_pe;
+  a.cache = (const char*)cache;
+  a.offsets = offsets;
+  a.prefix = prefix;
+  a.ovf = ovf;
+  a.part_o = (float*)(w + L.o_off);
+  a.part_ml = (float*)(w + L.ml_off);
+  a.B = B;
+  a.G = G;
+  a.scale_log2 = s.scale * kLog2e;
+  k_split<<<G, THREADS, 0, st>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CombineArgs c;
+  c.q_lat = a.q_lat;
+  c.q_pe = a.q_pe;
+  c.cache = (const __bf16*)cache;
+  c.offsets = offsets;
+  c.prefix = prefix;
+  c.ovf = ovf;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  c.o_lat = o_lat;
+  c.lse = lse;
+  c.B = B;
+  c.G = G;
+  c.scale_log2 = a.scale_log2;
+  k_combine<<<dim3(NH, B), 128, 0, st>>>(c);
+  return hipGetLastError();
+}
+
+}  // namespace mla

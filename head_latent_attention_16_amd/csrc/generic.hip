@@ -1,0 +1,283 @@
+// Generic MLA kernels: any head count and widths, fp32 or bf16 storage, fp32
+// arithmetic.  They serve the small fp32 configuration and any dims the MFMA
+// fast path does not cover; they favour obviousness over speed.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kMaxRowPerLane = 20;   // (d_c + d_r) <= 64 * 20 = 1280
+constexpr int kMaxLatPerLane = 16;   // d_c <= 1024
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i) { return to_f32(p[i]); }
+__device__ __forceinline__ float ld_any(const void* p, bool f32, size_t i) {
+  return f32 ? ((const float*)p)[i] : (float)((const __bf16*)p)[i];
+}
+
+// Y[m, n] = sum_k X[m, k] W[n, k].  One wave per (n, group of 8 rows m).
+template <typename T>
+__global__ void __launch_bounds__(64) k_linear(int M, int N, int K, const void* X, bool x_f32,
+                                               const T* __restrict__ W, float* __restrict__ Y) {
+  const int n = blockIdx.x;
+  const int m0 = blockIdx.y * 8;
+  const int lane = threadIdx.x;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  const T* w = W + (size_t)n * K;
+  for (int k = lane; k < K; k += 64) {
+    float wk = ld(w, k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (m0 + i < M) acc[i] += wk * ld_any(X, x_f32, (size_t)(m0 + i) * K + k);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = wave_sum(acc[i]);
+    if (lane == 0 && m0 + i < M) Y[(size_t)(m0 + i) * N + n] = v;
+  }
+}
+
+// q_lat[b,h,c] = sum_k qC[b,h,k] W_UK[h,k,c];  q_pe = RoPE(qR, pos[b]).
+template <typename T>
+__global__ void __launch_bounds__(256) k_absorb(int n_h, int d_c, int d_r, int d_h, double base,
+                                                const void* q, bool q_f32, const T* __restrict__ W_UK,
+                                                const int32_t* __restrict__ pos, T* __restrict__ q_lat,
+                                                T* __restrict__ q_pe) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t qrow = ((size_t)b * n_h + h) * (d_h + d_r);
+  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
+    float acc = 0.f;
+    for (int k = 0; k < d_h; ++k)
+      acc += ld_any(q, q_f32, qrow + k) * ld(W_UK, ((size_t)h * d_h + k) * d_c + c);
+    q_lat[((size_t)b * n_h + h) * d_c + c] = from_f32<T>(acc);
+  }
+  const int half = d_r / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    float cs, sn;
+    rope_cos_sin(pos[b], i, d_r, base, &cs, &sn);
+    float lo = ld_any(q, q_f32, qrow + d_h + i);
+    float hi = ld_any(q, q_f32, qrow + d_h + half + i);
+    T* out = q_pe + ((size_t)b * n_h + h) * d_r;
+    out[i] = from_f32<T>(lo * cs - hi * sn);
+    out[half + i] = from_f32<T>(hi * cs + lo * sn);
+  }
+}
+
+// One block per sequence: writes its n_new rows, then bumps lens[b].  Row
+// i of sequence b takes c from c_src + (b*n_new + i)*c_stride and the
+// un-rotated k from k_src + (b*n_new + i)*k_stride.
+template <typename T>
+__global__ void __launch_bounds__(256) k_append(int n_new, int d_c, int d_r, double base,
+                                                const void* c_src, size_t c_stride,
+                                                const void* k_src, size_t k_stride, bool src_f32,
+                                                T* __restrict__ cache,
+                                                const int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ lens, int32_t* err_flag) {
+  const int b = blockIdx.x;
+  const int D = d_c + d_r;
+  const int len = lens[b];
+  const int off = offsets[b];
+  const int cap = offsets[b + 1] - off;
+  if (len < 0 || (int64_t)len + n_new > (int64_t)cap) {
+    if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, MLA_DEVERR_OVERFLOW);
+    return;
+  }
+  const int half = d_r / 2;
+  for (int i = 0; i < n_new; ++i) {
+    const size_t idx = (size_t)b * n_new + i;
+    const size_t cs = idx * c_stride, ks = idx * k_stride;
+    T* dst = cache + (size_t)(off + len + i) * D;
+    for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
+      if (src_f32)
+        dst[c] = from_f32<T>(((const float*)c_src)[cs + c]);
+      else
+        dst[c] = ((const T*)c_src)[cs + c];   // bit-exact copy
+    }
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+      float cn, sn;
+      rope_cos_sin((int64_t)len + i, j, d_r, base, &cn, &sn);
+      float lo = ld_any(k_src, src_f32, ks + j);
+      float hi = ld_any(k_src, src_f32, ks + half + j);
+      dst[d_c + j] = from_f32<T>(lo * cn - hi * sn);
+      dst[d_c + half + j] = from_f32<T>(hi * cn + lo * sn);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) lens[b] = len + n_new;
+}
+
+// One block (4 waves) per (head, sequence).  Each wave streams every 4th row,
+// keeps an online softmax (running max m, sum l, accumulator), and the four
+// partial states are merged through LDS at the end.
+template <typename T>
+__global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, float scale_log2,
+                                                const T* __restrict__ q_lat, const T* __restrict__ q_pe,
+                                                const T* __restrict__ cache,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ lens,
+                                                float* __restrict__ o_lat, float* __restrict__ lse,
+                                                int32_t* err_flag) {
+  extern __shared__ float smem[];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int D = d_c + d_r;
+  const int len = lens[b];
+  const int off = offsets[b];
+  const int cap = offsets[b + 1] - off;
+  float* out = o_lat + ((size_t)b * n_h + h) * d_c;
+  if (len < 1 || len > cap) {
+    for (int c = threadIdx.x; c < d_c; c += blockDim.x) out[c] = __builtin_nanf("");
+    if (threadIdx.x == 0) {
+      if (lse) lse[(size_t)b * n_h + h] = __builtin_nanf("");
+      if (err_flag) atomicOr(err_flag, MLA_DEVERR_LENS);
+    }
+    return;
+  }
+  float q[kMaxRowPerLane];
+#pragma unroll
+  for (int k = 0; k < kMaxRowPerLane; ++k) {
+    int f = lane + 64 * k;
+    float v = 0.f;
+    if (f < d_c) v = ld(q_lat, ((size_t)b * n_h + h) * d_c + f);
+    else if (f < D) v = ld(q_pe, ((size_t)b * n_h + h) * d_r + (f - d_c));
+    q[k] = v;
+  }
+  float acc[kMaxLatPerLane];
+#pragma unroll
+  for (int k = 0; k < kMaxLatPerLane; ++k) acc[k] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int j = wave; j < len; j += nw) {
+    const T* row = cache + (size_t)(off + j) * D;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxRowPerLane; ++k) {
+      int f = lane + 64 * k;
+      if (f < D) s += q[k] * ld(row, f);
+    }
+    s = wave_sum(s) * scale_log2;
+    float mn = fmaxf(m, s);
+    float a = exp2f(m - mn);
+    float p = exp2f(s - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int k = 0; k < kMaxLatPerLane; ++k) {
+      int f = lane + 64 * k;
+      if (f < d_c) acc[k] = acc[k] * a + p * ld(row, f);
+    }
+    m = mn;
+  }
+  // merge the waves' states
+  float* sm = smem;                         // [nw]
+  float* sl = smem + nw;                    // [nw]
+  float* sacc = smem + 2 * nw;              // [nw][d_c]
+  if (lane == 0) { sm[wave] = m; sl[wave] = l; }
+#pragma unroll
+  for (int k = 0; k < kMaxLatPerLane; ++k) {
+    int f = lane + 64 * k;
+    if (f < d_c) sacc[wave * d_c + f] = acc[k];
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, sm[w]);
+  float L = 0.f;
+  for (int w = 0; w < nw; ++w) L += (sm[w] == -INFINITY) ? 0.f : sl[w] * exp2f(sm[w] - M);
+  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w)
+      if (sm[w] != -INFINITY) v += sacc[w * d_c + c] * exp2f(sm[w] - M);
+    out[c] = v / L;
+  }
+  if (threadIdx.x == 0 && lse) lse[(size_t)b * n_h + h] = (M + log2f(L)) * kLn2;
+}
+
+// o[b,h,v] = sum_c W_UV[h,v,c] o_lat[b,h,c]; one wave per (v-group of 4, h, b).
+template <typename T>
+__global__ void __launch_bounds__(64) k_uv(int n_h, int d_c, int d_v, const float* __restrict__ o_lat,
+                                           const T* __restrict__ W_UV, float* __restrict__ o) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const float* x = o_lat + ((size_t)b * n_h + h) * d_c;
+  for (int vi = 0; vi < 4; ++vi) {
+    int v = blockIdx.x * 4 + vi;
+    if (v >= d_v) break;
+    const T* w = W_UV + ((size_t)h * d_v + v) * d_c;
+    float acc = 0.f;
+    for (int c = lane; c < d_c; c += 64) acc += ld(w, c) * x[c];
+    acc = wave_sum(acc);
+    if (lane == 0) o[((size_t)b * n_h + h) * d_v + v] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_generic(const Shape& s, int M, int N, int K, const void* X, bool x_f32,
+                                 const void* W, float* Y, hipStream_t st) {
+  dim3 grid(N, (M + 7) / 8);
+  if (s.bf16)
+    k_linear<__bf16><<<grid, 64, 0, st>>>(M, N, K, X, x_f32, (const __bf16*)W, Y);
+  else
+    k_linear<float><<<grid, 64, 0, st>>>(M, N, K, X, x_f32, (const float*)W, Y);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_generic(const Shape& s, int B, const void* q, bool q_f32, const void* W_UK,
+                                 const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st) {
+  dim3 grid(s.n_h, B);
+  if (s.bf16)
+    k_absorb<__bf16><<<grid, 256, 0, st>>>(s.n_h, s.d_c, s.d_r, s.d_h, s.rope_base, q, q_f32,
+                                           (const __bf16*)W_UK, pos, (__bf16*)q_lat, (__bf16*)q_pe);
+  else
+    k_absorb<float><<<grid, 256, 0, st>>>(s.n_h, s.d_c, s.d_r, s.d_h, s.rope_base, q, q_f32,
+                                          (const float*)W_UK, pos, (float*)q_lat, (float*)q_pe);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c_src,
+                                 size_t c_stride, const void* k_src, size_t k_stride, bool src_f32,
+                                 void* cache, const int32_t* offsets, int32_t* lens,
+                                 int32_t* err_flag, hipStream_t st) {
+  if (s.bf16)
+    k_append<__bf16><<<B, 256, 0, st>>>(n_new, s.d_c, s.d_r, s.rope_base, c_src, c_stride, k_src,
+                                        k_stride, src_f32, (__bf16*)cache, offsets, lens, err_flag);
+  else
+    k_append<float><<<B, 256, 0, st>>>(n_new, s.d_c, s.d_r, s.rope_base, c_src, c_stride, k_src,
+                                       k_stride, src_f32, (float*)cache, offsets, lens, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_generic(const Shape& s, int B, const void* q_lat, const void* q_pe,
+                                 const void* cache, const int32_t* offsets, const int32_t* lens,
+                                 float* o_lat, float* lse, int32_t* err_flag, hipStream_t st) {
+  const int threads = 256, nw = threads / 64;
+  size_t smem = sizeof(float) * (2 * nw + (size_t)nw * s.d_c);
+  dim3 grid(s.n_h, B);
+  float sl2 = s.scale * kLog2e;
+  if (s.bf16)
+    k_decode<__bf16><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, sl2, (const __bf16*)q_lat,
+                                                  (const __bf16*)q_pe, (const __bf16*)cache, offsets,
+                                                  lens, o_lat, lse, err_flag);
+  else
+    k_decode<float><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, sl2, (const float*)q_lat,
+                                                 (const float*)q_pe, (const float*)cache, offsets,
+                                                 lens, o_lat, lse, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
+                             hipStream_t st) {
+  dim3 grid((s.d_v + 3) / 4, s.n_h, B);
+  if (s.bf16)
+    k_uv<__bf16><<<grid, 64, 0, st>>>(s.n_h, s.d_c, s.d_v, o_lat, (const __bf16*)W_UV, o);
+  else
+    k_uv<float><<<grid, 64, 0, st>>>(s.n_h, s.d_c, s.d_v, o_lat, (const float*)W_UV, o);
+  return hipGetLastError();
+}
+
+}  // namespace mla

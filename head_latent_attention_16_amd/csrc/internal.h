@@ -1,0 +1,56 @@
+// Host-side launchers behind the C ABI.  Each returns hipSuccess or the HIP
+// error of the failed launch; arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+struct Shape {
+  int n_h, d_c, d_r, d_h, d_v, d_model, d_q;
+  double rope_base;
+  float scale;   // softmax scale (already resolved)
+  bool bf16;
+};
+
+// ---- generic kernels: any dims, fp32 or bf16 storage, fp32 math -------------
+// Y[M,N] (fp32) = X[M,K] . W[N,K]^T ; X is fp32 or storage type, W storage type.
+hipError_t launch_linear_generic(const Shape& s, int M, int N, int K, const void* X, bool x_f32,
+                                 const void* W, float* Y, hipStream_t st);
+// q (fp32 or storage type) [B, n_h, d_h + d_r] -> q_lat, q_pe (storage type).
+hipError_t launch_absorb_generic(const Shape& s, int B, const void* q, bool q_f32, const void* W_UK,
+                                 const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st);
+// New rows -> cache: c from c_src (row stride c_stride elements), un-rotated
+// k from k_src (stride k_stride); both fp32 or both the storage type.
+hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c_src,
+                                 size_t c_stride, const void* k_src, size_t k_stride, bool src_f32,
+                                 void* cache, const int32_t* offsets, int32_t* lens,
+                                 int32_t* err_flag, hipStream_t st);
+hipError_t launch_decode_generic(const Shape& s, int B, const void* q_lat, const void* q_pe,
+                                 const void* cache, const int32_t* offsets, const int32_t* lens,
+                                 float* o_lat, float* lse, int32_t* err_flag, hipStream_t st);
+// o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 out)
+hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
+                             hipStream_t st);
+
+// ---- V3 fast path (bf16, d_c = 512, d_r = 64, n_h = 128) --------------------
+bool decode_v3_supported(const Shape& s);
+size_t decode_v3_workspace(const Shape& s, int B, int64_t total_rows_hint, int num_cu);
+hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void* q_pe,
+                            const void* cache, const int32_t* offsets, const int32_t* lens,
+                            int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
+                            void* ws, size_t ws_bytes, int num_cu, hipStream_t st);
+
+// Device properties of the current device (cached per device, thread-safe).
+struct DeviceInfo {
+  int device;
+  int num_cu;
+  bool gfx950;
+};
+hipError_t current_device_info(DeviceInfo* out);
+
+}  // namespace mla

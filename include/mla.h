@@ -1,0 +1,177 @@
+/*
+ * mla.h -- C ABI of libmla.so: one decode step of Multi-head Latent Attention
+ * (MLA) over a compressed latent KV cache, computed in latent space by matrix
+ * absorption, on AMD MI355X (gfx950).
+ *
+ * The problem as the pages state it ("MLA模型结构详解：从公式到推理代码",
+ * gentlecold.top, sections "MLA 的核心结构" and "一个实际推理示例"): given the new
+ * token's hidden state h_t, the weights W^DKV, W^KR, W^UK, W^UV, W^O (and for a
+ * compressed query W^DQ, W^UQ) and a cache holding, for every past token, only
+ * the latent c^KV (d_c numbers) and the shared RoPE key k^R (d_R numbers),
+ * produce the layer output.  The four calls below are the steps of that path:
+ *
+ *   mla_absorb_q      query side: q = W^UQ W^DQ h_t (or q given), then the
+ *                     latent query q_lat = W^UK^T q^C per head and q_pe = RoPE(q^R)
+ *   mla_append_cache  new row [c^KV | RoPE(k^R)] written at each sequence's end
+ *   mla_decode_attn   o_lat = softmax(scale (q_lat.c + q_pe.k^R)) . c  (the hot loop)
+ *   mla_project_out   o = W^UV o_lat per head, u = W^O flatten(o)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
+ *   that the caller allocated and owns.  The library allocates nothing and
+ *   keeps no per-call state; it caches device properties per device only.
+ * - ``stream`` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work on it and returns; there is no host synchronisation inside.
+ * - Every call validates its arguments on the host first.  On any return other
+ *   than MLA_OK nothing was enqueued and no output was touched.
+ * - Element types follow ``dims->dtype``: with MLA_DT_BF16 every ``void*``
+ *   tensor is bf16, with MLA_DT_F32 it is float32.  Outputs typed ``float*``
+ *   are always float32.  Index arrays are int32.
+ * - Conditions only the device can see (a length out of range, a full cache
+ *   region) are reported through an optional device ``err_flag`` (int32):
+ *   the kernels OR in the MLA_DEVERR_* bits below; the caller clears it.
+ * - Calls that overlap on one stream are ordered; calls on different streams
+ *   that write the same buffers race.
+ *
+ * Cache layout: ``cache`` is [rows, d_c + d_R]; row r = [c^KV (d_c) | k^R (d_R)]
+ * with k^R already rotated to the row's position (the worked example caches the
+ * RoPE'd k_pe).  Sequence b owns rows offsets[b] .. offsets[b+1]-1 (its
+ * capacity) and uses the first lens[b] of them, the row at index t holding the
+ * token at position t.  For V3 dims in bf16 a row is 1152 bytes.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,       /* a required pointer is NULL                          */
+  MLA_ERR_SHAPE = 2,      /* a size is out of range or dims are unsupported      */
+  MLA_ERR_DTYPE = 3,      /* unknown dims->dtype                                 */
+  MLA_ERR_WORKSPACE = 4,  /* ws_bytes smaller than the matching *_workspace()    */
+  MLA_ERR_LAUNCH = 5,     /* the HIP runtime refused a launch                    */
+  MLA_ERR_DEVICE = 6      /* no usable gfx950 device is current                  */
+} mla_status_t;
+
+typedef enum { MLA_DT_BF16 = 0, MLA_DT_F32 = 1 } mla_dtype_t;
+
+/* Device-side error bits OR-ed into *err_flag. */
+#define MLA_DEVERR_LENS 1       /* lens[b] < 1 or lens[b] > offsets[b+1]-offsets[b]   */
+#define MLA_DEVERR_OVERFLOW 2   /* an appended row would not fit in its region        */
+
+/* Model dimensions ("MLA模型结构详解", section "结合 DeepSeek 推理代码看 MLA":
+ * n_heads, kv_lora_rank = d_c, qk_nope_head_dim = d_h, qk_rope_head_dim = d_R,
+ * v_head_dim = d_v; q_lora_rank = d_q).  DeepSeek-V3: 128, 512, 64, 128, 128,
+ * d_model 7168, d_q 1536. */
+typedef struct {
+  int32_t n_h;            /* query heads                                     */
+  int32_t d_c;            /* latent width (kv_lora_rank)                     */
+  int32_t d_r;            /* decoupled RoPE width, even                      */
+  int32_t d_h;            /* per-head content query/key width                */
+  int32_t d_v;            /* per-head value width                            */
+  int32_t d_model;        /* hidden size (0 if no projection from h_t is used) */
+  int32_t d_q;            /* query latent width (0: no query compression)    */
+  float rope_base;        /* RoPE base; 10000                                */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(d_h + d_r)                  */
+  int32_t dtype;          /* mla_dtype_t                                     */
+} mla_dims_t;
+
+/* Query side ("MLA模型结构详解", section "MLA 的核心结构": c^Q = W^DQ h_t,
+ * q^C = W^UQ c^Q; worked example steps 1 and 4; key identity
+ * q^C.(W^UK c) = (q^C W^UK).c; RoPE on q^R per head).
+ *
+ * Source of the per-head query [q^C (d_h) | q^R (d_R)]:
+ *   h_t != NULL: q = W_UQ (W_DQ h_t), h_t [B, d_model], W_DQ [d_q, d_model],
+ *                W_UQ [n_h*(d_h+d_r), d_q] with rows head-major, each head
+ *                [d_h content | d_r rope].  With dims->d_q == 0, W_DQ must be
+ *                NULL and q = W_UQ h_t, W_UQ [n_h*(d_h+d_r), d_model].
+ *   h_t == NULL: q [B, n_h, d_h + d_r] is given.
+ * Outputs: q_lat [B, n_h, d_c] with q_lat[b,h,:] = W_UK[h]^T q^C[b,h,:]
+ *          (W_UK [n_h, d_h, d_c]), q_pe [B, n_h, d_r] = RoPE(q^R[b,h,:], pos[b])
+ *          (rotate-half, theta_i = base^(-2i/d_r), angle formed in fp64),
+ *          both in dims->dtype, rounded to nearest even once from fp32.
+ * pos [B] int32 device: the query position (the new token's index).
+ * ws: device scratch of at least mla_absorb_q_workspace(dims, B, h_t != NULL)
+ *     bytes (may be NULL when that is 0). */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
+                          const void* W_UQ, const void* q, const void* W_UK, const int32_t* pos,
+                          void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream);
+size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hidden);
+
+/* Append n_new tokens per sequence ("MLA模型结构详解", worked example steps 2-3:
+ * kv_and_pe = wkv_a(x) split into the latent and k_pe, RoPE(k_pe), written at
+ * index start_pos; c^KV = W^DKV h_t, k^R = RoPE(W^KR h_t)).
+ * For b < B, i < n_new: row offsets[b] + lens[b] + i  <-  [c | RoPE(k, lens[b] + i)]
+ *   with (c, k) = (W_DKV x, W_KR x), x = h_t[b, i, :] (h_t [B, n_new, d_model],
+ *   W_DKV [d_c, d_model], W_KR [d_r, d_model]); or, if h_t == NULL, (c, k) taken
+ *   from kv_raw[b, i, :] = [c | un-rotated k] (kv_raw [B, n_new, d_c + d_r];
+ *   the c part is copied bit-exactly).
+ * Then lens[b] += n_new.  No other row is written.  If the rows do not fit in
+ * the region (lens[b] + n_new > offsets[b+1] - offsets[b]) nothing is written
+ * for b, lens[b] is unchanged and MLA_DEVERR_OVERFLOW is set.
+ * ws: at least mla_append_cache_workspace(dims, B, n_new, h_t != NULL) bytes. */
+mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                              const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
+                              const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
+                              size_t ws_bytes, void* stream);
+size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_new,
+                                  int32_t from_hidden);
+
+/* Latent-space attention of one query per sequence ("MLA模型结构详解", worked
+ * example steps 4-5: score = (score_C + score_R) x scale, softmax, z = A . kv_cache;
+ * value identity sum_j a_j W^UV c_j = W^UV sum_j a_j c_j).
+ *   o_lat[b,h,:] = sum_{j < lens[b]} p_j c_j,
+ *   p = softmax_j( scale * (q_lat[b,h,:].c_j + q_pe[b,h,:].kR_j) ),
+ *   (c_j, kR_j) = row offsets[b] + j,  scale = dims->softmax_scale or 1/sqrt(d_h+d_r).
+ *   lse[b,h] = log sum_j exp(scale * score_j)  (natural log; lse may be NULL).
+ * q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] in dims->dtype; o_lat [B, n_h, d_c] fp32.
+ * No mask: every cached row precedes the query.  lens[b] must be in
+ * [1, offsets[b+1]-offsets[b]]; a sequence violating it gets NaN outputs and
+ * MLA_DEVERR_LENS.  total_rows_hint (> 0) is the expected sum of lens and only
+ * sizes the launch; results do not depend on it.
+ * ws: at least mla_decode_attn_workspace(dims, B, total_rows_hint) bytes. */
+mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                             const void* q_pe, const void* cache, const int32_t* offsets,
+                             const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                             float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
+                             void* stream);
+size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint);
+
+/* Output side ("MLA模型结构详解", worked example step 5: multiply by the value
+ * part of wkv_b per head, flatten heads, output projection).
+ *   o[b,h,:] = W_UV[h] o_lat[b,h,:]      W_UV [n_h, d_v, d_c], o [B, n_h, d_v] fp32
+ *   u[b,:]   = W_O flatten(o[b])          W_O [d_model, n_h*d_v] (input index h*d_v + v),
+ *                                         u [B, d_model] fp32
+ * o or u may be NULL to skip storing it (W_O may be NULL when u is NULL).  With
+ * bf16 weights the products run in bf16 with fp32 accumulation (o_lat and o are
+ * rounded to bf16 as operands).
+ * ws: at least mla_project_out_workspace(dims, B, u != NULL) bytes. */
+mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_lat,
+                             const void* W_UV, const void* W_O, float* o, float* u, void* ws,
+                             size_t ws_bytes, void* stream);
+size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u);
+
+/* Bytes of one cache row: (d_c + d_r) * element size (1152 for V3 bf16);
+ * 0 if dims is NULL or invalid. */
+size_t mla_cache_row_bytes(const mla_dims_t* dims);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* MLA_ABI_VERSION of the built library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports what include/mla.h
+declares, and rejects bad arguments before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_latent_attention_16_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "mla.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmla.so not built; run python -m head_latent_attention_16_amd.build")
+    return L.lib()
+
+
+def v3(dtype="bf16", **kw):
+    d = dict(n_h=128, d_c=512, d_r=64, d_h=128, d_v=128, d_model=7168, d_q=1536, dtype=dtype)
+    d.update(kw)
+    return L.Dims.make(**d)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for st in range(7):
+        s = lib.mla_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def test_cache_row_bytes(lib):
+    assert L.cache_row_bytes(v3()) == 1152            # 576 bf16 numbers per token and layer
+    assert L.cache_row_bytes(v3("f32")) == 2304
+    tiny = L.Dims.make(4, 32, 8, 16, 16, dtype="f32")
+    assert L.cache_row_bytes(tiny) == 160
+    assert lib.mla_cache_row_bytes(None) == 0
+    assert L.cache_row_bytes(v3(d_r=7)) == 0           # odd rope width is invalid
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first or no device
+
+
+def call_decode(lib, dims, B=2, q_lat=P, q_pe=P, cache=P, offsets=P, lens=P, hint=100, o=P,
+                ws=P, ws_bytes=1 << 40):
+    return lib.mla_decode_attn(ctypes.byref(dims) if dims is not None else None, B, q_lat, q_pe,
+                               cache, offsets, lens, hint, o, None, None, ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    d = v3()
+    assert call_decode(lib, None) == 1
+    assert call_decode(lib, v3(dtype=7)) == 3
+    assert call_decode(lib, v3(n_h=0)) == 2
+    assert call_decode(lib, v3(d_c=4096)) == 2
+    assert call_decode(lib, d, B=-1) == 2
+    assert call_decode(lib, d, B=0) == 0                 # empty batch: nothing to do
+    assert call_decode(lib, d, hint=0) == 2
+    for k in ("q_lat", "q_pe", "cache", "offsets", "lens", "o"):
+        assert call_decode(lib, d, **{k: None}) == 1, k
+    assert call_decode(lib, d, ws=None) == 4             # fast path needs scratch
+    assert call_decode(lib, d) == 6                      # valid call, no GPU here
+
+
+def test_absorb_append_project_validation(lib):
+    d = v3()
+    ab = lambda **kw: lib.mla_absorb_q(ctypes.byref(kw.pop("dims", d)), kw.pop("B", 2), kw.pop("h_t", None),  # noqa: E731
+                                      kw.pop("W_DQ", None), kw.pop("W_UQ", None), kw.pop("q", P),
+                                      kw.pop("W_UK", P), kw.pop("pos", P), kw.pop("q_lat", P),
+                                      kw.pop("q_pe", P), kw.pop("ws", None), kw.pop("ws_bytes", 0), None)
+    assert ab(q=None) == 1
+    assert ab(pos=None) == 1
+    assert ab(h_t=P, W_UQ=P) == 1                         # d_q > 0 needs W_DQ
+    assert ab(h_t=P, W_UQ=P, W_DQ=P) == 4                 # needs fp32 scratch for c_Q and q
+    assert ab(dims=v3(d_q=0), h_t=P, W_UQ=P, W_DQ=P) == 2
+    assert ab(B=0) == 0
+    assert ab() == 6
+    need = lib.mla_absorb_q_workspace(ctypes.byref(d), 2, 1)
+    assert need >= 2 * 1536 * 4 + 2 * 128 * 192 * 4
+    assert lib.mla_absorb_q_workspace(ctypes.byref(d), 2, 0) == 0
+
+    ap = lambda **kw: lib.mla_append_cache(ctypes.byref(kw.pop("dims", d)), kw.pop("B", 2), kw.pop("n_new", 1),  # noqa: E731
+                                          kw.pop("h_t", None), kw.pop("W_DKV", None), kw.pop("W_KR", None),
+                                          kw.pop("kv_raw", P), kw.pop("cache", P), kw.pop("offsets", P),
+                                          kw.pop("lens", P), None, kw.pop("ws", None), kw.pop("ws_bytes", 0), None)
+    assert ap(kv_raw=None) == 1
+    assert ap(cache=None) == 1
+    assert ap(n_new=-1) == 2
+    assert ap(n_new=0) == 0
+    assert ap(h_t=P, W_DKV=P) == 1
+    assert ap(h_t=P, W_DKV=P, W_KR=P) == 4
+    assert ap() == 6
+
+    po = lambda **kw: lib.mla_project_out(ctypes.byref(kw.pop("dims", d)), kw.pop("B", 2), kw.pop("o_lat", P),  # noqa: E731
+                                         kw.pop("W_UV", P), kw.pop("W_O", None), kw.pop("o", P),
+                                         kw.pop("u", None), kw.pop("ws", None), kw.pop("ws_bytes", 0), None)
+    assert po(W_UV=None) == 1
+    assert po(u=P) == 1                                   # u needs W_O
+    assert po(o=None, u=P, W_O=P) == 4                    # u without o needs scratch for o
+    assert po(o=None) == 0                                # nothing requested
+    assert po() == 6
+
+
+def test_decode_workspace_sizes(lib):
+    d = v3()
+    small = lib.mla_decode_attn_workspace(ctypes.byref(d), 16, 65536)
+    big = lib.mla_decode_attn_workspace(ctypes.byref(d), 64, 1101299)
+    assert 0 < small <= big
+    # generic path (fp32 tiny dims) needs none
+    tiny = L.Dims.make(4, 32, 8, 16, 16, dtype="f32")
+    assert lib.mla_decode_attn_workspace(ctypes.byref(tiny), 1, 64) == 0
