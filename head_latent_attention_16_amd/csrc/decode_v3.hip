@@ -11,9 +11,11 @@
 //   once (global_load_lds_dwordx4, 16 B per lane) and then feeds both
 //   contractions of all four waves: S^T = K . Q^T (QK, 576-deep) and
 //   O^T += C^T . P^T (PV, over the tile's 32 rows, first 512 columns).
-// * Wave w owns heads 32w..32w+31.  Q (32 heads x 576 bf16) lives in VGPRs;
-//   the output accumulator O^T (512 cols x 32 heads fp32) lives in 16 MFMA
-//   32x32 tiles (256 accumulation registers per lane).
+// * Four waves, one per SIMD; wave w owns heads 32w..32w+31.  Its Q
+//   (32 heads x 576 bf16) lives in 144 VGPRs and its output accumulator O^T
+//   (512 cols x 32 heads fp32) in 256 accumulation registers.  Each LDS byte
+//   of a tile is read by four waves (not eight): LDS read bandwidth, not the
+//   matrix cores, is the scarcer resource for these access patterns.
 // * Both contractions use v_mfma_f32_32x32x16_bf16.  QK reads row-major
 //   16-byte fragments; PV needs 8 rows of one column per lane and gets them
 //   with ds_read_b64_tr_b16 transpose reads from the same row-major tile.
@@ -21,11 +23,8 @@
 //   layout of S, so P goes from the QK result to the PV operand in registers.
 // * LDS rows are 1152 B with 16-byte chunks XOR-swizzled per row so that the
 //   row-strided reads of both contractions are free of bank conflicts.
-// * Four LDS stages (144 KiB): tile i is multiplied by Q while tile i-1 feeds
-//   PV and tiles i+1, i+2 are in flight.  The QK chain of tile i is
-//   interleaved with the PV products of tile i-1, and the softmax of tile i
-//   overlaps the second half of them, so the matrix cores stay busy while
-//   the single wave per SIMD waits on LDS or runs VALU work.
+// * Four LDS stages (144 KiB): while tile i is used, tiles i+1..i+3 are in
+//   flight.
 // * Softmax in base 2 against a per-piece reference max fixed by the piece's
 //   first tile: later scores may exceed it (p up to 2^64 stays far from fp32
 //   overflow), so the accumulator is never rescaled inside the loop -- the
@@ -55,16 +54,19 @@ constexpr int CHUNKS = ROWB / 16;      // 72
 constexpr int TILE = 32;               // rows per tile
 constexpr int TILEB = TILE * ROWB;     // 36864 bytes
 constexpr int NSTAGE = 4;
-constexpr int WAVES = 4;
+constexpr int WAVES = 4;                              // one per SIMD
+constexpr int HPW = NH / WAVES;                       // 32 heads per wave
 constexpr int THREADS = WAVES * 64;
 constexpr int DMA_PER_TILE = TILEB / 1024;            // 36 wave-instructions
 constexpr int DMA_PER_WAVE = DMA_PER_TILE / WAVES;    // 9
-constexpr int KSTEPS = DK / 16;                       // 36
+constexpr int KSTEPS = DK / 16;                       // 36 k-steps of 16 features
+constexpr int QK_PF = 6;                              // QK fragments in flight
+constexpr int PV_PF = 4;                              // PV fragment pairs in flight
 constexpr float OVF_TH = 64.0f;                       // log2 units
 constexpr int MIN_ROWS_PER_WG = 256;
 
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
-static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "uneven DMA split");
+static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 
 // Partial record of one (workgroup, sequence) piece.
 struct PartialLayout {
@@ -192,38 +194,28 @@ __device__ __forceinline__ void barrier_all_lds() {
 // one pass when the lanes hit 16 distinct 16-byte bank groups.  Row r starts
 // at bank group 8 r (mod 16), and its 16-byte chunk c is stored at
 // c ^ swz(r), swz = bit-reverse of bits 1..3 of r.  Then (a) 16 consecutive
-// rows at one chunk (the QK fragment read) and (b) 4 aligned rows x 4 aligned
+// rows at one chunk (the QK fragment read) and (b) 8 aligned rows x 2 aligned
 // chunks (one 32-lane half of a PV transpose read) cover 16 distinct groups.
 __device__ __forceinline__ int swz(int r) {
   return ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
 }
 
-// S^T[32 rows x 32 heads] += K[rows, k-step kk] . Q^T[k-step kk, heads]
-#define QK_STEP(T, kk, S) \
-  S = __builtin_amdgcn_mfma_f32_32x32x16_bf16( \
-      *(const MLA_LDS bf16x8*)((T) + qk_off[(kk) & 3] + ((kk) >> 2) * 128), q[kk], S, 0, 0, 0)
-
-// O^T[cols 32cb.., 32 heads] += C^T[cols, rows of half kk2] . P^T[rows, heads]
-#define PV_STEP(T, kk2, cb, P) \
-  do { \
-    const MLA_LDS char* p0_ = (T) + tr_base[0][(cb) & 1] + (kk2) * 16 * ROWB + (cb) * 64; \
-    const MLA_LDS char* p1_ = (T) + tr_base[1][(cb) & 1] + (kk2) * 16 * ROWB + (cb) * 64; \
-    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0_); \
-    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1_); \
-    const bf16x8 cf_ = {lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]}; \
-    O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf_, (P)[kk2], O[cb], 0, 0, 0); \
-  } while (0)
-
+// Wave w owns heads 32w .. 32w+31.  Per 32-row tile it computes
+//   S^T[32 rows x 32 heads] = K[rows x 576] . Q^T[576 x heads]          (36 MFMA 32x32x16)
+//   O^T[512 cols x 32 heads] += C^T[cols x 32 rows] . P^T[rows x heads]  (32 MFMA 32x32x16)
+// One wave per SIMD holds Q (144 VGPRs) and O (256 accumulation registers);
+// latency is hidden inside the wave by loading LDS fragments several
+// steps ahead of the MFMA that consumes them.
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
-  // Per-lane DMA source offsets, kept in LDS rather than in 9 VGPRs.
-  __shared__ __attribute__((aligned(16))) uint32_t dma_tab[DMA_PER_WAVE / 4 * 4 + 4][THREADS];
+  // Per-lane DMA source offsets, kept in LDS rather than in VGPRs.
+  __shared__ __attribute__((aligned(16))) uint32_t dma_tab[DMA_PER_WAVE][THREADS];
 
   const int g = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g32 = lane >> 5;          // which half of the wave
-  const int n32 = lane & 31;          // head within the wave's 32 / row within tile
+  const int n32 = lane & 31;          // head within the wave / row within the tile
 
   const int64_t total = a.prefix[a.B];
   if (total <= 0) return;
@@ -233,9 +225,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
-  // DMA mapping for full tiles: wave-instruction j = wave*9 + k covers LDS
-  // chunks [64 j, 64 j + 64); lane i fills chunk p = 64 j + i, which holds
-  // logical chunk (p % 72) ^ swz(row) of row p / 72.
+  // DMA: wave-instruction j = 9 wave + k covers LDS chunks [64 j, 64 j + 64);
+  // lane i fills chunk p = 64 j + i, which holds logical chunk
+  // (p % 72) ^ swz(row) of row p / 72.
 #pragma unroll
   for (int k = 0; k < DMA_PER_WAVE; ++k) {
     const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
@@ -243,17 +235,17 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int c = (p % CHUNKS) ^ swz(r);
     dma_tab[k][threadIdx.x] = (uint32_t)(r * ROWB + c * 16);
   }
-  // (read back by each wave itself only: no barrier needed)
+  // (each lane reads back only its own entries: no barrier needed)
 
-  // QK fragment addresses: row n32, logical chunk 2kk + g32 stored at
-  // (2kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
+  // QK A-fragment (32x32x16): row n32, logical chunk 2 kk + g32 stored at
+  // (2 kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
   // (2v + g32) ^ swz(n32); the rest is the constant 8u chunks.
   uint32_t qk_off[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     qk_off[v] = (uint32_t)(n32 * ROWB + (((2 * v + g32) ^ swz(n32)) << 4));
 
-  // PV transpose-read addresses.  In each 16-lane group G (i = lane % 16),
+  // PV A-fragment via transpose reads.  In each 16-lane group G (i = lane%16),
   // lane i reads 8 bytes of row 16 kk2 + 8 rd + rr, rr = 4 g32 + i/4, at
   // columns 32 cb + 16 (G & 1) + 4 (i & 3); after the transpose lane j of the
   // group holds column 32 cb + 16 (G & 1) + j for four consecutive rows.
@@ -275,7 +267,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     }
   }
 
-  const int head = wave * 32 + n32;
+  const int head = wave * HPW + n32;
 
   // Find the first sequence touching [start, end).
   int b;
@@ -297,12 +289,13 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int t0 = (int)(pos - seq_begin);
     const int seg_len = (int)(seg_end - pos);
     const int ntiles = (seg_len + TILE - 1) / TILE;
+    const bool last_partial = (seg_len % TILE) != 0;
     const char* rows = a.cache + ((size_t)a.offsets[b] + (size_t)t0) * ROWB;
 
     if (!first_segment) barrier_all_lds();   // previous segment's tiles fully consumed
     first_segment = false;
 
-    // Q fragments for this sequence: B operand of QK (head n32, 8 features).
+    // Q fragments (B operand of QK): head n32, features 16 kk + 8 g32 .. +8.
     bf16x8 q[KSTEPS];
     {
       const bf16x8* ql = (const bf16x8*)(a.q_lat + ((size_t)b * NH + head) * DC);
@@ -316,20 +309,22 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       const uint32_t stage_lds = lds0 + (uint32_t)((tile % NSTAGE) * TILEB);
       const char* tbase = rows + (size_t)tile * TILEB;
       const int nvalid = seg_len - tile * TILE;
-      uint32_t dma_off[DMA_PER_WAVE];
+      // All offsets are read before the first DMA: the DMA asm is a memory
+      // barrier for the compiler, so interleaved reads would each wait alone.
+      uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) dma_off[k] = dma_tab[k][threadIdx.x];
+      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = dma_tab[k][threadIdx.x];
       if (nvalid >= TILE) {
 #pragma unroll
         for (int k = 0; k < DMA_PER_WAVE; ++k)
-          dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), dma_off[k], tbase);
+          dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
       } else {
         // Partial tile (the last of a piece): rows nvalid..31 of the stage are
         // zeroed (finite, and their scores are masked out), and only lanes
         // whose chunk lies in a row below nvalid load -- chunk p is in row
         // p / 72, so the test is the uniform bound p < 72 * nvalid.  No byte
-        // outside the sequence is read.  Such a tile may issue fewer than
-        // DMA_PER_WAVE instructions, so waits that precede it use vmcnt(0).
+        // outside the sequence is read.  Such a tile may issue fewer
+        // instructions; waits never count on its instructions.
         MLA_LDS char* st = (MLA_LDS char*)lds + (tile % NSTAGE) * TILEB;
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
         for (int off = nvalid * ROWB + (int)threadIdx.x * 16; off < TILEB; off += THREADS * 16)
@@ -338,119 +333,127 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         for (int k = 0; k < DMA_PER_WAVE; ++k) {
           const int bound = nvalid * CHUNKS - (wave * DMA_PER_WAVE + k) * 64;
           if (lane < bound)
-            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), dma_off[k], tbase);
+            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
         }
       }
     };
-    const bool last_partial = (seg_len % TILE) != 0;
-    // Wait until tile `it` has landed in LDS (this wave's DMA), then barrier.
-    // Tile it + 1 may still be in flight unless it is a partial tile.
+    // Wait for tile `it`: tiles it+1, it+2 may still be in flight; only full
+    // ones are counted (a partial tile is the newest, so under-counting it only
+    // makes the wait stricter).
     auto wait_tile = [&](int it) {
-      if (it + 1 < ntiles && !(it + 1 == ntiles - 1 && last_partial))
-        wait_vm_then_barrier<DMA_PER_WAVE>();
-      else
-        wait_vm_then_barrier<0>();
+      int ahead_full = 0;
+      for (int t = it + 1; t <= it + 2 && t < ntiles; ++t)
+        if (!(t == ntiles - 1 && last_partial)) ++ahead_full;
+      if (ahead_full >= 2) wait_vm_then_barrier<2 * DMA_PER_WAVE>();
+      else if (ahead_full == 1) wait_vm_then_barrier<DMA_PER_WAVE>();
+      else wait_vm_then_barrier<0>();
     };
 
-    // Tile `it` lives in stage it % NSTAGE.  While tile it is multiplied by
-    // Q, tile it-1 is still needed for its PV product, and tiles it+1 and
-    // it+2 are in flight: four stages.
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    // Three tiles ahead: tile it+3 goes into the stage of tile it-1.
+    for (int t = 0; t < NSTAGE - 1 && t < ntiles; ++t) issue_tile(t);
 
     floatx16 O[DC / 32];
 #pragma unroll
     for (int cb = 0; cb < DC / 32; ++cb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
-    float m_ref;               // reference max of scaled scores (log2 units)
+    float m_ref = 0.f;         // reference max of scaled scores (log2 units)
     float l_run = 0.f;         // this lane's share of the sum of weights
-    bf16x8 P[2];               // weights of the previous tile (PV operand)
 
-    // Softmax of one tile's scores into bf16 weights; lane holds head n32 and
-    // rows 8 (i/4) + 4 g32 + i%4.  One separately rounded product per score
-    // feeds both the max and the exponent, so the maximal score gets exactly
-    // exp2(0) = 1; l sums the same bf16-rounded weights that enter PV, so
-    // O / l is an exactly normalised average of the rows.
-    auto softmax = [&](floatx16& S, int nvalid, bf16x8* Pn) {
+    for (int it = 0; it < ntiles; ++it) {
+      wait_tile(it);
+      if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1);
+      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
+
+      // ---- S^T = K . Q^T, fragments loaded QK_PF steps ahead ----
+      floatx16 S;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] = 0.f;
+      bf16x8 kf[QK_PF];
+#pragma unroll
+      for (int j = 0; j < QK_PF; ++j)
+        kf[j] = *(const MLA_LDS bf16x8*)(T + qk_off[j & 3] + (j >> 2) * 128);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % QK_PF], q[kk], S, 0, 0, 0);
+        const int nk = kk + QK_PF;
+        if (nk < KSTEPS)
+          kf[kk % QK_PF] = *(const MLA_LDS bf16x8*)(T + qk_off[nk & 3] + (nk >> 2) * 128);
+      }
+      // Schedule: QK_PF fragment loads, then (MFMA, load) pairs, then the
+      // remaining MFMAs -- each fragment is in flight for QK_PF steps.
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_PF, 0);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS - QK_PF; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, QK_PF, 0);
+
+      // ---- PV fragments for the first column blocks go out before the
+      //      softmax so their latency hides behind it ----
+      bf16x4 pa[PV_PF][2];
+#pragma unroll
+      for (int j = 0; j < PV_PF; ++j) {
+        const int kk2 = j / (DC / 32), cb = j % (DC / 32);
+        const MLA_LDS char* p0 = T + tr_base[0][cb & 1] + kk2 * 16 * ROWB + cb * 64;
+        const MLA_LDS char* p1 = T + tr_base[1][cb & 1] + kk2 * 16 * ROWB + cb * 64;
+        pa[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
+        pa[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
+      }
+
+      // ---- softmax: lane holds head n32, rows 8 (i/4) + 4 g32 + i%4 ----
+      // One separately rounded product per score feeds both the max and the
+      // exponent, so the maximal score gets exactly exp2(0) = 1; l sums the
+      // same bf16-rounded weights that enter PV, so O / l is an exactly
+      // normalised average of the rows.
+      const int nvalid = seg_len - it * TILE;
+      float mloc = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + 4 * g32 + (i & 3);
-        const float x = __fmul_rn(S[i], a.scale_log2);
-        S[i] = row < nvalid ? x : -INFINITY;
+        const float v = __fmul_rn(S[i], a.scale_log2);
+        S[i] = row < nvalid ? v : -INFINITY;
+        mloc = fmaxf(mloc, S[i]);
       }
+      if (it == 0) {
+        m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      } else if (__any(mloc > m_ref + OVF_TH)) {
+        if (lane == 0) a.ovf[b] = 1;
+      }
+      bf16x8 P[2];
       float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(S[i] - m_ref);
         lsum += (float)pb;
-        Pn[i >> 3][i & 7] = pb;
+        P[i >> 3][i & 7] = pb;
       }
       l_run += lsum;
-    };
 
-    // ---- tile 0: QK, reference max, weights ----
-    {
-      wait_tile(0);
-      if (ntiles > 2) issue_tile(2);
-      const MLA_LDS char* T = (const MLA_LDS char*)lds;
-      floatx16 S;
+      // ---- O^T += C^T . P^T over 2 row halves x 16 column blocks ----
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) QK_STEP(T, kk, S);
-      const int nvalid = seg_len;
-      float smax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * g32 + (i & 3);
-        smax = fmaxf(smax, row < nvalid ? S[i] : -INFINITY);
+      for (int s = 0; s < 2 * (DC / 32); ++s) {
+        const int kk2 = s / (DC / 32), cb = s % (DC / 32);
+        const bf16x4 lo = pa[s % PV_PF][0], hi = pa[s % PV_PF][1];
+        const bf16x8 cf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int ns = s + PV_PF;
+        if (ns < 2 * (DC / 32)) {
+          const int nk2 = ns / (DC / 32), ncb = ns % (DC / 32);
+          const MLA_LDS char* p0 = T + tr_base[0][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
+          const MLA_LDS char* p1 = T + tr_base[1][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
+          pa[s % PV_PF][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
+          pa[s % PV_PF][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
+        }
+        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
       }
-      const float mloc = __fmul_rn(smax, a.scale_log2);
-      m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      softmax(S, nvalid, P);
-    }
-
-    // ---- steady state: QK(it) and the first half of PV(it-1) interleaved,
-    //      then softmax(it) overlapping the second half of PV(it-1) ----
-    for (int it = 1; it < ntiles; ++it) {
-      wait_tile(it);
-      if (it + 2 < ntiles) issue_tile(it + 2);
-      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
-      const MLA_LDS char* Tp = (const MLA_LDS char*)lds + ((it - 1) % NSTAGE) * TILEB;
-      floatx16 S;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = 0.f;
-      // 36 QK steps against the first 16 PV steps (kk2 = 0: cb 0..15)
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        QK_STEP(T, kk, S);
-        if (kk < 32 && (kk & 1) == 0) PV_STEP(Tp, 0, kk >> 1, P);
+      for (int s2 = 0; s2 < 2 * (DC / 32) - PV_PF; ++s2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
-      bf16x8 Pn[2];
-      const int nvalid = seg_len - it * TILE;
-      softmax(S, nvalid, Pn);
-      // second half of PV(it-1): kk2 = 1
-#pragma unroll
-      for (int cb = 0; cb < DC / 32; ++cb) PV_STEP(Tp, 1, cb, P);
-      P[0] = Pn[0];
-      P[1] = Pn[1];
-      // Overflow guard: a score far above the reference max flags the sequence.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-      if (__any(mx > m_ref + OVF_TH)) {
-        if (lane == 0) a.ovf[b] = 1;
-      }
-    }
-
-    // ---- PV of the last tile ----
-    {
-      const MLA_LDS char* Tp = (const MLA_LDS char*)lds + ((ntiles - 1) % NSTAGE) * TILEB;
-#pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2)
-#pragma unroll
-        for (int cb = 0; cb < DC / 32; ++cb) PV_STEP(Tp, kk2, cb, P);
+      __builtin_amdgcn_sched_group_barrier(0x008, PV_PF, 1);
     }
 
     // ---- emit the partial (unnormalised O, m, l) of this piece ----
