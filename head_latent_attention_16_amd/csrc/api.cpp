@@ -196,6 +196,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
     qsrc = qf;
     q_f32 = true;
   }
+  if (!q_f32 && !force_generic() && proj_v3_supported(s))
+    return launched(launch_absorb_v3(s, B, qsrc, W_UK, pos, q_lat, q_pe, hs));
   return launched(launch_absorb_generic(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
 }
 
@@ -309,7 +311,9 @@ mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_l
   if ((st = device_ready(&info)) != MLA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   float* ob = o ? o : (float*)ws;
-  hipError_t e = launch_uv_generic(s, B, o_lat, W_UV, ob, hs);
+  hipError_t e = (!force_generic() && proj_v3_supported(s))
+                     ? launch_uv_v3(s, B, o_lat, W_UV, ob, hs)
+                     : launch_uv_generic(s, B, o_lat, W_UV, ob, hs);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (u) {
     e = launch_linear_generic(s, B, s.d_model, s.n_h * s.d_v, ob, true, W_O, u, hs);

@@ -45,6 +45,15 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t ws_bytes, int num_cu, hipStream_t st);
 
+// bf16 per-head projections at n_h = 128, d_h = d_v = 128, d_c = 512, d_r = 64.
+bool proj_v3_supported(const Shape& s);
+// q (bf16) [B, n_h, d_h + d_r] -> q_lat, q_pe (bf16).
+hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, const void* W_UK,
+                            const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st);
+// o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 in and out).
+hipError_t launch_uv_v3(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
+                        hipStream_t st);
+
 // Device properties of the current device (cached per device, thread-safe).
 struct DeviceInfo {
   int device;

@@ -1,0 +1,212 @@
+// Per-head projections around the latent attention, DeepSeek-V3 dims, bf16.
+//
+// absorb: q_lat[b,h,:] = W_UK[h]^T q^C[b,h,:]   ("MLA模型结构详解", section
+//         "为什么矩阵吸收很关键": q^C . (W^UK c) = (q^C W^UK) . c), plus
+//         q_pe[b,h,:] = RoPE(q^R[b,h,:], pos[b]) on the decoupled part.
+// uv:     o[b,h,:] = W_UV[h] o_lat[b,h,:]        (worked example step 5).
+//
+// Both are batched skinny products (M = batch, 128 x 512 weight per head) whose
+// cost is streaming the 16.8 MB weight once; they run on bf16 MFMA with fp32
+// accumulation.  W_UK[h] is [d_h=128][d_c=512] with the contraction index d_h
+// strided, so its tile is staged in LDS and read with transpose reads; W_UV[h]
+// is [d_v][d_c] with the contraction index contiguous and is read directly.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int NH = 128, DH = 128, DC = 512, DR = 64, DV = 128;
+constexpr int QW = DH + DR;   // per-head width of the given query [q^C | q^R]
+
+// ---------------------------------------------------------------------------
+// absorb: one workgroup per (head, half of the 512 latent columns).
+//   q_lat^T[cols x batch] = W_UK[h]^T[cols x k] . q_C^T[k x batch]   (32x32x16)
+// LDS holds W_UK[h][0:128][256 columns] with rows padded to 544 bytes so the
+// 4-row x 32-byte transpose reads of a 16-lane group fall in distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int ABS_COLS = 256;
+constexpr int ABS_ROWB = ABS_COLS * 2 + 32;   // 544
+constexpr int ABS_THREADS = 256;
+
+__global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_base,
+                                                           const __bf16* __restrict__ q,
+                                                           const __bf16* __restrict__ W_UK,
+                                                           const int32_t* __restrict__ pos,
+                                                           __bf16* __restrict__ q_lat,
+                                                           __bf16* __restrict__ q_pe) {
+  __shared__ __attribute__((aligned(16))) char w[DH * ABS_ROWB];
+  const int h = blockIdx.x, half = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // Stage W_UK[h][:, 256 half .. +256] (128 rows x 32 chunks of 16 B).
+  const __bf16* src = W_UK + (size_t)h * DH * DC + half * ABS_COLS;
+#pragma unroll
+  for (int j = 0; j < DH * (ABS_COLS / 8) / ABS_THREADS; ++j) {
+    const int idx = j * ABS_THREADS + tid;
+    const int r = idx >> 5, c = idx & 31;
+    const floatx4 v = *(const floatx4*)(src + (size_t)r * DC + c * 8);
+    *(floatx4*)(w + r * ABS_ROWB + c * 16) = v;
+  }
+  __syncthreads();
+
+  // Transpose-read addressing (see the decode kernel): in 16-lane group G,
+  // lane i reads 8 bytes of row r0 + i/4 at columns c0 + 4 (i & 3); lane j of
+  // the group then holds column c0 + j for rows r0 .. r0+3.
+  const int G = lane >> 4, i16 = lane & 15, g32 = lane >> 5;
+  const int h16 = G & 1;
+  const uint32_t tr_off = (uint32_t)((i16 >> 2) * ABS_ROWB + 32 * h16 + 8 * (i16 & 3));
+
+  // Each wave owns two 32-column blocks; loop over 32-wide batch blocks.
+  for (int nb = 0; nb * 32 < B; ++nb) {
+    const int bq = nb * 32 + (lane & 31);
+    const bool bok = bq < B;
+    // B operand: q_C[bq][h][16 ks + 8 g32 .. +8]
+    bf16x8 qb[DH / 16];
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      if (bok)
+        qb[ks] = *(const bf16x8*)(q + ((size_t)bq * NH + h) * QW + 16 * ks + 8 * g32);
+      else
+        qb[ks] = bf16x8{};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int cb = wave * 2 + t;   // column block within this half
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        const char* p = w + (16 * ks + 8 * g32) * ABS_ROWB + 64 * cb + tr_off;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)p);
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
+      }
+      // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
+      if (bok) {
+        __bf16* dst = q_lat + ((size_t)bq * NH + h) * DC + half * ABS_COLS + 32 * cb + 4 * g32;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const bf16x4 v = {(__bf16)acc[4 * q4 + 0], (__bf16)acc[4 * q4 + 1],
+                            (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
+          *(bf16x4*)(dst + 8 * q4) = v;
+        }
+      }
+    }
+  }
+
+  // RoPE on the decoupled part (first half only): q_pe = rotate(q^R, pos[b]).
+  if (half == 0) {
+    for (int idx = tid; idx < B * (DR / 2); idx += ABS_THREADS) {
+      const int b = idx / (DR / 2), i = idx % (DR / 2);
+      float cs, sn;
+      rope_cos_sin(pos[b], i, DR, rope_base, &cs, &sn);
+      const __bf16* qr = q + ((size_t)b * NH + h) * QW + DH;
+      const float lo = (float)qr[i], hi = (float)qr[DR / 2 + i];
+      __bf16* out = q_pe + ((size_t)b * NH + h) * DR;
+      out[i] = (__bf16)(lo * cs - hi * sn);
+      out[DR / 2 + i] = (__bf16)(hi * cs + lo * sn);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// uv: one workgroup per (head, 32-row block of W_UV); it keeps its 32 x 512
+// weight block in registers and walks the batch in blocks of 32.  The four
+// waves split the 512-long contraction and add their partial sums through LDS.
+//   o^T[v x batch] = W_UV[h][v x c] . o_lat^T[c x batch]   (32x32x16)
+// o_lat is fp32; it enters the bf16 product as hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), two MFMAs per step, so the result keeps about 16
+// significant bits of o_lat instead of the 8 a single bf16 rounding leaves.
+// ---------------------------------------------------------------------------
+constexpr int UV_KS = DC / 16 / 4;   // 8 k-steps per wave
+
+__device__ __forceinline__ void split_bf16(const floatx4& x0, const floatx4& x1, bf16x8& hi,
+                                           bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (__bf16)x0[i];
+    hi[4 + i] = (__bf16)x1[i];
+    lo[i] = (__bf16)(x0[i] - (float)hi[i]);
+    lo[4 + i] = (__bf16)(x1[i] - (float)hi[4 + i]);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ o_lat,
+                                               const __bf16* __restrict__ W_UV,
+                                               float* __restrict__ o) {
+  __shared__ floatx16 red[3][64];
+  const int h = blockIdx.x, vb = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g32 = lane >> 5;
+  const int v = 32 * vb + (lane & 31);
+  const __bf16* wrow = W_UV + ((size_t)h * DV + v) * DC;
+  bf16x8 aw[UV_KS];
+#pragma unroll
+  for (int j = 0; j < UV_KS; ++j) aw[j] = *(const bf16x8*)(wrow + 16 * (wave * UV_KS + j) + 8 * g32);
+
+  for (int nb = 0; nb * 32 < B; ++nb) {
+    const int bq = 32 * nb + (lane & 31);
+    const bool bok = bq < B;
+    const float* orow = o_lat + ((size_t)(bok ? bq : 0) * NH + h) * DC;
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < UV_KS; ++j) {
+      const int c = 16 * (wave * UV_KS + j) + 8 * g32;
+      floatx4 x0 = *(const floatx4*)(orow + c);
+      floatx4 x1 = *(const floatx4*)(orow + c + 4);
+      if (!bok) x0 = x1 = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 hi, lo;
+      split_bf16(x0, x1, hi, lo);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], lo, acc, 0, 0, 0);
+    }
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w2 = 0; w2 < 3; ++w2) {
+        const floatx16 r = red[w2][lane];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += r[i];
+      }
+      // lane: batch bq, rows v = 32 vb + 8 (i/4) + 4 g32 + i%4
+      if (bok) {
+        float* dst = o + ((size_t)bq * NH + h) * DV + 32 * vb + 4 * g32;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(floatx4*)(dst + 8 * q4) =
+              floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool proj_v3_supported(const Shape& s) {
+  return s.bf16 && s.n_h == NH && s.d_c == DC && s.d_r == DR && s.d_h == DH && s.d_v == DV;
+}
+
+hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, const void* W_UK,
+                            const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st) {
+  k_absorb_v3<<<dim3(NH, DC / ABS_COLS), ABS_THREADS, 0, st>>>(
+      B, s.rope_base, (const __bf16*)q, (const __bf16*)W_UK, pos, (__bf16*)q_lat, (__bf16*)q_pe);
+  return hipGetLastError();
+}
+
+hipError_t launch_uv_v3(const Shape&, int B, const float* o_lat, const void* W_UV, float* o,
+                        hipStream_t st) {
+  k_uv_v3<<<dim3(NH, DV / 32), 256, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o);
+  return hipGetLastError();
+}
+
+}  // namespace mla
