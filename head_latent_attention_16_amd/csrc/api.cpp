@@ -67,20 +67,54 @@ mla_status_t launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 bool force_generic() { return env_flag("MLA_FORCE_GENERIC"); }
 
+// Linear layers: the MFMA kernel for bf16 weights when the sizes suit it,
+// the generic kernel otherwise.  Both paths of a call site are chosen by the
+// same predicate in the workspace query and in the call.
+bool fast_linear(const Shape& s, int M, int N, int K) {
+  return !force_generic() && s.bf16 && gemm_v3_supported(M, N, K);
+}
+size_t linear_ws(const Shape& s, int M, int N, int K) {
+  return fast_linear(s, M, N, K) ? gemm_v3_workspace(M, N, K) : 0;
+}
+hipError_t linear(const Shape& s, int M, int N, int K, const void* X, bool x_f32, const void* W,
+                  float* Y, void* part, hipStream_t st) {
+  if (fast_linear(s, M, N, K)) return launch_gemm_v3(M, N, N, K, X, x_f32, W, nullptr, Y, part, st);
+  return launch_linear_generic(s, M, N, K, X, x_f32, W, Y, st);
+}
+
 // Workspace layouts (byte offsets, each region 256-aligned).
 size_t absorb_ws(const Shape& s, int B, bool from_hidden) {
   if (!from_hidden) return 0;
+  const int qw = s.n_h * (s.d_h + s.d_r);
   size_t cq = s.d_q > 0 ? align256((size_t)B * s.d_q * sizeof(float)) : 0;
-  size_t q = align256((size_t)B * s.n_h * (s.d_h + s.d_r) * sizeof(float));
-  return cq + q;
+  size_t q = align256((size_t)B * qw * sizeof(float));
+  size_t part = linear_ws(s, B, qw, s.d_q > 0 ? s.d_q : s.d_model);
+  if (s.d_q > 0) {
+    const size_t p1 = linear_ws(s, B, s.d_q, s.d_model);
+    if (p1 > part) part = p1;
+  }
+  return cq + q + align256(part);
 }
+// Fused rope+latent key projection: one linear layer of d_c + d_r outputs
+// whose rows come from W_DKV then W_KR.
+bool fused_kv(const Shape& s, int M) { return fast_linear(s, M, s.d_c + s.d_r, s.d_model) && s.d_c % 32 == 0; }
 size_t append_ws(const Shape& s, int B, int n_new, bool from_hidden) {
   if (!from_hidden) return 0;
-  return align256((size_t)B * n_new * (s.d_c + s.d_r) * sizeof(float));
+  const int M = B * n_new;
+  size_t part = 0;
+  if (fused_kv(s, M)) {
+    part = gemm_v3_workspace(M, s.d_c + s.d_r, s.d_model);
+  } else {
+    part = linear_ws(s, M, s.d_c, s.d_model);
+    const size_t p2 = linear_ws(s, M, s.d_r, s.d_model);
+    if (p2 > part) part = p2;
+  }
+  return align256((size_t)M * (s.d_c + s.d_r) * sizeof(float)) + align256(part);
 }
 size_t project_ws(const Shape& s, int B, bool with_u) {
   if (!with_u) return 0;
-  return align256((size_t)B * s.n_h * s.d_v * sizeof(float));
+  return align256((size_t)B * s.n_h * s.d_v * sizeof(float)) +
+         align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v));
 }
 size_t decode_ws(const Shape& s, int B, int64_t hint, int num_cu) {
   if (!force_generic() && decode_v3_supported(s)) return decode_v3_workspace(s, B, hint, num_cu);
@@ -176,28 +210,31 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
   const void* qsrc = q;
   bool q_f32 = storage_f32;
   if (from_hidden) {
+    // [c^Q (fp32) | q (fp32) | split partials of the linear layers]
     char* w = (char*)ws;
     const int qw = s.n_h * (s.d_h + s.d_r);
     const void* x = h_t;
     bool x_f32 = storage_f32;
     int K = s.d_model;
+    float* cq = (float*)w;
+    if (s.d_q > 0) w += align256((size_t)B * s.d_q * sizeof(float));
+    float* qf = (float*)w;
+    w += align256((size_t)B * qw * sizeof(float));
+    void* part = w;
     if (s.d_q > 0) {
-      float* cq = (float*)w;
-      w += align256((size_t)B * s.d_q * sizeof(float));
-      hipError_t e = launch_linear_generic(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, hs);
+      hipError_t e = linear(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, part, hs);
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
       x = cq;
       x_f32 = true;
       K = s.d_q;
     }
-    float* qf = (float*)w;
-    hipError_t e = launch_linear_generic(s, B, qw, K, x, x_f32, W_UQ, qf, hs);
+    hipError_t e = linear(s, B, qw, K, x, x_f32, W_UQ, qf, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
     qsrc = qf;
     q_f32 = true;
   }
-  if (!q_f32 && !force_generic() && proj_v3_supported(s))
-    return launched(launch_absorb_v3(s, B, qsrc, W_UK, pos, q_lat, q_pe, hs));
+  if (!force_generic() && proj_v3_supported(s))
+    return launched(launch_absorb_v3(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
   return launched(launch_absorb_generic(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
 }
 
@@ -233,12 +270,20 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
   const size_t D = (size_t)(s.d_c + s.d_r);
   if (from_hidden) {
     // c = x W_DKV^T and k = x W_KR^T into fp32 scratch, then rotate + write.
-    float* kc = (float*)ws;
     const int M = B * n_new;
+    float* kc = (float*)ws;
+    void* part = (char*)ws + align256((size_t)M * D * sizeof(float));
+    if (fused_kv(s, M)) {
+      // one [M, d_c + d_r] product: row i = [c_i | k_i]
+      hipError_t e = launch_gemm_v3(M, (int)D, s.d_c, s.d_model, h_t, false, W_DKV, W_KR, kc, part, hs);
+      if (e != hipSuccess) return MLA_ERR_LAUNCH;
+      return launched(launch_append_generic(s, B, n_new, kc, D, kc + s.d_c, D, true, cache, offsets,
+                                            lens, err_flag, hs));
+    }
     float* kr = kc + (size_t)M * s.d_c;
-    hipError_t e = launch_linear_generic(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, hs);
+    hipError_t e = linear(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
-    e = launch_linear_generic(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, hs);
+    e = linear(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
     return launched(launch_append_generic(s, B, n_new, kc, (size_t)s.d_c, kr, (size_t)s.d_r, true,
                                           cache, offsets, lens, err_flag, hs));
@@ -305,18 +350,20 @@ mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_l
     if (!W_O) return MLA_ERR_NULL;
     if (s.d_model < 1) return MLA_ERR_SHAPE;
   }
-  const size_t need = (u && !o) ? project_ws(s, B, true) : 0;
+  const size_t need = u ? project_ws(s, B, true) : 0;
   if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   DeviceInfo info;
   if ((st = device_ready(&info)) != MLA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
+  // workspace: [o when not given (fp32) | split partials of W_O]
   float* ob = o ? o : (float*)ws;
+  void* part = u ? (char*)ws + align256((size_t)B * s.n_h * s.d_v * sizeof(float)) : nullptr;
   hipError_t e = (!force_generic() && proj_v3_supported(s))
                      ? launch_uv_v3(s, B, o_lat, W_UV, ob, hs)
                      : launch_uv_generic(s, B, o_lat, W_UV, ob, hs);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (u) {
-    e = launch_linear_generic(s, B, s.d_model, s.n_h * s.d_v, ob, true, W_O, u, hs);
+    e = linear(s, B, s.d_model, s.n_h * s.d_v, ob, true, W_O, u, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -541,15 +541,26 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
   if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
 }
 
-__global__ void __launch_bounds__(128) k_combine(CombineArgs a) {
+// One workgroup per (head, sequence): 128 lanes x 4 columns.  The (m, l) of
+// all pieces are read in parallel and reduced to the common max M; each
+// piece's weight 2^(m - M) goes to LDS, then the partial rows are read eight
+// at a time so that many loads are in flight per lane.
+constexpr int CMB_THREADS = 128;
+constexpr int MAX_G = 256;   // pieces per sequence <= G <= MAX_G
+
+__global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
+  __shared__ float s_w[MAX_G];
+  __shared__ int s_slot[MAX_G];
+  __shared__ float s_red[2][2];
   const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t total = a.prefix[a.B];
   const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
   float4* out = (float4*)(a.o_lat + ((size_t)b * NH + h) * DC);
   if (p1 <= p0) {   // invalid length: NaN result (the error flag is set)
     const float nan = __builtin_nanf("");
-    out[threadIdx.x] = make_float4(nan, nan, nan, nan);
-    if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = nan;
+    out[tid] = make_float4(nan, nan, nan, nan);
+    if (tid == 0 && a.lse) a.lse[(size_t)b * NH + h] = nan;
     return;
   }
   if (a.ovf[b]) {
@@ -558,36 +569,81 @@ __global__ void __launch_bounds__(128) k_combine(CombineArgs a) {
   }
   const int G = a.G;
   const int g_lo = wg_of(p0, total, G);
-  const int g_hi = wg_of(p1 - 1, total, G);
+  const int npiece = wg_of(p1 - 1, total, G) - g_lo + 1;
+
+  // Workgroup g_lo's range holds row p0, so it is never empty.  Empty ranges
+  // (only when the total is below G) wrote nothing: they get weight 0 and
+  // read g_lo's finite partial instead of their own unwritten slot.
+  constexpr int PER = MAX_G / CMB_THREADS;
+  float m[PER];
+  int slot[PER];
   float M = -INFINITY;
-  for (int g = g_lo; g <= g_hi; ++g) {
-    if (range_start(g, total, G) == range_start(g + 1, total, G)) continue;
-    M = fmaxf(M, a.part_ml[(((size_t)g + b) * NH + h) * 2]);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * CMB_THREADS;
+    const int g = g_lo + i;
+    m[k] = -INFINITY;
+    slot[k] = g_lo + b;
+    if (i < npiece && range_start(g, total, G) != range_start(g + 1, total, G)) {
+      slot[k] = g + b;
+      m[k] = a.part_ml[((size_t)slot[k] * NH + h) * 2];
+    }
+    M = fmaxf(M, m[k]);
   }
+  M = wave_max(M);
+  if (lane == 0) s_red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(s_red[0][0], s_red[0][1]);
   float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * CMB_THREADS;
+    if (i < npiece) {
+      const float w = m[k] == -INFINITY ? 0.f : exp2f(m[k] - M);
+      if (w > 0.f) L += w * a.part_ml[((size_t)slot[k] * NH + h) * 2 + 1];
+      s_w[i] = w;
+      s_slot[i] = slot[k];
+    }
+  }
+  L = wave_sum(L);
+  if (lane == 0) s_red[1][wave] = L;
+  __syncthreads();
+  L = s_red[1][0] + s_red[1][1];
+
+  const float* po = a.part_o + (size_t)h * DC + 4 * tid;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int g = g_lo; g <= g_hi; ++g) {
-    if (range_start(g, total, G) == range_start(g + 1, total, G)) continue;
-    const size_t slot = (size_t)g + b;
-    const float m = a.part_ml[(slot * NH + h) * 2];
-    const float l = a.part_ml[(slot * NH + h) * 2 + 1];
-    const float w = exp2f(m - M);
-    L += l * w;
-    const float4 v = ((const float4*)(a.part_o + (slot * NH + h) * DC))[threadIdx.x];
+  int i = 0;
+  for (; i + 8 <= npiece; i += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *(const float4*)(po + (size_t)s_slot[i + j] * NH * DC);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = s_w[i + j];
+      acc.x += w * v[j].x;
+      acc.y += w * v[j].y;
+      acc.z += w * v[j].z;
+      acc.w += w * v[j].w;
+    }
+  }
+  for (; i < npiece; ++i) {
+    const float4 v = *(const float4*)(po + (size_t)s_slot[i] * NH * DC);
+    const float w = s_w[i];
     acc.x += w * v.x;
     acc.y += w * v.y;
     acc.z += w * v.z;
     acc.w += w * v.w;
   }
   const float inv = 1.f / L;
-  out[threadIdx.x] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
+  out[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (tid == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
 }
 
 int choose_groups(int64_t total_rows_hint, int num_cu) {
   int64_t g = (total_rows_hint + MIN_ROWS_PER_WG - 1) / MIN_ROWS_PER_WG;
   if (g < 1) g = 1;
   if (g > num_cu) g = num_cu;
+  if (g > MAX_G) g = MAX_G;
   return (int)g;
 }
 
@@ -642,7 +698,7 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   c.B = B;
   c.G = G;
   c.scale_log2 = a.scale_log2;
-  k_combine<<<dim3(NH, B), 128, 0, st>>>(c);
+  k_combine<<<dim3(NH, B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();
 }
 

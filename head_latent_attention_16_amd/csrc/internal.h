@@ -47,9 +47,18 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
 
 // bf16 per-head projections at n_h = 128, d_h = d_v = 128, d_c = 512, d_r = 64.
 bool proj_v3_supported(const Shape& s);
-// q (bf16) [B, n_h, d_h + d_r] -> q_lat, q_pe (bf16).
-hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, const void* W_UK,
+// q (bf16, or fp32 when q_f32) [B, n_h, d_h + d_r] -> q_lat, q_pe (bf16).
+hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, const void* W_UK,
                             const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st);
+
+// bf16-weight linear layer Y[M,N] (fp32) = X[M,K] . W^T, X bf16 or fp32.
+// Rows n < N1 of W come from W1 (stride K), rows >= N1 from W2 (W2 == NULL:
+// all rows from W1).  Needs N % 32 == 0 and K % 256 == 0, and a workspace of
+// gemm_v3_workspace(M, N, K) bytes for the split partials (may be 0).
+bool gemm_v3_supported(int M, int N, int K);
+size_t gemm_v3_workspace(int M, int N, int K);
+hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32, const void* W1,
+                          const void* W2, float* Y, void* ws, hipStream_t st);
 // o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 in and out).
 hipError_t launch_uv_v3(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
                         hipStream_t st);

@@ -32,8 +32,11 @@ constexpr int ABS_COLS = 256;
 constexpr int ABS_ROWB = ABS_COLS * 2 + 32;   // 544
 constexpr int ABS_THREADS = 256;
 
+// q is bf16, or fp32 (QF32: the query computed from the hidden state), which
+// enters the bf16 product as hi + lo (two MFMAs per step).
+template <bool QF32>
 __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_base,
-                                                           const __bf16* __restrict__ q,
+                                                           const void* __restrict__ qv,
                                                            const __bf16* __restrict__ W_UK,
                                                            const int32_t* __restrict__ pos,
                                                            __bf16* __restrict__ q_lat,
@@ -64,14 +67,23 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
   for (int nb = 0; nb * 32 < B; ++nb) {
     const int bq = nb * 32 + (lane & 31);
     const bool bok = bq < B;
-    // B operand: q_C[bq][h][16 ks + 8 g32 .. +8]
-    bf16x8 qb[DH / 16];
+    // B operand: q_C[bq][h][16 ks + 8 g32 .. +8] (and its low part)
+    bf16x8 qb[DH / 16], ql[QF32 ? DH / 16 : 1];
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
-      if (bok)
-        qb[ks] = *(const bf16x8*)(q + ((size_t)bq * NH + h) * QW + 16 * ks + 8 * g32);
-      else
-        qb[ks] = bf16x8{};
+      const size_t e0 = ((size_t)(bok ? bq : 0) * NH + h) * QW + 16 * ks + 8 * g32;
+      if constexpr (QF32) {
+        const float* qf = (const float*)qv + e0;
+        const floatx4 x0 = *(const floatx4*)qf, x1 = *(const floatx4*)(qf + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = bok ? (e < 4 ? x0[e] : x1[e - 4]) : 0.f;
+          qb[ks][e] = (__bf16)x;
+          ql[ks][e] = (__bf16)(x - (float)qb[ks][e]);
+        }
+      } else {
+        qb[ks] = bok ? *(const bf16x8*)((const __bf16*)qv + e0) : bf16x8{};
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -87,6 +99,7 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
+        if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], acc, 0, 0, 0);
       }
       // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
       if (bok) {
@@ -107,8 +120,15 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
       const int b = idx / (DR / 2), i = idx % (DR / 2);
       float cs, sn;
       rope_cos_sin(pos[b], i, DR, rope_base, &cs, &sn);
-      const __bf16* qr = q + ((size_t)b * NH + h) * QW + DH;
-      const float lo = (float)qr[i], hi = (float)qr[DR / 2 + i];
+      const size_t e0 = ((size_t)b * NH + h) * QW + DH;
+      float lo, hi;
+      if constexpr (QF32) {
+        lo = ((const float*)qv)[e0 + i];
+        hi = ((const float*)qv)[e0 + DR / 2 + i];
+      } else {
+        lo = (float)((const __bf16*)qv)[e0 + i];
+        hi = (float)((const __bf16*)qv)[e0 + DR / 2 + i];
+      }
       __bf16* out = q_pe + ((size_t)b * NH + h) * DR;
       out[i] = (__bf16)(lo * cs - hi * sn);
       out[DR / 2 + i] = (__bf16)(hi * cs + lo * sn);
@@ -196,10 +216,15 @@ bool proj_v3_supported(const Shape& s) {
   return s.bf16 && s.n_h == NH && s.d_c == DC && s.d_r == DR && s.d_h == DH && s.d_v == DV;
 }
 
-hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, const void* W_UK,
+hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, const void* W_UK,
                             const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st) {
-  k_absorb_v3<<<dim3(NH, DC / ABS_COLS), ABS_THREADS, 0, st>>>(
-      B, s.rope_base, (const __bf16*)q, (const __bf16*)W_UK, pos, (__bf16*)q_lat, (__bf16*)q_pe);
+  const dim3 grid(NH, DC / ABS_COLS);
+  if (q_f32)
+    k_absorb_v3<true><<<grid, ABS_THREADS, 0, st>>>(B, s.rope_base, q, (const __bf16*)W_UK, pos,
+                                                    (__bf16*)q_lat, (__bf16*)q_pe);
+  else
+    k_absorb_v3<false><<<grid, ABS_THREADS, 0, st>>>(B, s.rope_base, q, (const __bf16*)W_UK, pos,
+                                                     (__bf16*)q_lat, (__bf16*)q_pe);
   return hipGetLastError();
 }
 

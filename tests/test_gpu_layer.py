@@ -1,0 +1,72 @@
+"""GPU parity of the full decode-layer step at DeepSeek-V3 dims (bf16 weights):
+query path from the hidden state, append of the new token's latent row,
+latent attention, up-projection and output projection, against the fp64
+oracle's explicit route.  The batch sizes cover one row and more than one
+128-row block of the linear layers (a partial second block)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from head_latent_attention_16_amd import _lib as L
+from head_latent_attention_16_amd import inputs as I
+
+from gpu_support import compare, dev, dims_of, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,lo,hi,check", [(1, 40, 40, [0]), (130, 1, 90, [0, 31, 32, 127, 128, 129])])
+def test_layer_step_v3(B, lo, hi, check):
+    w = I.layer(seed=3, B=B, lo=lo, hi=hi, spare=2)
+    say(f"layer: B={B} T_prior in [{lo},{hi}] checked seqs {check}")
+    d = dims_of(w)
+    dd = w.dims
+    n_h, d_c, d_r = dd["n_h"], dd["d_c"], dd["d_r"]
+    cache, offsets, lens = dev(w.cache), dev(w.offsets), dev(w.lens)
+    W = {k: dev(v) for k, v in w.W.items()}
+    h_t = dev(w.h_t)
+    pos = lens.clone()
+    q_lat = torch.empty(B, n_h, d_c, dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(B, n_h, d_r, dtype=torch.bfloat16, device="cuda")
+    L.absorb_q(d, q_lat, q_pe, W["W_UK"], pos, h_t=h_t, W_DQ=W["W_DQ"], W_UQ=W["W_UQ"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.append_cache(d, cache, offsets, lens, 1, h_t=h_t, W_DKV=W["W_DKV"], W_KR=W["W_KR"],
+                   err_flag=err)
+    o_lat = torch.empty(B, n_h, d_c, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
+    L.decode_attn(d, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
+                  total_rows_hint=int(w.total_rows) + B, err_flag=err)
+    o = torch.empty(B, n_h, dd["d_v"], dtype=torch.float32, device="cuda")
+    u = torch.empty(B, dd["d_model"], dtype=torch.float32, device="cuda")
+    L.project_out(d, o_lat, W["W_UV"], o=o, u=u, W_O=W["W_O"])
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(lens.cpu().numpy(), w.lens + 1)
+
+    Wf = {k: w.f64(v) for k, v in w.W.items()}
+    prior_c = {b: w.f64(w.seq_rows(b))[:, :d_c] for b in check}
+    prior_k = {b: w.f64(w.seq_rows(b))[:, d_c:] for b in check}
+    ref = O.layer_step(w.f64(w.h_t), Wf, prior_c, prior_k, dd, O.scale_for(dd["d_h"], d_r),
+                       seqs=check)
+    got_cache = host_f64(cache)
+    for b in check:
+        r = ref[b]
+        # the appended row: the projections rounded once to bf16 (k after RoPE)
+        row = got_cache[int(w.offsets[b]) + int(w.lens[b])]
+        cmax = np.max(np.abs(r["c_new"]))
+        assert np.max(np.abs(row[:d_c] - r["c_new"])) <= 2.0 ** -8 * cmax + 1e-6, b
+        kmax = np.max(np.abs(r["k_new"]))
+        assert np.max(np.abs(row[d_c:] - r["k_new"])) <= 2.0 ** -7 * kmax + 1e-6, b
+        # rows other than the new one are untouched
+        t0 = int(w.offsets[b])
+        assert np.array_equal(got_cache[t0:t0 + int(w.lens[b])], w.f64(w.seq_rows(b))), b
+        # query path + absorption: q_lat within one bf16 rounding of W_UK^T q_C
+        want = O.absorb_query(r["q_C"], Wf["W_UK"])
+        got = host_f64(q_lat[b])
+        assert np.max(np.abs(got - want)) <= 2.0 ** -7 * np.max(np.abs(want)), b
+        compare(host_f64(o_lat[b]), r["o_lat"], f"o_lat[{b}]")
+        compare(host_f64(o[b]), r["o"], f"o[{b}]")
+        compare(host_f64(lse[b]), r["lse"], f"lse[{b}]")
+        compare(host_f64(u[b]), r["u"], f"u[{b}]")
