@@ -65,6 +65,8 @@ constexpr int PV_PF = 4;                              // PV fragment pairs in fl
 constexpr float OVF_TH = 64.0f;                       // log2 units
 constexpr int MIN_ROWS_PER_WG = 256;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
 static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 
@@ -289,7 +291,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int t0 = (int)(pos - seq_begin);
     const int seg_len = (int)(seg_end - pos);
     const int ntiles = (seg_len + TILE - 1) / TILE;
-    const bool last_partial = (seg_len % TILE) != 0;
     const char* rows = a.cache + ((size_t)a.offsets[b] + (size_t)t0) * ROWB;
 
     if (!first_segment) barrier_all_lds();   // previous segment's tiles fully consumed
@@ -305,52 +306,47 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         q[kk] = kk < DC / 16 ? ql[2 * kk + g32] : qp[2 * (kk - DC / 16) + g32];
     }
 
-    auto issue_tile = [&](int tile) {
-      const uint32_t stage_lds = lds0 + (uint32_t)((tile % NSTAGE) * TILEB);
-      const char* tbase = rows + (size_t)tile * TILEB;
-      const int nvalid = seg_len - tile * TILE;
+    // Every tile index t gets exactly DMA_PER_WAVE DMA instructions per wave,
+    // issued in order t = 0, 1, 2, ...  Tile t goes into stage t % NSTAGE.
+    // Row clamping keeps every source byte inside the piece:
+    //  * t < ntiles, partial tile: lanes whose chunk lies in a row at or past
+    //    nvalid load the last valid 16 bytes instead, so the whole stage
+    //    holds finite cache values (their scores are masked out);
+    //  * t >= ntiles (past the end of the piece): a copy of the last tile
+    //    (just fetched, so served by L2) into the stage that tile t would
+    //    use -- it is free, and no later tile of this piece uses it.
+    // With a fixed count per tile the wait for tile `it` is always the same.
+    auto dma_src = [&](int t, const char*& tbase, uint32_t& bound) {
+      const int ts = t < ntiles ? t : ntiles - 1;
+      tbase = rows + (size_t)ts * TILEB;
+      const int nv = seg_len - ts * TILE;
+      bound = nv >= TILE ? (uint32_t)TILEB - 16u : (uint32_t)(nv * ROWB - 16);
+    };
+    auto issue_tile = [&](int t) {
+      const char* tbase;
+      uint32_t bound;
+      dma_src(t, tbase, bound);
+      const uint32_t stage_lds = lds0 + (uint32_t)((t % NSTAGE) * TILEB);
       // All offsets are read before the first DMA: the DMA asm is a memory
       // barrier for the compiler, so interleaved reads would each wait alone.
       uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = dma_tab[k][threadIdx.x];
-      if (nvalid >= TILE) {
+      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_tab[k][threadIdx.x], bound);
 #pragma unroll
-        for (int k = 0; k < DMA_PER_WAVE; ++k)
-          dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
-      } else {
-        // Partial tile (the last of a piece): rows nvalid..31 of the stage are
-        // zeroed (finite, and their scores are masked out), and only lanes
-        // whose chunk lies in a row below nvalid load -- chunk p is in row
-        // p / 72, so the test is the uniform bound p < 72 * nvalid.  No byte
-        // outside the sequence is read.  Such a tile may issue fewer
-        // instructions; waits never count on its instructions.
-        MLA_LDS char* st = (MLA_LDS char*)lds + (tile % NSTAGE) * TILEB;
-        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-        for (int off = nvalid * ROWB + (int)threadIdx.x * 16; off < TILEB; off += THREADS * 16)
-          *(MLA_LDS floatx4*)(st + off) = zero;
-#pragma unroll
-        for (int k = 0; k < DMA_PER_WAVE; ++k) {
-          const int bound = nvalid * CHUNKS - (wave * DMA_PER_WAVE + k) * 64;
-          if (lane < bound)
-            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
-        }
-      }
+      for (int k = 0; k < DMA_PER_WAVE; ++k)
+        dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
     };
-    // Wait for tile `it`: tiles it+1, it+2 may still be in flight; only full
-    // ones are counted (a partial tile is the newest, so under-counting it only
-    // makes the wait stricter).
-    auto wait_tile = [&](int it) {
-      int ahead_full = 0;
-      for (int t = it + 1; t <= it + 2 && t < ntiles; ++t)
-        if (!(t == ntiles - 1 && last_partial)) ++ahead_full;
-      if (ahead_full >= 2) wait_vm_then_barrier<2 * DMA_PER_WAVE>();
-      else if (ahead_full == 1) wait_vm_then_barrier<DMA_PER_WAVE>();
-      else wait_vm_then_barrier<0>();
-    };
+    // Wait for tile `it`: the tiles it+1 and it+2 were issued after it.
+    auto wait_tile = [&]() { wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>(); };
 
-    // Three tiles ahead: tile it+3 goes into the stage of tile it-1.
-    for (int t = 0; t < NSTAGE - 1 && t < ntiles; ++t) issue_tile(t);
+    // Three tiles ahead: tile it+3 goes into the stage of tile it-1.  The Q
+    // loads are consumed (waited for) right after tile 0's DMAs: the compiler
+    // counts only its own loads when it places waits, so a Q use after the
+    // tile 1 and 2 DMAs would make it wait for those tiles too.
+    issue_tile(0);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(q[kk]));
+    for (int t = 1; t < NSTAGE - 1; ++t) issue_tile(t);
 
     floatx16 O[DC / 32];
 #pragma unroll
@@ -360,9 +356,15 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     float m_ref = 0.f;         // reference max of scaled scores (log2 units)
     float l_run = 0.f;         // this lane's share of the sum of weights
 
+    float s_thr = INFINITY;    // raw-score bound of the overflow check
+
     for (int it = 0; it < ntiles; ++it) {
-      wait_tile(it);
-      if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1);
+      wait_tile();
+      // Tile nt = it+3 goes into the stage of tile it-1 (free: every wave is
+      // past the barrier above).  Its nine DMA instructions per wave are
+      // spread over this tile's PV loop: the address unit moves 64 B per
+      // clock, so issuing them back to back stalls the wave for ~600 cycles.
+      const int nt = it + NSTAGE - 1;
       const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
 
       // ---- S^T = K . Q^T, fragments loaded QK_PF steps ahead ----
@@ -403,58 +405,97 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       }
 
       // ---- softmax: lane holds head n32, rows 8 (i/4) + 4 g32 + i%4 ----
-      // One separately rounded product per score feeds both the max and the
-      // exponent, so the maximal score gets exactly exp2(0) = 1; l sums the
-      // same bf16-rounded weights that enter PV, so O / l is an exactly
-      // normalised average of the rows.
+      // The first tile fixes the reference m_ref as the max of separately
+      // rounded products S * scale * log2(e).  Every weight is then
+      // bf16(2^fma(S, scale log2 e, -m_ref)); at the maximal score the fma
+      // leaves only the product's rounding error, so that weight rounds to
+      // exactly 1.  l sums the same bf16 weights that enter PV, so O / l is
+      // an exactly normalised average of the rows.  Later tiles only check
+      // that no score exceeds the reference by more than 2^64 (else the
+      // sequence is flagged for the fallback); rows past nvalid (zero-filled
+      // in a partial tile) get weight 0.
       const int nvalid = seg_len - it * TILE;
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * g32 + (i & 3);
-        const float v = __fmul_rn(S[i], a.scale_log2);
-        S[i] = row < nvalid ? v : -INFINITY;
-        mloc = fmaxf(mloc, S[i]);
-      }
+      const bool full = nvalid >= TILE;
+      auto row_of = [&](int i) { return 8 * (i >> 2) + 4 * g32 + (i & 3); };
       if (it == 0) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = __fmul_rn(S[i], a.scale_log2);
+          mloc = fmaxf(mloc, row_of(i) < nvalid ? v : -INFINITY);
+        }
         m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      } else if (__any(mloc > m_ref + OVF_TH)) {
-        if (lane == 0) a.ovf[b] = 1;
+        s_thr = (m_ref + OVF_TH) / a.scale_log2;
+      } else {
+        float smax = -INFINITY;
+        if (full) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) smax = fmaxf(smax, S[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) smax = fmaxf(smax, row_of(i) < nvalid ? S[i] : -INFINITY);
+        }
+        if (__any(smax > s_thr)) {
+          if (lane == 0) a.ovf[b] = 1;
+        }
       }
       bf16x8 P[2];
-      float lsum = 0.f;
+      {
+        float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(S[i] - m_ref);
-        lsum += (float)pb;
-        P[i >> 3][i & 7] = pb;
+        for (int i = 0; i < 16; ++i) x[i] = fmaf(S[i], a.scale_log2, -m_ref);
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = row_of(i) < nvalid ? x[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) P[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x[i]);
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bf16x2 pr = {P[j >> 2][2 * (j & 3)], P[j >> 2][2 * (j & 3) + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
+        }
       }
-      l_run += lsum;
 
       // ---- O^T += C^T . P^T over 2 row halves x 16 column blocks ----
+      {
+        const char* tbase;
+        uint32_t bound;
+        dma_src(nt, tbase, bound);
+        const uint32_t stage_lds = lds0 + (uint32_t)((nt % NSTAGE) * TILEB);
+        uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-      for (int s = 0; s < 2 * (DC / 32); ++s) {
-        const int kk2 = s / (DC / 32), cb = s % (DC / 32);
-        const bf16x4 lo = pa[s % PV_PF][0], hi = pa[s % PV_PF][1];
-        const bf16x8 cf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int ns = s + PV_PF;
-        if (ns < 2 * (DC / 32)) {
-          const int nk2 = ns / (DC / 32), ncb = ns % (DC / 32);
-          const MLA_LDS char* p0 = T + tr_base[0][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
-          const MLA_LDS char* p1 = T + tr_base[1][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
-          pa[s % PV_PF][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
-          pa[s % PV_PF][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
+        for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_tab[k][threadIdx.x], bound);
+#pragma unroll
+        for (int s = 0; s < 2 * (DC / 32); ++s) {
+          const int kk2 = s / (DC / 32), cb = s % (DC / 32);
+          const bf16x4 lo = pa[s % PV_PF][0], hi = pa[s % PV_PF][1];
+          const bf16x8 cf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int ns = s + PV_PF;
+          if (ns < 2 * (DC / 32)) {
+            const int nk2 = ns / (DC / 32), ncb = ns % (DC / 32);
+            const MLA_LDS char* p0 = T + tr_base[0][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
+            const MLA_LDS char* p1 = T + tr_base[1][ncb & 1] + nk2 * 16 * ROWB + ncb * 64;
+            pa[s % PV_PF][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
+            pa[s % PV_PF][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
+          }
+          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
+          if (s % 3 == 2 && s / 3 < DMA_PER_WAVE)
+            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024), off[s / 3], tbase);
         }
-        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
 #pragma unroll
-      for (int s2 = 0; s2 < 2 * (DC / 32) - PV_PF; ++s2) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        for (int s2 = 0; s2 < 2 * (DC / 32) - PV_PF; ++s2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PV_PF, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, PV_PF, 1);
     }
+    // DMAs issued during the last tiles only fill stages this piece no
+    // longer reads; they must land before a next piece reuses the stages.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- emit the partial (unnormalised O, m, l) of this piece ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
