@@ -67,6 +67,7 @@ constexpr int MIN_ROWS_PER_WG = 256;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
 static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 
@@ -175,10 +176,12 @@ __device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const 
   // inline asm so that the compiler does not add a conservative vmcnt(0)
   // before every LDS read (it cannot see which stage the DMA targets);
   // completion is tracked by hand with s_waitcnt vmcnt before the barrier.
+  // No "memory" clobber: the target stage is never read between a DMA and
+  // the barrier asm (itself a compiler memory barrier) that precedes its
+  // first use, and without it LDS reads may be scheduled across the DMA.
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
-               : "memory");
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base)));
 }
 
 template <int N>
@@ -189,6 +192,23 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
 
 __device__ __forceinline__ void barrier_all_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The QK accumulator S is kept in VGPRs with MFMAs written as asm: the
+// builtin form puts every accumulator in AGPRs, and with the 256-register
+// O accumulator there S would displace an O block and be copied back and
+// forth every tile.  Hazards the compiler cannot see in asm are covered by
+// construction: the first MFMA takes srcC = 0 (no VALU-written input), a
+// chain only accumulates into the same registers (forwarded by the
+// hardware), and mfma_drain's 24 wait states precede any other use of S.
+__device__ __forceinline__ void mfma_first(floatx16& S, const bf16x8& A, const bf16x8& B) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(A), "v"(B));
+}
+__device__ __forceinline__ void mfma_acc(floatx16& S, const bf16x8& A, const bf16x8& B) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(A), "v"(B));
+}
+__device__ __forceinline__ void mfma_drain(floatx16& S) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S));
 }
 
 // Bank swizzle of a 1152-byte row in LDS.  gfx950's LDS has 64 four-byte
@@ -210,8 +230,6 @@ __device__ __forceinline__ int swz(int r) {
 // steps ahead of the MFMA that consumes them.
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
-  // Per-lane DMA source offsets, kept in LDS rather than in VGPRs.
-  __shared__ __attribute__((aligned(16))) uint32_t dma_tab[DMA_PER_WAVE][THREADS];
 
   const int g = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,15 +247,16 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
   // DMA: wave-instruction j = 9 wave + k covers LDS chunks [64 j, 64 j + 64);
   // lane i fills chunk p = 64 j + i, which holds logical chunk
-  // (p % 72) ^ swz(row) of row p / 72.
-#pragma unroll
-  for (int k = 0; k < DMA_PER_WAVE; ++k) {
-    const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
-    const int r = p / CHUNKS;
-    const int c = (p % CHUNKS) ^ swz(r);
-    dma_tab[k][threadIdx.x] = (uint32_t)(r * ROWB + c * 16);
-  }
-  // (each lane reads back only its own entries: no barrier needed)
+  // (p % 72) ^ swz(row) of row p / 72.  The 64 chunks span at most two rows
+  // (72 > 64), so everything but a per-lane select is wave-uniform.
+  auto dma_off = [&](int k) -> uint32_t {
+    const int base = (wave * DMA_PER_WAVE + k) * 64;
+    const int r0 = base / CHUNKS, m0 = base % CHUNKS;
+    const int qc = m0 + lane;
+    const bool next = qc >= CHUNKS;
+    const int c = (next ? qc - CHUNKS : qc) ^ (next ? swz(r0 + 1) : swz(r0));
+    return (uint32_t)((next ? (r0 + 1) * ROWB : r0 * ROWB) + c * 16);
+  };
 
   // QK A-fragment (32x32x16): row n32, logical chunk 2 kk + g32 stored at
   // (2 kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
@@ -327,11 +346,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       uint32_t bound;
       dma_src(t, tbase, bound);
       const uint32_t stage_lds = lds0 + (uint32_t)((t % NSTAGE) * TILEB);
-      // All offsets are read before the first DMA: the DMA asm is a memory
-      // barrier for the compiler, so interleaved reads would each wait alone.
       uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_tab[k][threadIdx.x], bound);
+      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_off(k), bound);
 #pragma unroll
       for (int k = 0; k < DMA_PER_WAVE; ++k)
         dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
@@ -355,45 +372,153 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
     float m_ref = 0.f;         // reference max of scaled scores (log2 units)
     float l_run = 0.f;         // this lane's share of the sum of weights
-
     float s_thr = INFINITY;    // raw-score bound of the overflow check
+    bool ovf_any = false;      // a score of this lane exceeded it
 
-    for (int it = 0; it < ntiles; ++it) {
-      wait_tile();
-      // Tile nt = it+3 goes into the stage of tile it-1 (free: every wave is
-      // past the barrier above).  Its nine DMA instructions per wave are
-      // spread over this tile's PV loop: the address unit moves 64 B per
-      // clock, so issuing them back to back stalls the wave for ~600 cycles.
-      const int nt = it + NSTAGE - 1;
-      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
-
-      // ---- S^T = K . Q^T, fragments loaded QK_PF steps ahead ----
-      floatx16 S;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    // ---- S^T = K . Q^T of tile t, fragments loaded QK_PF steps ahead ----
+    auto qk = [&](int t, floatx16& S) {
+      const MLA_LDS char* T = (const MLA_LDS char*)lds + (t % NSTAGE) * TILEB;
       bf16x8 kf[QK_PF];
 #pragma unroll
       for (int j = 0; j < QK_PF; ++j)
         kf[j] = *(const MLA_LDS bf16x8*)(T + qk_off[j & 3] + (j >> 2) * 128);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % QK_PF], q[kk], S, 0, 0, 0);
+        if (kk == 0)
+          mfma_first(S, kf[0], q[0]);
+        else
+          mfma_acc(S, kf[kk % QK_PF], q[kk]);
         const int nk = kk + QK_PF;
         if (nk < KSTEPS)
           kf[kk % QK_PF] = *(const MLA_LDS bf16x8*)(T + qk_off[nk & 3] + (nk >> 2) * 128);
       }
-      // Schedule: QK_PF fragment loads, then (MFMA, load) pairs, then the
-      // remaining MFMAs -- each fragment is in flight for QK_PF steps.
+      mfma_drain(S);
+    };
+    // Schedule of one QK block: QK_PF fragment loads, then (MFMA, load)
+    // pairs, then the remaining MFMAs.
+    auto qk_schedule = [&]() {
       __builtin_amdgcn_sched_group_barrier(0x100, QK_PF, 0);
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS - QK_PF; ++kk) {
+      for (int kk = 0; kk < KSTEPS; ++kk) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kk < KSTEPS - QK_PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, QK_PF, 0);
+    };
 
-      // ---- PV fragments for the first column blocks go out before the
-      //      softmax so their latency hides behind it ----
+    // ---- softmax of one tile: lane holds head n32, rows 8 (i/4) + 4 g32 + i%4 ----
+    // Every weight is bf16(2^fma(S, scale log2 e, -m_ref)) with m_ref fixed by
+    // the first tile as the max of separately rounded products; at the
+    // maximal score the fma leaves only that product's rounding error, so the
+    // weight rounds to exactly 1.  l sums the same bf16 weights that enter PV,
+    // so O / l is an exactly normalised average of the rows.  A score more
+    // than 2^64 above the reference flags the piece for the fallback.  Rows
+    // at or past nvalid (a partial tile) get weight 0.  No branches: the
+    // instructions interleave with the next tile's QK MFMAs.
+    auto row_of = [&](int i) { return 8 * (i >> 2) + 4 * g32 + (i & 3); };
+    // weights of scores 2j, 2j+1 -> P pair j; smax tracks the unmasked max
+    auto sm_pair = [&](const floatx16& S, int j, int nvalid, bf16x8 (&P)[2], float& smax) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * j + e;
+        const bool ok = row_of(i) < nvalid;
+        smax = fmaxf(smax, ok ? S[i] : -INFINITY);
+        const float x = ok ? fmaf(S[i], a.scale_log2, -m_ref) : -INFINITY;
+        P[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+      }
+    };
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    auto sm_sum = [&](const bf16x8 (&P)[2], int j) {
+      const bf16x2 pr = {P[j >> 2][2 * (j & 3)], P[j >> 2][2 * (j & 3) + 1]};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
+    };
+    auto softmax = [&](const floatx16& S, int nvalid, bf16x8 (&P)[2]) {
+      float smax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm_pair(S, j, nvalid, P, smax);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm_sum(P, j);
+      ovf_any = ovf_any || (smax > s_thr);
+    };
+
+    // ---- prologue: QK of tile 0 and the reference max ----
+    floatx16 S_cur;
+    wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>();   // tile 0 landed
+    qk(0, S_cur);
+    qk_schedule();
+    {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = __fmul_rn(S_cur[i], a.scale_log2);
+        mloc = fmaxf(mloc, row_of(i) < seg_len ? v : -INFINITY);
+      }
+      m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      s_thr = (m_ref + OVF_TH) / a.scale_log2;
+    }
+
+    // ---- software pipeline: [QK(it+1) || softmax(it)], then PV(it) ----
+    for (int it = 0; it < ntiles; ++it) {
+      const int nvalid = seg_len - it * TILE;
+      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
+      bf16x8 P[2];
+      floatx16 S_next;
+      // (The empty asm statements pin the softmax inside each branch: the
+      // compiler would otherwise hoist the common code above the branch, out
+      // of reach of the QK MFMAs it is meant to overlap.)
+      if (it + 1 < ntiles) {
+        // Tile it+1 landed (only tile it+2 was issued after it); the barrier
+        // also means every wave is past PV(it-1), so that tile's stage may be
+        // refilled below.
+        wait_vm_then_barrier<(NSTAGE - 3) * DMA_PER_WAVE>();
+        floatx16 Sc = S_cur;
+        asm volatile("" : "+v"(Sc));
+        // QK of tile it+1 with the softmax of tile it in its MFMA gaps: one
+        // pair of weights after each odd MFMA, their row sums later; the
+        // scheduling barriers keep every step where it is written, so the
+        // fragment prefetch and the VALU placement stay as planned.
+        const MLA_LDS char* Tn = (const MLA_LDS char*)lds + ((it + 1) % NSTAGE) * TILEB;
+        bf16x8 kf[QK_PF];
+#pragma unroll
+        for (int j = 0; j < QK_PF; ++j)
+          kf[j] = *(const MLA_LDS bf16x8*)(Tn + qk_off[j & 3] + (j >> 2) * 128);
+        // Tile it is full here (only the last tile of a piece can be
+        // partial, and it takes the other branch): no row masking.  Each
+        // weight's fma, exp2, bf16 packing and row sum sit several MFMAs
+        // apart, so no VALU instruction waits on the one before it.
+        float smax = -INFINITY;
+        float x[16], e[16];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          if (kk == 0)
+            mfma_first(S_next, kf[0], q[0]);
+          else
+            mfma_acc(S_next, kf[kk % QK_PF], q[kk]);
+          const int nk = kk + QK_PF;
+          if (nk < KSTEPS)
+            kf[kk % QK_PF] = *(const MLA_LDS bf16x8*)(Tn + qk_off[nk & 3] + (nk >> 2) * 128);
+          if (kk < 16) {
+            x[kk] = fmaf(Sc[kk], a.scale_log2, -m_ref);
+            if (kk & 1) smax = fmaxf(smax, fmaxf(Sc[kk - 1], Sc[kk]));
+          }
+          if (kk >= 4 && kk < 20) e[kk - 4] = __builtin_amdgcn_exp2f(x[kk - 4]);
+          if (kk >= 9 && kk < 25 && (kk & 1)) {
+            const int j = (kk - 9) / 2;
+            P[j >> 2][2 * (j & 3)] = (__bf16)e[2 * j];
+            P[j >> 2][2 * (j & 3) + 1] = (__bf16)e[2 * j + 1];
+          }
+          if (kk >= 26 && kk < 34) sm_sum(P, kk - 26);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_drain(S_next);
+        ovf_any = ovf_any || (smax > s_thr);
+      } else {
+        barrier_all_lds();
+        floatx16 Sc = S_cur;
+        asm volatile("" : "+v"(Sc));
+        softmax(Sc, nvalid, P);
+      }
+
+      // ---- PV fragments for the first column blocks ----
       bf16x4 pa[PV_PF][2];
 #pragma unroll
       for (int j = 0; j < PV_PF; ++j) {
@@ -404,69 +529,18 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         pa[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
       }
 
-      // ---- softmax: lane holds head n32, rows 8 (i/4) + 4 g32 + i%4 ----
-      // The first tile fixes the reference m_ref as the max of separately
-      // rounded products S * scale * log2(e).  Every weight is then
-      // bf16(2^fma(S, scale log2 e, -m_ref)); at the maximal score the fma
-      // leaves only the product's rounding error, so that weight rounds to
-      // exactly 1.  l sums the same bf16 weights that enter PV, so O / l is
-      // an exactly normalised average of the rows.  Later tiles only check
-      // that no score exceeds the reference by more than 2^64 (else the
-      // sequence is flagged for the fallback); rows past nvalid (zero-filled
-      // in a partial tile) get weight 0.
-      const int nvalid = seg_len - it * TILE;
-      const bool full = nvalid >= TILE;
-      auto row_of = [&](int i) { return 8 * (i >> 2) + 4 * g32 + (i & 3); };
-      if (it == 0) {
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = __fmul_rn(S[i], a.scale_log2);
-          mloc = fmaxf(mloc, row_of(i) < nvalid ? v : -INFINITY);
-        }
-        m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        s_thr = (m_ref + OVF_TH) / a.scale_log2;
-      } else {
-        float smax = -INFINITY;
-        if (full) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) smax = fmaxf(smax, S[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) smax = fmaxf(smax, row_of(i) < nvalid ? S[i] : -INFINITY);
-        }
-        if (__any(smax > s_thr)) {
-          if (lane == 0) a.ovf[b] = 1;
-        }
-      }
-      bf16x8 P[2];
-      {
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = fmaf(S[i], a.scale_log2, -m_ref);
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = row_of(i) < nvalid ? x[i] : -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) P[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x[i]);
-        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16x2 pr = {P[j >> 2][2 * (j & 3)], P[j >> 2][2 * (j & 3) + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
-        }
-      }
-
       // ---- O^T += C^T . P^T over 2 row halves x 16 column blocks ----
+      // Tile it+3 goes into the stage of tile it-1; its nine DMA instructions
+      // per wave are spread over the loop: the address unit moves 64 B per
+      // clock, so issuing them back to back stalls the wave for ~600 cycles.
       {
+        const int nt = it + NSTAGE - 1;
         const char* tbase;
         uint32_t bound;
         dma_src(nt, tbase, bound);
         const uint32_t stage_lds = lds0 + (uint32_t)((nt % NSTAGE) * TILEB);
-        uint32_t off[DMA_PER_WAVE];
-#pragma unroll
-        for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_tab[k][threadIdx.x], bound);
+        // DMA k goes out after MFMA 3k+2 (its source offset is recomputed
+        // there: a few VALU instructions in the MFMA gaps, no registers held).
 #pragma unroll
         for (int s = 0; s < 2 * (DC / 32); ++s) {
           const int kk2 = s / (DC / 32), cb = s % (DC / 32);
@@ -482,7 +556,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
           }
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
           if (s % 3 == 2 && s / 3 < DMA_PER_WAVE)
-            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024), off[s / 3], tbase);
+            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024),
+                    min(dma_off(s / 3), bound), tbase);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
 #pragma unroll
@@ -492,6 +567,10 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, PV_PF, 1);
       }
+      S_cur = S_next;
+    }
+    if (__any(ovf_any)) {
+      if (lane == 0) a.ovf[b] = 1;
     }
     // DMAs issued during the last tiles only fill stages this piece no
     // longer reads; they must land before a next piece reuses the stages.
