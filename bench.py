@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="launch each kernel from the host")
     return p.parse_args()
 
 
@@ -161,26 +162,19 @@ def main():
     ws_prj = torch.empty(max(1, lib.mla_project_out_workspace(ctypes.byref(dims), B, int(layer))),
                          dtype=torch.uint8, device="cuda")
 
-    ev = []
-
-    def step(i, timed):
-        s = sets[i % copies]
+    def step(c):
+        """One pass of the hot path over input copy c (launches only)."""
+        s = sets[c]
         if layer:
-            pos[i % copies].copy_(s["lens"])   # query position = current length
-            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[i % copies], h_t=s["h_t"], W_DQ=s["W_DQ"],
+            pos[c].copy_(s["lens"])   # query position = current length
+            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[c], h_t=s["h_t"], W_DQ=s["W_DQ"],
                        W_UQ=s["W_UQ"], ws=ws_abs)
             L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
                            W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
         else:
             L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["lens"], q=s["q"])
-        if timed:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
         L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
                       total_rows_hint=hint, ws=ws_dec)
-        if timed:
-            b.record()
-            ev.append((a, b))
         if layer:
             L.project_out(dims, o_lat, s["W_UV"], o=o, u=u, W_O=s["W_O"], ws=ws_prj)
         else:
@@ -188,22 +182,63 @@ def main():
 
     log(f"warmup {args.warmup} steps ...")
     for i in range(args.warmup):
-        step(i, False)
+        step(i % copies)
     torch.cuda.synchronize()
+    # The step's kernels are captured once per input copy into a HIP graph and
+    # replayed, so the timed region holds device work only (no per-launch
+    # host overhead between the ~6 kernels of a step).
+    graphs = None
+    if not args.no_graph:
+        log(f"capturing {copies} step graphs ...")
+        graphs = []
+        cap = torch.cuda.Stream()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps ...")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        if graphs is not None:
+            graphs[(args.warmup + i) % copies].replay()
+        else:
+            step((args.warmup + i) % copies)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
+    # Roofline: mla_decode_attn alone (its scan, split and combine kernels),
+    # HIP events on the launch stream around each call, same input rotation.
+    ev = []
+    for i in range(args.steps):
+        s = sets[(args.warmup + i) % copies]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
+                      total_rows_hint=hint, ws=ws_dec)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     tokens, byts, flops = algorithmic(w)
     if layer:
-        tokens += B * (args.warmup + args.steps // 2 + 1)     # rows grow by one per step
+        # Every step appends one row per sequence to the copy it uses: step j
+        # (j = warmup + i) on copy j % copies attends over the prior rows plus
+        # the floor(j / copies) + 1 rows appended to that copy so far.  The
+        # decode-only timing pass afterwards sees each copy at its final size.
+        per_copy_steps = [sum(1 for j in range(args.warmup + args.steps) if j % copies == c)
+                          for c in range(copies)]
+        grown = [B * (j // copies + 1) for j in range(args.warmup, args.warmup + args.steps)]
+        tokens += sum(grown) / len(grown)
+        dec_rows = [B * per_copy_steps[(args.warmup + i) % copies] for i in range(args.steps)]
+        extra = sum(dec_rows) / len(dec_rows)
+        n_h, d_c, d_r = d["n_h"], d["d_c"], d["d_r"]
+        byts += extra * (d_c + d_r) * 2
+        flops += extra * 2 * n_h * ((d_c + d_r) + d_c)
     achieved = byts / (dec_ms * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, decode_attn {dec_ms * 1e3:.1f} us, {achieved:.0f} GB/s, "
         f"{flops / (dec_ms * 1e-3) / 1e12:.0f} TFLOP/s")
@@ -228,7 +263,8 @@ def main():
                    "B": w.B, "cache_tokens": tokens,
                    "step": "absorb_q+append+decode_attn+project_out(o,u)" if layer
                    else "absorb_q+decode_attn+project_out(o)",
-                   "input_copies_rotated": copies},
+                   "input_copies_rotated": copies,
+                   "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "mla_decode_attn (scan + split attention + combine)",

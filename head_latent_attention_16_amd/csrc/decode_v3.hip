@@ -66,6 +66,10 @@ constexpr float OVF_TH = 64.0f;                       // log2 units
 constexpr int MIN_ROWS_PER_WG = 256;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+// Largest |O / l| a partial may carry in fp16 (max finite 65504); a piece
+// above it is flagged and its sequence recomputed by the fallback.
+constexpr float PART_MAX = 65000.0f;
 
 
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
@@ -73,11 +77,21 @@ static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 
 // Partial record of one (workgroup, sequence) piece.
 struct PartialLayout {
-  size_t o_off;    // float [slots][NH][DC]
+  size_t o_off;    // fp16 [slots][NH][DC]  O / l of the piece
   size_t ml_off;   // float [slots][NH][2]   (m in log2 units, l)
   size_t pre_off;  // int64 [B + 1] prefix of valid lengths
   size_t ovf_off;  // int32 [B] sequence needs the fallback recompute
+  size_t rec_off;  // WgRec [G] each workgroup's row range and first sequence
   size_t bytes;
+};
+
+// A split workgroup's share: rows [start, end) of the concatenated valid
+// lengths, starting in sequence b.  Written by the scan kernel so that the
+// split kernel needs one load instead of a chain of dependent ones.
+struct WgRec {
+  int64_t start, end;
+  int32_t b, pad;
+  int64_t pad2;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,8 +102,9 @@ __host__ __device__ inline PartialLayout partial_layout(int B, int G) {
   L.pre_off = 0;
   L.ovf_off = align256(sizeof(int64_t) * (B + 1));
   L.o_off = L.ovf_off + align256(sizeof(int32_t) * B);
-  L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(float));
-  L.bytes = L.ml_off + align256(slots * NH * 2 * sizeof(float));
+  L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(_Float16));
+  L.rec_off = L.ml_off + align256(slots * NH * 2 * sizeof(float));
+  L.bytes = L.rec_off + align256(sizeof(WgRec) * (size_t)G);
   return L;
 }
 
@@ -109,10 +124,11 @@ __device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
 // ---------------------------------------------------------------------------
 // Scheduler: validate lengths, prefix-sum the valid ones (invalid -> 0).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_sched(int B, const int32_t* __restrict__ offsets,
+__global__ void __launch_bounds__(1024) k_sched(int B, int G, const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ lens,
                                                 int64_t* __restrict__ prefix,
-                                                int32_t* __restrict__ ovf, int32_t* err_flag) {
+                                                int32_t* __restrict__ ovf, WgRec* __restrict__ rec,
+                                                int32_t* err_flag) {
   __shared__ int64_t part[1024];
   __shared__ int64_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -145,19 +161,40 @@ __global__ void __launch_bounds__(1024) k_sched(int B, const int32_t* __restrict
     __syncthreads();
   }
   if (threadIdx.x == 0) prefix[0] = 0;
+  __syncthreads();
+  // Each split workgroup's row range and the first sequence it touches
+  // (the smallest b with prefix[b + 1] > start).
+  const int64_t total = prefix[B];
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    WgRec r;
+    r.start = range_start(g, total, G);
+    r.end = range_start(g + 1, total, G);
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (prefix[mid + 1] > r.start) hi = mid; else lo = mid + 1;
+    }
+    r.b = lo;
+    r.pad = 0;
+    r.pad2 = 0;
+    rec[g] = r;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Split kernel.
 // ---------------------------------------------------------------------------
 struct SplitArgs {
+  const WgRec* rec;
+  float* o_lat;   // a sequence handled whole by one workgroup is written here
+  float* lse;
   const __bf16* q_lat;
   const __bf16* q_pe;
   const char* cache;
   const int32_t* offsets;
   const int64_t* prefix;
   int32_t* ovf;
-  float* part_o;
+  _Float16* part_o;
   float* part_ml;
   int B;
   int G;
@@ -201,6 +238,24 @@ __device__ __forceinline__ void barrier_all_lds() {
 // construction: the first MFMA takes srcC = 0 (no VALU-written input), a
 // chain only accumulates into the same registers (forwarded by the
 // hardware), and mfma_drain's 24 wait states precede any other use of S.
+// Value of lane ^ 32 (the other half of the wave), with the lane index
+// taken opaque so that the compiler does not keep the permute address live
+// across the kernel.
+__device__ __forceinline__ float swap_halves(float v, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  ln &= 63;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((ln ^ 32) << 2, __float_as_int(v)));
+}
+
+// max of three floats as one instruction (fmaxf chains would add a
+// canonicalising max per operand)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ void mfma_first(floatx16& S, const bf16x8& A, const bf16x8& B) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(A), "v"(B));
 }
@@ -237,10 +292,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   const int g32 = lane >> 5;          // which half of the wave
   const int n32 = lane & 31;          // head within the wave / row within the tile
 
-  const int64_t total = a.prefix[a.B];
-  if (total <= 0) return;
-  const int64_t start = range_start(g, total, a.G);
-  const int64_t end = range_start(g + 1, total, a.G);
+  const WgRec rec = a.rec[g];
+  const int64_t start = rec.start, end = rec.end;
   if (start >= end) return;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
@@ -249,22 +302,35 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   // lane i fills chunk p = 64 j + i, which holds logical chunk
   // (p % 72) ^ swz(row) of row p / 72.  The 64 chunks span at most two rows
   // (72 > 64), so everything but a per-lane select is wave-uniform.
-  auto dma_off = [&](int k) -> uint32_t {
-    const int base = (wave * DMA_PER_WAVE + k) * 64;
-    const int r0 = base / CHUNKS, m0 = base % CHUNKS;
-    const int qc = m0 + lane;
-    const bool next = qc >= CHUNKS;
-    const int c = (next ? qc - CHUNKS : qc) ^ (next ? swz(r0 + 1) : swz(r0));
-    return (uint32_t)((next ? (r0 + 1) * ROWB : r0 * ROWB) + c * 16);
-  };
+  // The nine per-lane source offsets (< 36864) are computed once and kept
+  // as 16-bit pairs in five registers; each DMA extracts its own with one
+  // instruction.
+  uint32_t dma_pk[(DMA_PER_WAVE + 1) / 2];
+#pragma unroll
+  for (int j = 0; j < (DMA_PER_WAVE + 1) / 2; ++j) dma_pk[j] = 0;
+#pragma unroll
+  for (int k = 0; k < DMA_PER_WAVE; ++k) {
+    const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
+    const int r = p / CHUNKS;
+    const int c = (p % CHUNKS) ^ swz(r);
+    dma_pk[k >> 1] |= (uint32_t)(r * ROWB + c * 16) << (16 * (k & 1));
+  }
+  auto dma_off = [&](int k) -> uint32_t { return (dma_pk[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
 
   // QK A-fragment (32x32x16): row n32, logical chunk 2 kk + g32 stored at
   // (2 kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
   // (2v + g32) ^ swz(n32); the rest is the constant 8u chunks.
-  uint32_t qk_off[4];
+  // These lane-dependent offsets are rebuilt at the start of every QK / PV
+  // block from an opaque copy of the lane index (a handful of VALU
+  // instructions) rather than kept in registers across the whole loop.
+  auto make_qk_off = [&](uint32_t (&o)[4]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    ln &= 63;
+    const int n = ln & 31, h = ln >> 5;
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    qk_off[v] = (uint32_t)(n32 * ROWB + (((2 * v + g32) ^ swz(n32)) << 4));
+    for (int v = 0; v < 4; ++v) o[v] = (uint32_t)(n * ROWB + (((2 * v + h) ^ swz(n)) << 4));
+  };
 
   // PV A-fragment via transpose reads.  In each 16-lane group G (i = lane%16),
   // lane i reads 8 bytes of row 16 kk2 + 8 rd + rr, rr = 4 g32 + i/4, at
@@ -272,34 +338,27 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   // group holds column 32 cb + 16 (G & 1) + j for four consecutive rows.
   // Logical chunk 4 cb + e sits at (4 cb + e) ^ swz(8 rd + rr)
   //   = 4 (cb ^ bb) + (e ^ ff),  bb = bit 2 of swz, ff = its low two bits.
-  uint32_t tr_base[2][2];
-  {
-    const int Gq = lane >> 4;
-    const int i16 = lane & 15;
-    const int rr = 4 * g32 + (i16 >> 2);
+  auto make_tr_base = [&](uint32_t (&t)[2][2]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    ln &= 63;
+    const int Gq = ln >> 4;
+    const int i16 = ln & 15;
+    const int rr = 4 * (ln >> 5) + (i16 >> 2);
     const int e = 2 * (Gq & 1) + ((i16 & 3) >> 1);
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
       const int sw = swz(8 * rd + rr);
       const int bb = sw >> 2, ff = sw & 3;
       const uint32_t base = (uint32_t)((8 * rd + rr) * ROWB + ((e ^ ff) << 4) + 8 * (i16 & 1));
-      tr_base[rd][0] = base + (uint32_t)(bb << 6);   // cb even: cb ^ bb = cb + bb
-      tr_base[rd][1] = base - (uint32_t)(bb << 6);   // cb odd:  cb ^ bb = cb - bb
+      t[rd][0] = base + (uint32_t)(bb << 6);   // cb even: cb ^ bb = cb + bb
+      t[rd][1] = base - (uint32_t)(bb << 6);   // cb odd:  cb ^ bb = cb - bb
     }
-  }
+  };
 
   const int head = wave * HPW + n32;
 
-  // Find the first sequence touching [start, end).
-  int b;
-  {
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.prefix[mid + 1] > start) hi = mid; else lo = mid + 1;
-    }
-    b = lo;
-  }
+  int b = rec.b;   // first sequence touching [start, end)
 
   int64_t pos = start;
   bool first_segment = true;
@@ -378,6 +437,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // ---- S^T = K . Q^T of tile t, fragments loaded QK_PF steps ahead ----
     auto qk = [&](int t, floatx16& S) {
       const MLA_LDS char* T = (const MLA_LDS char*)lds + (t % NSTAGE) * TILEB;
+      uint32_t qk_off[4];
+      make_qk_off(qk_off);
       bf16x8 kf[QK_PF];
 #pragma unroll
       for (int j = 0; j < QK_PF; ++j)
@@ -414,13 +475,16 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // than 2^64 above the reference flags the piece for the fallback.  Rows
     // at or past nvalid (a partial tile) get weight 0.  No branches: the
     // instructions interleave with the next tile's QK MFMAs.
-    auto row_of = [&](int i) { return 8 * (i >> 2) + 4 * g32 + (i & 3); };
+    // Row of score i is 8 (i/4) + i%4 + 4 g32: "row < n" is tested as
+    // 4 g32 < n - (8 (i/4) + i%4), one lane value against wave-uniform bounds.
+    const int row4 = 4 * g32;
+    auto row_lt = [&](int i, int n) { return row4 < n - (8 * (i >> 2) + (i & 3)); };
     // weights of scores 2j, 2j+1 -> P pair j; smax tracks the unmasked max
     auto sm_pair = [&](const floatx16& S, int j, int nvalid, bf16x8 (&P)[2], float& smax) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int i = 2 * j + e;
-        const bool ok = row_of(i) < nvalid;
+        const bool ok = row_lt(i, nvalid);
         smax = fmaxf(smax, ok ? S[i] : -INFINITY);
         const float x = ok ? fmaf(S[i], a.scale_log2, -m_ref) : -INFINITY;
         P[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
@@ -450,9 +514,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float v = __fmul_rn(S_cur[i], a.scale_log2);
-        mloc = fmaxf(mloc, row_of(i) < seg_len ? v : -INFINITY);
+        mloc = fmaxf(mloc, row_lt(i, seg_len) ? v : -INFINITY);
       }
-      m_ref = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      m_ref = fmaxf(mloc, swap_halves(mloc, lane));
       s_thr = (m_ref + OVF_TH) / a.scale_log2;
     }
 
@@ -477,6 +541,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // scheduling barriers keep every step where it is written, so the
         // fragment prefetch and the VALU placement stay as planned.
         const MLA_LDS char* Tn = (const MLA_LDS char*)lds + ((it + 1) % NSTAGE) * TILEB;
+        uint32_t qk_off[4];
+        make_qk_off(qk_off);
         bf16x8 kf[QK_PF];
 #pragma unroll
         for (int j = 0; j < QK_PF; ++j)
@@ -498,7 +564,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
             kf[kk % QK_PF] = *(const MLA_LDS bf16x8*)(Tn + qk_off[nk & 3] + (nk >> 2) * 128);
           if (kk < 16) {
             x[kk] = fmaf(Sc[kk], a.scale_log2, -m_ref);
-            if (kk & 1) smax = fmaxf(smax, fmaxf(Sc[kk - 1], Sc[kk]));
+            if (kk & 1) smax = max3f(smax, Sc[kk - 1], Sc[kk]);
           }
           if (kk >= 4 && kk < 20) e[kk - 4] = __builtin_amdgcn_exp2f(x[kk - 4]);
           if (kk >= 9 && kk < 25 && (kk & 1)) {
@@ -519,6 +585,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       }
 
       // ---- PV fragments for the first column blocks ----
+      uint32_t tr_base[2][2];
+      make_tr_base(tr_base);
       bf16x4 pa[PV_PF][2];
 #pragma unroll
       for (int j = 0; j < PV_PF; ++j) {
@@ -576,17 +644,51 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // longer reads; they must land before a next piece reuses the stages.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- emit the partial (unnormalised O, m, l) of this piece ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = l_run + swap_halves(l_run, lane);
+    const float inv_l = 1.0f / l_tot;
+    if (t0 == 0 && seg_end == a.prefix[b + 1]) {
+      // ---- the whole sequence is in this piece: final output, fp32 ----
+      float* out = a.o_lat + ((size_t)b * NH + head) * DC;
+#pragma unroll
+      for (int cb = 0; cb < DC / 32; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const floatx4 v = {O[cb][4 * q4 + 0] * inv_l, O[cb][4 * q4 + 1] * inv_l,
+                             O[cb][4 * q4 + 2] * inv_l, O[cb][4 * q4 + 3] * inv_l};
+          *(floatx4*)(out + 32 * cb + 8 * q4 + 4 * g32) = v;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if (g32 == 0 && a.lse) a.lse[(size_t)b * NH + head] = (m_ref + log2f(l_tot)) * kLn2;
+      pos = seg_end;
+      continue;
+    }
+    // ---- emit the partial (O / l in fp16, m, l) of this piece ----
+    // The normalised rows are weighted averages of cache rows, so fp16
+    // (11-bit significand, finer than the bf16 weights and queries that bound
+    // the result) holds them; a piece whose values exceed the fp16 range is
+    // flagged for the fallback instead.
     const size_t slot = (size_t)g + (size_t)b;
-    float* po = a.part_o + (slot * NH + head) * DC;
+    _Float16* po = a.part_o + (slot * NH + head) * DC;
+    float amax = 0.f;
 #pragma unroll
     for (int cb = 0; cb < DC / 32; ++cb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        floatx4 v = {O[cb][4 * q4 + 0], O[cb][4 * q4 + 1], O[cb][4 * q4 + 2], O[cb][4 * q4 + 3]};
-        *(floatx4*)(po + 32 * cb + 8 * q4 + 4 * g32) = v;
+        halfx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = O[cb][4 * q4 + e] * inv_l;
+          amax = fmaxf(amax, fabsf(x));
+          v[e] = (_Float16)x;
+        }
+        *(halfx4*)(po + 32 * cb + 8 * q4 + 4 * g32) = v;
+        // one group of four at a time: converting all 256 accumulators at
+        // once would need as many VGPRs
+        __builtin_amdgcn_sched_barrier(0);
       }
+    if (__any(amax > PART_MAX)) {
+      if (lane == 0) a.ovf[b] = 1;
+    }
     if (g32 == 0) {
       float* pm = a.part_ml + (slot * NH + head) * 2;
       pm[0] = m_ref;
@@ -606,7 +708,7 @@ struct CombineArgs {
   const int32_t* offsets;
   const int64_t* prefix;
   const int32_t* ovf;
-  const float* part_o;
+  const _Float16* part_o;
   const float* part_ml;
   float* o_lat;
   float* lse;
@@ -690,6 +792,7 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   const int G = a.G;
   const int g_lo = wg_of(p0, total, G);
   const int npiece = wg_of(p1 - 1, total, G) - g_lo + 1;
+  if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
 
   // Workgroup g_lo's range holds row p0, so it is never empty.  Empty ranges
   // (only when the total is below G) wrote nothing: they get weight 0 and
@@ -719,8 +822,9 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   for (int k = 0; k < PER; ++k) {
     const int i = tid + k * CMB_THREADS;
     if (i < npiece) {
-      const float w = m[k] == -INFINITY ? 0.f : exp2f(m[k] - M);
-      if (w > 0.f) L += w * a.part_ml[((size_t)slot[k] * NH + h) * 2 + 1];
+      float w = m[k] == -INFINITY ? 0.f : exp2f(m[k] - M);
+      if (w > 0.f) w *= a.part_ml[((size_t)slot[k] * NH + h) * 2 + 1];   // 2^(m-M) l
+      L += w;
       s_w[i] = w;
       s_slot[i] = slot[k];
     }
@@ -730,29 +834,29 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   __syncthreads();
   L = s_red[1][0] + s_red[1][1];
 
-  const float* po = a.part_o + (size_t)h * DC + 4 * tid;
+  const _Float16* po = a.part_o + (size_t)h * DC + 4 * tid;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   int i = 0;
   for (; i + 8 <= npiece; i += 8) {
-    float4 v[8];
+    halfx4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *(const float4*)(po + (size_t)s_slot[i + j] * NH * DC);
+    for (int j = 0; j < 8; ++j) v[j] = *(const halfx4*)(po + (size_t)s_slot[i + j] * NH * DC);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float w = s_w[i + j];
-      acc.x += w * v[j].x;
-      acc.y += w * v[j].y;
-      acc.z += w * v[j].z;
-      acc.w += w * v[j].w;
+      acc.x += w * (float)v[j][0];
+      acc.y += w * (float)v[j][1];
+      acc.z += w * (float)v[j][2];
+      acc.w += w * (float)v[j][3];
     }
   }
   for (; i < npiece; ++i) {
-    const float4 v = *(const float4*)(po + (size_t)s_slot[i] * NH * DC);
+    const halfx4 v = *(const halfx4*)(po + (size_t)s_slot[i] * NH * DC);
     const float w = s_w[i];
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+    acc.x += w * (float)v[0];
+    acc.y += w * (float)v[1];
+    acc.z += w * (float)v[2];
+    acc.w += w * (float)v[3];
   }
   const float inv = 1.f / L;
   out[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
@@ -786,17 +890,21 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   char* w = (char*)ws;
   int64_t* prefix = (int64_t*)(w + L.pre_off);
   int32_t* ovf = (int32_t*)(w + L.ovf_off);
-  k_sched<<<1, 1024, 0, st>>>(B, offsets, lens, prefix, ovf, err_flag);
+  WgRec* rec = (WgRec*)(w + L.rec_off);
+  k_sched<<<1, 1024, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, err_flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SplitArgs a;
+  a.rec = rec;
+  a.o_lat = o_lat;
+  a.lse = lse;
   a.q_lat = (const __bf16*)q_lat;
   a.q_pe = (const __bf16*)q_pe;
   a.cache = (const char*)cache;
   a.offsets = offsets;
   a.prefix = prefix;
   a.ovf = ovf;
-  a.part_o = (float*)(w + L.o_off);
+  a.part_o = (_Float16*)(w + L.o_off);
   a.part_ml = (float*)(w + L.ml_off);
   a.B = B;
   a.G = G;
