@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch each kernel from the host")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="first run one plain device-to-device copy of MIB MiB (a reference "
+                        "for the HBM byte counters of a profiler run)")
     return p.parse_args()
 
 
@@ -61,6 +64,33 @@ def algorithmic(w):
     byts = tokens * (d_c + d_r) * 2 + w.B * n_h * (d_c + d_r) * 2 + w.B * n_h * d_c * 4
     flops = tokens * 2 * n_h * ((d_c + d_r) + d_c)
     return tokens, byts, flops
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_16_amd", "csrc", "decode_v3.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per mla_decode_attn call from the recorded counter runs, or None.
+
+    The record holds FETCH_SIZE + WRITE_SIZE of the call's kernels, scaled by a
+    plain copy of known size, and the SHA-256 of the kernel source it was taken
+    with: a changed kernel makes the figure stale, so it is not reported."""
+    import hashlib
+    try:
+        rec = None
+        for line in open(TRAFFIC_FILE):
+            line = line.strip()
+            if line.startswith("{") and '"workload"' in line:
+                r = json.loads(line)
+                if r.get("workload") == workload:
+                    rec = r
+        if rec is None:
+            return None
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        return rec["bytes_per_call"] if rec.get("kernel_sha256") == src else None
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(w, budget_s):
@@ -115,6 +145,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read and written")
+        del src, dst
     name = args.workload
     spare = args.warmup + args.steps + 2
     log(f"generating workload {name} ...")
@@ -266,7 +305,7 @@ def main():
                    "input_copies_rotated": copies,
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                      "kernel": "mla_decode_attn (scan + split attention + combine)",
                      "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
                      "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,

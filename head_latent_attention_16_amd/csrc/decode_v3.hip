@@ -286,7 +286,12 @@ __device__ __forceinline__ int swz(int r) {
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
 
-  const int g = blockIdx.x;
+  // Range index of this workgroup.  Workgroups are dealt to the 8 XCDs
+  // round-robin (block i runs on XCD i % 8); giving each XCD a contiguous
+  // run of ranges keeps the workgroups of one sequence on one XCD, where they
+  // share its L2 for the query and neighbouring rows.
+  const int g = (a.G % 8 == 0) ? (int)(blockIdx.x % 8) * (a.G / 8) + (int)(blockIdx.x / 8)
+                               : (int)blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g32 = lane >> 5;          // which half of the wave
