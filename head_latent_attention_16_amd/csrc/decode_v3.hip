@@ -89,9 +89,10 @@ struct PartialLayout {
 // lengths, starting in sequence b.  Written by the scan kernel so that the
 // split kernel needs one load instead of a chain of dependent ones.
 struct WgRec {
-  int64_t start, end;
-  int32_t b, pad;
-  int64_t pad2;
+  int64_t start, end;            // rows [start, end) of the concatenated lengths
+  int64_t seq_begin, seq_end;    // prefix[b], prefix[b + 1] of its first sequence
+  int32_t b, off_b;              // that sequence and its cache offset
+  int32_t pad[2];
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -124,60 +125,102 @@ __device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
 // ---------------------------------------------------------------------------
 // Scheduler: validate lengths, prefix-sum the valid ones (invalid -> 0).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_sched(int B, int G, const int32_t* __restrict__ offsets,
-                                                const int32_t* __restrict__ lens,
-                                                int64_t* __restrict__ prefix,
-                                                int32_t* __restrict__ ovf, WgRec* __restrict__ rec,
-                                                int32_t* err_flag) {
-  __shared__ int64_t part[1024];
+// One workgroup of 1024 threads, four sequences per thread per chunk.  The
+// prefix sum is a wave scan (DPP shuffles) plus a scan of the 16 wave totals;
+// then every non-empty sequence b writes the record of each split workgroup
+// whose first row lies in it: g with start(g) in [prefix[b], prefix[b+1]),
+// i.e. ceil(prefix[b] G / total) <= g < ceil(prefix[b+1] G / total).
+constexpr int SCHED_THREADS = 1024;
+constexpr int SCHED_PER = 4;
+
+__device__ __forceinline__ int64_t ceil_div_i64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ lens,
+                                                         int64_t* __restrict__ prefix,
+                                                         int32_t* __restrict__ ovf, WgRec* __restrict__ rec,
+                                                         int32_t* err_flag) {
+  __shared__ int64_t wsum[SCHED_THREADS / 64];
   __shared__ int64_t carry;
-  if (threadIdx.x == 0) carry = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    carry = 0;
+    prefix[0] = 0;
+  }
   __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    int b = base + threadIdx.x;
-    int64_t v = 0;
-    if (b < B) {
-      int len = lens[b];
-      int cap = offsets[b + 1] - offsets[b];
-      if (len >= 1 && len <= cap) {
-        v = len;
-      } else if (err_flag) {
-        atomicOr(err_flag, MLA_DEVERR_LENS);
+  for (int base = 0; base < B; base += SCHED_THREADS * SCHED_PER) {
+    int64_t v[SCHED_PER];
+    int64_t tsum = 0;
+#pragma unroll
+    for (int j = 0; j < SCHED_PER; ++j) {
+      const int b = base + SCHED_PER * tid + j;
+      v[j] = 0;
+      if (b < B) {
+        const int len = lens[b];
+        const int cap = offsets[b + 1] - offsets[b];
+        if (len >= 1 && len <= cap)
+          v[j] = len;
+        else if (err_flag)
+          atomicOr(err_flag, MLA_DEVERR_LENS);
+        ovf[b] = 0;
       }
+      tsum += v[j];
     }
-    if (b < B) ovf[b] = 0;
-    part[threadIdx.x] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      int64_t add = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-      __syncthreads();
-      part[threadIdx.x] += add;
-      __syncthreads();
+    // inclusive scan of tsum over the wave
+    int64_t x = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
-    int64_t c = carry;
-    if (b < B) prefix[b + 1] = c + part[threadIdx.x];   // inclusive
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 1023) carry = c + part[1023];
+    if (wave == 0) {
+      int64_t w = lane < SCHED_THREADS / 64 ? wsum[lane] : 0;
+#pragma unroll
+      for (int o = 1; o < SCHED_THREADS / 64; o <<= 1) {
+        const int64_t y = __shfl_up(w, o, 64);
+        if (lane >= o) w += y;
+      }
+      if (lane < SCHED_THREADS / 64) wsum[lane] = w;   // inclusive over waves
+    }
+    __syncthreads();
+    int64_t run = carry + (wave > 0 ? wsum[wave - 1] : 0) + x - tsum;   // exclusive
+#pragma unroll
+    for (int j = 0; j < SCHED_PER; ++j) {
+      const int b = base + SCHED_PER * tid + j;
+      run += v[j];
+      if (b < B) prefix[b + 1] = run;
+    }
+    __syncthreads();
+    if (tid == 0) carry += wsum[SCHED_THREADS / 64 - 1];
     __syncthreads();
   }
-  if (threadIdx.x == 0) prefix[0] = 0;
-  __syncthreads();
-  // Each split workgroup's row range and the first sequence it touches
-  // (the smallest b with prefix[b + 1] > start).
-  const int64_t total = prefix[B];
-  for (int g = threadIdx.x; g < G; g += 1024) {
-    WgRec r;
-    r.start = range_start(g, total, G);
-    r.end = range_start(g + 1, total, G);
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (prefix[mid + 1] > r.start) hi = mid; else lo = mid + 1;
+  const int64_t total = carry;
+  if (total <= 0) {
+    for (int g = tid; g < G; g += SCHED_THREADS) {
+      WgRec r = {};
+      rec[g] = r;
     }
-    r.b = lo;
-    r.pad = 0;
-    r.pad2 = 0;
-    rec[g] = r;
+    return;
+  }
+  for (int b = tid; b < B; b += SCHED_THREADS) {
+    const int64_t p0 = prefix[b], p1 = prefix[b + 1];
+    if (p1 <= p0) continue;
+    const int g_lo = (int)ceil_div_i64(p0 * G, total);
+    const int g_hi = (int)ceil_div_i64(p1 * G, total);
+    const int off = offsets[b];
+    for (int g = g_lo; g < g_hi; ++g) {
+      WgRec r;
+      r.start = range_start(g, total, G);
+      r.end = range_start(g + 1, total, G);
+      r.seq_begin = p0;
+      r.seq_end = p1;
+      r.b = b;
+      r.off_b = off;
+      r.pad[0] = r.pad[1] = 0;
+      rec[g] = r;
+    }
   }
 }
 
@@ -368,13 +411,24 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   int64_t pos = start;
   bool first_segment = true;
   while (pos < end) {
-    while (a.prefix[b + 1] <= pos) ++b;
-    const int64_t seq_begin = a.prefix[b];
-    const int64_t seg_end = end < a.prefix[b + 1] ? end : a.prefix[b + 1];
+    // The record describes the first sequence; later ones are looked up.
+    int64_t seq_begin, seq_endx;
+    int off_b;
+    if (first_segment) {
+      seq_begin = rec.seq_begin;
+      seq_endx = rec.seq_end;
+      off_b = rec.off_b;
+    } else {
+      while (a.prefix[b + 1] <= pos) ++b;
+      seq_begin = a.prefix[b];
+      seq_endx = a.prefix[b + 1];
+      off_b = a.offsets[b];
+    }
+    const int64_t seg_end = end < seq_endx ? end : seq_endx;
     const int t0 = (int)(pos - seq_begin);
     const int seg_len = (int)(seg_end - pos);
     const int ntiles = (seg_len + TILE - 1) / TILE;
-    const char* rows = a.cache + ((size_t)a.offsets[b] + (size_t)t0) * ROWB;
+    const char* rows = a.cache + ((size_t)off_b + (size_t)t0) * ROWB;
 
     if (!first_segment) barrier_all_lds();   // previous segment's tiles fully consumed
     first_segment = false;
@@ -651,7 +705,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
     const float l_tot = l_run + swap_halves(l_run, lane);
     const float inv_l = 1.0f / l_tot;
-    if (t0 == 0 && seg_end == a.prefix[b + 1]) {
+    if (t0 == 0 && seg_end == seq_endx) {
       // ---- the whole sequence is in this piece: final output, fp32 ----
       float* out = a.o_lat + ((size_t)b * NH + head) * DC;
 #pragma unroll
@@ -896,7 +950,7 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   int64_t* prefix = (int64_t*)(w + L.pre_off);
   int32_t* ovf = (int32_t*)(w + L.ovf_off);
   WgRec* rec = (WgRec*)(w + L.rec_off);
-  k_sched<<<1, 1024, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, err_flag);
+  k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, err_flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SplitArgs a;
