@@ -77,11 +77,12 @@ static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 
 // Partial record of one (workgroup, sequence) piece.
 struct PartialLayout {
-  size_t o_off;    // fp16 [slots][NH][DC]  O / l of the piece
+  size_t o_off;    // fp16 [slots][NH / 32][DC / 32][2 KiB] O / l of the piece, lane order
   size_t ml_off;   // float [slots][NH][2]   (m in log2 units, l)
   size_t pre_off;  // int64 [B + 1] prefix of valid lengths
   size_t ovf_off;  // int32 [B] sequence needs the fallback recompute
   size_t rec_off;  // WgRec [G] each workgroup's row range and first sequence
+  size_t si_off;   // int2 [B] first range holding the sequence, number of ranges
   size_t bytes;
 };
 
@@ -105,7 +106,8 @@ __host__ __device__ inline PartialLayout partial_layout(int B, int G) {
   L.o_off = L.ovf_off + align256(sizeof(int32_t) * B);
   L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(_Float16));
   L.rec_off = L.ml_off + align256(slots * NH * 2 * sizeof(float));
-  L.bytes = L.rec_off + align256(sizeof(WgRec) * (size_t)G);
+  L.si_off = L.rec_off + align256(sizeof(WgRec) * (size_t)G);
+  L.bytes = L.si_off + align256(sizeof(int2) * (size_t)B);
   return L;
 }
 
@@ -125,27 +127,30 @@ __device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
 // ---------------------------------------------------------------------------
 // Scheduler: validate lengths, prefix-sum the valid ones (invalid -> 0).
 // ---------------------------------------------------------------------------
-// One workgroup of 1024 threads, four sequences per thread per chunk.  The
-// prefix sum is a wave scan (DPP shuffles) plus a scan of the 16 wave totals;
-// then every non-empty sequence b writes the record of each split workgroup
-// whose first row lies in it: g with start(g) in [prefix[b], prefix[b+1]),
-// i.e. ceil(prefix[b] G / total) <= g < ceil(prefix[b+1] G / total).
 constexpr int SCHED_THREADS = 1024;
 constexpr int SCHED_PER = 4;
+constexpr int SCHED_LDS_B = 4096;   // prefix kept in LDS up to this many sequences
 
-__device__ __forceinline__ int64_t ceil_div_i64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
+// One workgroup of 1024 threads, four sequences per thread per chunk.
+// (1) Inclusive scan of the valid lengths (wave scans, then a scan of the 16
+// wave totals), written to prefix[] and, for B up to
+// SCHED_LDS_B, to LDS.  (2) One lane per range g: its bounds and, by binary
+// search over the prefix, the sequence holding its first row.  (3) One lane
+// per sequence: the first range holding it and how many ranges it spans.
 __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ lens,
                                                          int64_t* __restrict__ prefix,
                                                          int32_t* __restrict__ ovf, WgRec* __restrict__ rec,
-                                                         int32_t* err_flag) {
+                                                         int2* __restrict__ seqinfo, int32_t* err_flag) {
   __shared__ int64_t wsum[SCHED_THREADS / 64];
   __shared__ int64_t carry;
+  __shared__ int64_t s_pre[SCHED_LDS_B + 1];
+  const bool in_lds = B <= SCHED_LDS_B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
     carry = 0;
     prefix[0] = 0;
+    s_pre[0] = 0;
   }
   __syncthreads();
   for (int base = 0; base < B; base += SCHED_THREADS * SCHED_PER) {
@@ -190,37 +195,51 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     for (int j = 0; j < SCHED_PER; ++j) {
       const int b = base + SCHED_PER * tid + j;
       run += v[j];
-      if (b < B) prefix[b + 1] = run;
+      if (b < B) {
+        prefix[b + 1] = run;
+        if (in_lds) s_pre[b + 1] = run;
+      }
     }
     __syncthreads();
     if (tid == 0) carry += wsum[SCHED_THREADS / 64 - 1];
     __syncthreads();
   }
   const int64_t total = carry;
-  if (total <= 0) {
+  if (total <= 0) {   // no valid sequence: the combine writes NaN everywhere
     for (int g = tid; g < G; g += SCHED_THREADS) {
       WgRec r = {};
       rec[g] = r;
     }
     return;
   }
-  for (int b = tid; b < B; b += SCHED_THREADS) {
-    const int64_t p0 = prefix[b], p1 = prefix[b + 1];
-    if (p1 <= p0) continue;
-    const int g_lo = (int)ceil_div_i64(p0 * G, total);
-    const int g_hi = (int)ceil_div_i64(p1 * G, total);
-    const int off = offsets[b];
-    for (int g = g_lo; g < g_hi; ++g) {
-      WgRec r;
-      r.start = range_start(g, total, G);
-      r.end = range_start(g + 1, total, G);
-      r.seq_begin = p0;
-      r.seq_end = p1;
-      r.b = b;
-      r.off_b = off;
-      r.pad[0] = r.pad[1] = 0;
-      rec[g] = r;
+  auto pre = [&](int i) -> int64_t { return in_lds ? s_pre[i] : prefix[i]; };
+  for (int g = tid; g < G; g += SCHED_THREADS) {
+    const int64_t start = range_start(g, total, G);
+    // largest b with prefix[b] <= start; start < total, so prefix[b + 1] > start
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre(mid) <= start) lo = mid;
+      else hi = mid - 1;
     }
+    WgRec r;
+    r.start = start;
+    r.end = range_start(g + 1, total, G);
+    r.seq_begin = pre(lo);
+    r.seq_end = pre(lo + 1);
+    r.b = lo;
+    r.off_b = offsets[lo];
+    r.pad[0] = r.pad[1] = 0;
+    rec[g] = r;
+  }
+  for (int b = tid; b < B; b += SCHED_THREADS) {
+    const int64_t p0 = pre(b), p1 = pre(b + 1);
+    int2 si = make_int2(0, 0);
+    if (p1 > p0) {
+      si.x = wg_of(p0, total, G);
+      si.y = wg_of(p1 - 1, total, G) - si.x + 1;
+    }
+    seqinfo[b] = si;
   }
 }
 
@@ -342,7 +361,19 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
   const WgRec rec = a.rec[g];
   const int64_t start = rec.start, end = rec.end;
-  if (start >= end) return;
+  if (start >= end) {
+    // An empty range (fewer rows than workgroups) can fall inside the span of
+    // ranges the combine walks for sequence rec.b: leave it a zero partial
+    // with weight 0 there (m = -inf, l = 0).
+    if (rec.seq_end > rec.seq_begin) {
+      const size_t slot = (size_t)g + (size_t)rec.b;
+      uint4* po = (uint4*)(a.part_o + slot * NH * DC);
+      for (int i = threadIdx.x; i < NH * DC / 8; i += THREADS) po[i] = make_uint4(0, 0, 0, 0);
+      if (threadIdx.x < NH)
+        ((float2*)a.part_ml)[slot * NH + threadIdx.x] = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
@@ -725,9 +756,11 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // The normalised rows are weighted averages of cache rows, so fp16
     // (11-bit significand, finer than the bf16 weights and queries that bound
     // the result) holds them; a piece whose values exceed the fp16 range is
-    // flagged for the fallback instead.
+    // flagged for the fallback instead.  The values leave in the
+    // accumulator's own lane order (the combine kernel reads that order), so
+    // every store instruction writes 512 contiguous bytes.
     const size_t slot = (size_t)g + (size_t)b;
-    _Float16* po = a.part_o + (slot * NH + head) * DC;
+    _Float16* po = a.part_o + (slot * NH + wave * HPW) * DC;   // this wave's 32 heads
     float amax = 0.f;
 #pragma unroll
     for (int cb = 0; cb < DC / 32; ++cb)
@@ -740,7 +773,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
           amax = fmaxf(amax, fabsf(x));
           v[e] = (_Float16)x;
         }
-        *(halfx4*)(po + 32 * cb + 8 * q4 + 4 * g32) = v;
+        *(halfx4*)(po + (cb * 4 + q4) * 256 + 4 * lane) = v;
         // one group of four at a time: converting all 256 accumulators at
         // once would need as many VGPRs
         __builtin_amdgcn_sched_barrier(0);
@@ -766,6 +799,7 @@ struct CombineArgs {
   const __bf16* cache;
   const int32_t* offsets;
   const int64_t* prefix;
+  const int2* seqinfo;
   const int32_t* ovf;
   const _Float16* part_o;
   const float* part_ml;
@@ -777,11 +811,14 @@ struct CombineArgs {
 };
 
 // Fallback for a flagged sequence: a plain online softmax over all its rows
-// (two waves, alternate rows, 64 lanes across the 576 features, running max
-// with rescale), then the two wave states are merged.
+// (the block's waves take alternate rows, 64 lanes across the 576 features,
+// running max with rescale), then the wave states are merged.
+constexpr int CMB_THREADS = 256;
+constexpr int CMB_WAVES = CMB_THREADS / 64;
+
 __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
-  __shared__ float st_m[2], st_l[2];
-  __shared__ float st_o[2][DC];
+  __shared__ float st_m[CMB_WAVES], st_l[CMB_WAVES];
+  __shared__ float st_o[CMB_WAVES][DC];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float q[DK / 64];
 #pragma unroll
@@ -795,7 +832,7 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
   for (int k = 0; k < DC / 64; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
   const __bf16* rows = a.cache + (size_t)a.offsets[b] * DK;
-  for (int j = wave; j < len; j += 2) {
+  for (int j = wave; j < len; j += CMB_WAVES) {
     const __bf16* r = rows + (size_t)j * DK;
     float sdot = 0.f;
 #pragma unroll
@@ -813,114 +850,114 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
 #pragma unroll
   for (int k = 0; k < DC / 64; ++k) st_o[wave][lane + 64 * k] = acc[k];
   __syncthreads();
-  const float M = fmaxf(st_m[0], st_m[1]);
-  const float w0 = st_m[0] == -INFINITY ? 0.f : exp2f(st_m[0] - M);
-  const float w1 = st_m[1] == -INFINITY ? 0.f : exp2f(st_m[1] - M);
-  const float L = st_l[0] * w0 + st_l[1] * w1;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < CMB_WAVES; ++w) M = fmaxf(M, st_m[w]);
+  float wt[CMB_WAVES], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < CMB_WAVES; ++w) {
+    wt[w] = st_m[w] == -INFINITY ? 0.f : exp2f(st_m[w] - M);
+    L += st_l[w] * wt[w];
+  }
   float* out = a.o_lat + ((size_t)b * NH + h) * DC;
-  for (int c = threadIdx.x; c < DC; c += blockDim.x) out[c] = (st_o[0][c] * w0 + st_o[1][c] * w1) / L;
+  for (int c = threadIdx.x; c < DC; c += blockDim.x) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < CMB_WAVES; ++w) v += st_o[w][c] * wt[w];
+    out[c] = v / L;
+  }
   if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
+  __syncthreads();   // the LDS state is reused by the next head
 }
 
-// One workgroup per (head, sequence): 128 lanes x 4 columns.  The (m, l) of
-// all pieces are read in parallel and reduced to the common max M; each
-// piece's weight 2^(m - M) goes to LDS, then the partial rows are read eight
-// at a time so that many loads are in flight per lane.
-constexpr int CMB_THREADS = 128;
-constexpr int MAX_G = 256;   // pieces per sequence <= G <= MAX_G
+// One workgroup per (32-head block, 32-column block, sequence).  A piece's
+// partial O is stored in the split kernel's accumulator lane order: for each
+// (piece, head block, column block) 2 KiB of fp16, entry t = 64 q4 + lane
+// holding columns 8 q4 + 4 (lane / 32) + [0, 4) of head lane % 32.  Lane t of
+// this block reads entry t of every piece, so each piece is one contiguous
+// 2 KiB read.  Each lane forms the weights of its own head itself: a first
+// pass over the pieces' m gives the common max M, the second weights every
+// piece by 2^(m - M) l while accumulating.  Pieces over empty ranges carry
+// m = -inf, l = 0 and zero rows.  The result is transposed through LDS so
+// that every head's 32 columns leave as one 128-byte store.
+constexpr int CMB_HB = HPW;          // heads per block (one split-kernel wave)
+constexpr int CMB_CB = 32;           // columns per block (one accumulator tile)
 
 __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
-  __shared__ float s_w[MAX_G];
-  __shared__ int s_slot[MAX_G];
-  __shared__ float s_red[2][2];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t total = a.prefix[a.B];
+  __shared__ float s_out[CMB_HB][CMB_CB + 1];
+  constexpr int NCB = DC / CMB_CB;
+  const int hb = blockIdx.x / NCB, cb = blockIdx.x % NCB, b = blockIdx.y;
+  const int tid = threadIdx.x;
   const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
-  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + h) * DC);
+  const int2 si = a.seqinfo[b];
+  const int h_r = tid >> 3, c_r = (tid & 7) * 4;   // this lane's output row / columns
+  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r);
   if (p1 <= p0) {   // invalid length: NaN result (the error flag is set)
     const float nan = __builtin_nanf("");
-    out[tid] = make_float4(nan, nan, nan, nan);
-    if (tid == 0 && a.lse) a.lse[(size_t)b * NH + h] = nan;
+    *out = make_float4(nan, nan, nan, nan);
+    if (cb == 0 && tid < CMB_HB && a.lse) a.lse[(size_t)b * NH + hb * CMB_HB + tid] = nan;
     return;
   }
   if (a.ovf[b]) {
-    recompute_head(a, b, h, (int)(p1 - p0));
+    // the NCB blocks of this head block share its heads out, whole rows each
+    for (int k = cb; k < CMB_HB; k += NCB) recompute_head(a, b, hb * CMB_HB + k, (int)(p1 - p0));
     return;
   }
-  const int G = a.G;
-  const int g_lo = wg_of(p0, total, G);
-  const int npiece = wg_of(p1 - 1, total, G) - g_lo + 1;
+  const int npiece = si.y;
   if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
 
-  // Workgroup g_lo's range holds row p0, so it is never empty.  Empty ranges
-  // (only when the total is below G) wrote nothing: they get weight 0 and
-  // read g_lo's finite partial instead of their own unwritten slot.
-  constexpr int PER = MAX_G / CMB_THREADS;
-  float m[PER];
-  int slot[PER];
+  const int n32 = tid & 31, cols = 8 * (tid >> 6) + 4 * ((tid >> 5) & 1);
+  const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
+  const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
   float M = -INFINITY;
+  {
+    int i = 0;
+    for (; i + 8 <= npiece; i += 8) {
+      float2 v[8];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int i = tid + k * CMB_THREADS;
-    const int g = g_lo + i;
-    m[k] = -INFINITY;
-    slot[k] = g_lo + b;
-    if (i < npiece && range_start(g, total, G) != range_start(g + 1, total, G)) {
-      slot[k] = g + b;
-      m[k] = a.part_ml[((size_t)slot[k] * NH + h) * 2];
-    }
-    M = fmaxf(M, m[k]);
-  }
-  M = wave_max(M);
-  if (lane == 0) s_red[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(s_red[0][0], s_red[0][1]);
-  float L = 0.f;
+      for (int j = 0; j < 8; ++j) v[j] = ml[(size_t)(i + j) * NH];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int i = tid + k * CMB_THREADS;
-    if (i < npiece) {
-      float w = m[k] == -INFINITY ? 0.f : exp2f(m[k] - M);
-      if (w > 0.f) w *= a.part_ml[((size_t)slot[k] * NH + h) * 2 + 1];   // 2^(m-M) l
-      L += w;
-      s_w[i] = w;
-      s_slot[i] = slot[k];
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, v[j].x);
     }
+    for (; i < npiece; ++i) M = fmaxf(M, ml[(size_t)i * NH].x);
   }
-  L = wave_sum(L);
-  if (lane == 0) s_red[1][wave] = L;
-  __syncthreads();
-  L = s_red[1][0] + s_red[1][1];
-
-  const _Float16* po = a.part_o + (size_t)h * DC + 4 * tid;
+  constexpr size_t SLOT_STRIDE = (size_t)NH * DC;
+  const _Float16* po = a.part_o + slot0 * SLOT_STRIDE + ((size_t)hb * NCB + cb) * (CMB_HB * CMB_CB) + 4 * tid;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int i = 0;
-  for (; i + 8 <= npiece; i += 8) {
-    halfx4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *(const halfx4*)(po + (size_t)s_slot[i + j] * NH * DC);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = s_w[i + j];
-      acc.x += w * (float)v[j][0];
-      acc.y += w * (float)v[j][1];
-      acc.z += w * (float)v[j][2];
-      acc.w += w * (float)v[j][3];
-    }
-  }
-  for (; i < npiece; ++i) {
-    const halfx4 v = *(const halfx4*)(po + (size_t)s_slot[i] * NH * DC);
-    const float w = s_w[i];
+  float L = 0.f;
+  auto add = [&](const float2 mlv, const halfx4 v) {
+    const float w = mlv.x == -INFINITY ? 0.f : exp2f(mlv.x - M) * mlv.y;   // 2^(m - M) l
+    L += w;
     acc.x += w * (float)v[0];
     acc.y += w * (float)v[1];
     acc.z += w * (float)v[2];
     acc.w += w * (float)v[3];
+  };
+  int i = 0;
+  for (; i + 8 <= npiece; i += 8) {
+    halfx4 v[8];
+    float2 m8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = *(const halfx4*)(po + (size_t)(i + j) * SLOT_STRIDE);
+      m8[j] = ml[(size_t)(i + j) * NH];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add(m8[j], v[j]);
   }
+  for (; i < npiece; ++i) add(ml[(size_t)i * NH], *(const halfx4*)(po + (size_t)i * SLOT_STRIDE));
   const float inv = 1.f / L;
-  out[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (tid == 0 && a.lse) a.lse[(size_t)b * NH + h] = (M + log2f(L)) * kLn2;
+  s_out[n32][cols + 0] = acc.x * inv;
+  s_out[n32][cols + 1] = acc.y * inv;
+  s_out[n32][cols + 2] = acc.z * inv;
+  s_out[n32][cols + 3] = acc.w * inv;
+  __syncthreads();
+  *out = make_float4(s_out[h_r][c_r], s_out[h_r][c_r + 1], s_out[h_r][c_r + 2], s_out[h_r][c_r + 3]);
+  if (cb == 0 && tid < CMB_HB && a.lse)
+    a.lse[(size_t)b * NH + hb * CMB_HB + tid] = (M + log2f(L)) * kLn2;
 }
+
+constexpr int MAX_G = 256;   // split workgroups per call (one per compute unit)
 
 int choose_groups(int64_t total_rows_hint, int num_cu) {
   int64_t g = (total_rows_hint + MIN_ROWS_PER_WG - 1) / MIN_ROWS_PER_WG;
@@ -950,7 +987,8 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   int64_t* prefix = (int64_t*)(w + L.pre_off);
   int32_t* ovf = (int32_t*)(w + L.ovf_off);
   WgRec* rec = (WgRec*)(w + L.rec_off);
-  k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, err_flag);
+  int2* seqinfo = (int2*)(w + L.si_off);
+  k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, seqinfo, err_flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SplitArgs a;
@@ -977,6 +1015,7 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   c.cache = (const __bf16*)cache;
   c.offsets = offsets;
   c.prefix = prefix;
+  c.seqinfo = seqinfo;
   c.ovf = ovf;
   c.part_o = a.part_o;
   c.part_ml = a.part_ml;
@@ -985,7 +1024,7 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   c.B = B;
   c.G = G;
   c.scale_log2 = a.scale_log2;
-  k_combine<<<dim3(NH, B), CMB_THREADS, 0, st>>>(c);
+  k_combine<<<dim3((NH / CMB_HB) * (DC / CMB_CB), B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();
 }
 

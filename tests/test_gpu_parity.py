@@ -123,6 +123,26 @@ def test_decode_latent_definition(hint):
         compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
 
 
+def test_decode_more_workgroups_than_rows():
+    """Fewer rows than split workgroups (a large hint over a small batch):
+    most workgroup ranges are empty, several fall inside one sequence's span
+    and must count as weight-0 pieces there."""
+    lens = [1, 2, 3, 40, 5, 70, 1, 33]
+    w = small_v3(lens, seed=11)
+    rng = np.random.default_rng(12)
+    q_lat = I.bf16_bits(rng.standard_normal((w.B, 128, 512)).astype(np.float32) * 0.05)
+    q_pe = I.bf16_bits(rng.standard_normal((w.B, 128, 64)).astype(np.float32))
+    say(f"decode-only lens={lens} hint=10**7 (empty ranges)")
+    got, glse, err = _decode_only(w, q_lat, q_pe, 10 ** 7)
+    assert err == 0
+    scale = 1 / math.sqrt(192)
+    for b in range(w.B):
+        rows = w.f64(w.seq_rows(b))
+        ref, lse = O.latent_attention(w.f64(q_lat[b]), w.f64(q_pe[b]), rows[:, :512], rows[:, 512:], scale)
+        compare(got[b], ref, f"b={b} T={lens[b]} o_lat")
+        compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
+
+
 def test_single_row_is_exact():
     """T = 1: the only weight is exp2(0) = 1, so o_lat is the row itself, bit for bit."""
     w = small_v3([1, 1, 1])
