@@ -64,6 +64,10 @@ constexpr int QK_PF = 6;                              // QK fragments in flight
 constexpr int PV_PF = 4;                              // PV fragment pairs in flight
 constexpr float OVF_TH = 64.0f;                       // log2 units
 constexpr int MIN_ROWS_PER_WG = 256;
+// Batches up to SPL_MAXB sequences are scanned inside the split kernel (the
+// prefix sits in LDS next to the stages); larger ones by a scan kernel.
+constexpr int SPL_MAXB = 1024;
+constexpr int SPL_PER = SPL_MAXB / THREADS;           // sequences per lane
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
@@ -79,10 +83,10 @@ static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
 struct PartialLayout {
   size_t o_off;    // fp16 [slots][NH / 32][DC / 32][2 KiB] O / l of the piece, lane order
   size_t ml_off;   // float [slots][NH][2]   (m in log2 units, l)
-  size_t pre_off;  // int64 [B + 1] prefix of valid lengths
-  size_t ovf_off;  // int32 [B] sequence needs the fallback recompute
+  size_t pre_off;  // int64 [B + 1] prefix of valid lengths (scan kernel path)
+  size_t flag_off; // int32 [slots][WAVES] the piece needs the fallback recompute
   size_t rec_off;  // WgRec [G] each workgroup's row range and first sequence
-  size_t si_off;   // int2 [B] first range holding the sequence, number of ranges
+  size_t si_off;   // int4 [B] first range holding the sequence, ranges, valid length
   size_t bytes;
 };
 
@@ -102,26 +106,46 @@ __host__ __device__ inline PartialLayout partial_layout(int B, int G) {
   PartialLayout L;
   size_t slots = (size_t)G + (size_t)B;   // slot = g + b  <  G + B - 1
   L.pre_off = 0;
-  L.ovf_off = align256(sizeof(int64_t) * (B + 1));
-  L.o_off = L.ovf_off + align256(sizeof(int32_t) * B);
+  L.flag_off = align256(sizeof(int64_t) * (B + 1));
+  L.o_off = L.flag_off + align256(sizeof(int32_t) * WAVES * slots);
   L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(_Float16));
   L.rec_off = L.ml_off + align256(slots * NH * 2 * sizeof(float));
   L.si_off = L.rec_off + align256(sizeof(WgRec) * (size_t)G);
-  L.bytes = L.si_off + align256(sizeof(int2) * (size_t)B);
+  L.bytes = L.si_off + align256(sizeof(int4) * (size_t)B);
   return L;
 }
 
+// Ranges: workgroup g owns rows [floor(g total / G), floor((g + 1) total / G)).
+// Below 2^40 rows (G <= 1024) the quotients are formed in fp64: numerator
+// and divisor are exact, and the rounding error of the quotient (relative
+// 2^-53) is far below the distance 1 / divisor from the true quotient to the
+// next integer, so the floor is the exact integer quotient.
+constexpr int64_t FP64_EXACT_ROWS = (int64_t)1 << 40;
+
+__device__ __forceinline__ int64_t floor_div(int64_t n, int64_t d, bool fp64) {
+  return fp64 ? (int64_t)floor((double)n / (double)d) : n / d;
+}
+
 __device__ __forceinline__ int64_t range_start(int g, int64_t total, int G) {
-  return (int64_t)((int64_t)g * total) / G;
+  return floor_div((int64_t)g * total, G, total < FP64_EXACT_ROWS);
 }
 
 // Largest g in [0, G) with range_start(g) <= p (p < total).
 __device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
-  int g = (int)((p * (int64_t)G) / total);
+  int g = (int)floor_div(p * (int64_t)G, total, total < FP64_EXACT_ROWS);
   if (g > G - 1) g = G - 1;
   while (g + 1 < G && range_start(g + 1, total, G) <= p) ++g;
   while (g > 0 && range_start(g, total, G) > p) --g;
   return g;
+}
+
+// What the combine needs of sequence b (rows [p0, p1) of the concatenated
+// valid lengths): the first range holding it, how many ranges it spans, and
+// its valid length (0: invalid, the result is NaN).
+__device__ __forceinline__ int4 seq_info(int64_t p0, int64_t p1, int64_t total, int G) {
+  if (p1 <= p0) return make_int4(0, 0, 0, 0);
+  const int lo = wg_of(p0, total, G);
+  return make_int4(lo, wg_of(p1 - 1, total, G) - lo + 1, (int)(p1 - p0), 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -140,8 +164,8 @@ constexpr int SCHED_LDS_B = 4096;   // prefix kept in LDS up to this many sequen
 __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ lens,
                                                          int64_t* __restrict__ prefix,
-                                                         int32_t* __restrict__ ovf, WgRec* __restrict__ rec,
-                                                         int2* __restrict__ seqinfo, int32_t* err_flag) {
+                                                         WgRec* __restrict__ rec,
+                                                         int4* __restrict__ seqinfo, int32_t* err_flag) {
   __shared__ int64_t wsum[SCHED_THREADS / 64];
   __shared__ int64_t carry;
   __shared__ int64_t s_pre[SCHED_LDS_B + 1];
@@ -167,7 +191,6 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
           v[j] = len;
         else if (err_flag)
           atomicOr(err_flag, MLA_DEVERR_LENS);
-        ovf[b] = 0;
       }
       tsum += v[j];
     }
@@ -210,6 +233,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
       WgRec r = {};
       rec[g] = r;
     }
+    for (int b = tid; b < B; b += SCHED_THREADS) seqinfo[b] = make_int4(0, 0, 0, 0);
     return;
   }
   auto pre = [&](int i) -> int64_t { return in_lds ? s_pre[i] : prefix[i]; };
@@ -233,13 +257,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     rec[g] = r;
   }
   for (int b = tid; b < B; b += SCHED_THREADS) {
-    const int64_t p0 = pre(b), p1 = pre(b + 1);
-    int2 si = make_int2(0, 0);
-    if (p1 > p0) {
-      si.x = wg_of(p0, total, G);
-      si.y = wg_of(p1 - 1, total, G) - si.x + 1;
-    }
-    seqinfo[b] = si;
+    seqinfo[b] = seq_info(pre(b), pre(b + 1), total, G);
   }
 }
 
@@ -247,7 +265,11 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
 // Split kernel.
 // ---------------------------------------------------------------------------
 struct SplitArgs {
-  const WgRec* rec;
+  const WgRec* rec;      // scan-kernel path only
+  const int32_t* lens;   // in-kernel scan path only
+  int32_t* err_flag;
+  int4* seqinfo;         // written by the in-kernel scan path
+  int32_t* flags;        // [slots][WAVES]
   float* o_lat;   // a sequence handled whole by one workgroup is written here
   float* lse;
   const __bf16* q_lat;
@@ -255,7 +277,6 @@ struct SplitArgs {
   const char* cache;
   const int32_t* offsets;
   const int64_t* prefix;
-  int32_t* ovf;
   _Float16* part_o;
   float* part_ml;
   int B;
@@ -345,8 +366,14 @@ __device__ __forceinline__ int swz(int r) {
 // One wave per SIMD holds Q (144 VGPRs) and O (256 accumulation registers);
 // latency is hidden inside the wave by loading LDS fragments several
 // steps ahead of the MFMA that consumes them.
+template <bool SCAN>
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
+  // in-kernel scan (SCAN): prefix of the valid lengths and the offsets
+  __shared__ int64_t s_pre[SCAN ? SPL_MAXB + 1 : 1];
+  __shared__ int32_t s_off[SCAN ? SPL_MAXB : 1];
+  __shared__ int64_t s_wsum[WAVES];
+  __shared__ int32_t s_first;
 
   // Range index of this workgroup.  Workgroups are dealt to the 8 XCDs
   // round-robin (block i runs on XCD i % 8); giving each XCD a contiguous
@@ -359,18 +386,101 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   const int g32 = lane >> 5;          // which half of the wave
   const int n32 = lane & 31;          // head within the wave / row within the tile
 
-  const WgRec rec = a.rec[g];
-  const int64_t start = rec.start, end = rec.end;
+  // This workgroup's rows [start, end) and the sequence b holding row start.
+  int64_t start, end, seq_begin0, seq_end0;
+  int b0, off0;
+  if constexpr (SCAN) {
+    // Every workgroup scans the (at most SPL_MAXB) lengths itself: four
+    // sequences per lane, a wave scan, then the four wave totals.
+    const int tid = threadIdx.x;
+    const int B = a.B, G = a.G;
+    int64_t v[SPL_PER];
+    int64_t tsum = 0;
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < SPL_PER; ++j) {
+      const int bb = tid * SPL_PER + j;
+      v[j] = 0;
+      if (bb < B) {
+        const int len = a.lens[bb];
+        const int o0 = a.offsets[bb];
+        const int cap = a.offsets[bb + 1] - o0;
+        if (len >= 1 && len <= cap)
+          v[j] = len;
+        else
+          bad = 1;
+        s_off[bb] = o0;
+      }
+      tsum += v[j];
+    }
+    int64_t x = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    if (tid == 0) {
+      s_pre[0] = 0;
+      s_first = 0;
+    }
+    __syncthreads();
+    int64_t total = 0, run = x - tsum;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      total += s_wsum[w];
+      if (w < wave) run += s_wsum[w];
+    }
+    start = total > 0 ? range_start(g, total, G) : 0;
+    end = total > 0 ? range_start(g + 1, total, G) : 0;
+#pragma unroll
+    for (int j = 0; j < SPL_PER; ++j) {
+      const int bb = tid * SPL_PER + j;
+      if (bb < B) {
+        s_pre[bb + 1] = run + v[j];
+        if (v[j] > 0 && run <= start && start < run + v[j]) s_first = bb;   // one writer
+      }
+      run += v[j];
+    }
+    bad = __syncthreads_or(bad);
+    if (g == 0 && tid == 0 && bad && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_LENS);
+    // what the combine needs of sequences g, g + G, g + 2G, ...
+    for (int bb = g + tid * G; bb < B; bb += THREADS * G)
+      a.seqinfo[bb] = seq_info(s_pre[bb], s_pre[bb + 1], total, G);
+    if (total <= 0) return;   // no valid sequence: the combine writes NaN
+    b0 = s_first;
+    seq_begin0 = s_pre[b0];
+    seq_end0 = s_pre[b0 + 1];
+    off0 = s_off[b0];
+  } else {
+    const WgRec rec = a.rec[g];
+    start = rec.start;
+    end = rec.end;
+    seq_begin0 = rec.seq_begin;
+    seq_end0 = rec.seq_end;
+    b0 = rec.b;
+    off0 = rec.off_b;
+  }
+  auto pre = [&](int i) -> int64_t {
+    if constexpr (SCAN) return s_pre[i];
+    else return a.prefix[i];
+  };
+  auto off_of = [&](int i) -> int {
+    if constexpr (SCAN) return s_off[i];
+    else return a.offsets[i];
+  };
+
   if (start >= end) {
     // An empty range (fewer rows than workgroups) can fall inside the span of
-    // ranges the combine walks for sequence rec.b: leave it a zero partial
-    // with weight 0 there (m = -inf, l = 0).
-    if (rec.seq_end > rec.seq_begin) {
-      const size_t slot = (size_t)g + (size_t)rec.b;
+    // ranges the combine walks for sequence b0: leave it a zero partial
+    // with weight 0 there (m = -inf, l = 0) and no fallback flag.
+    if (seq_end0 > seq_begin0) {
+      const size_t slot = (size_t)g + (size_t)b0;
       uint4* po = (uint4*)(a.part_o + slot * NH * DC);
       for (int i = threadIdx.x; i < NH * DC / 8; i += THREADS) po[i] = make_uint4(0, 0, 0, 0);
       if (threadIdx.x < NH)
         ((float2*)a.part_ml)[slot * NH + threadIdx.x] = make_float2(-INFINITY, 0.f);
+      if (threadIdx.x < WAVES) a.flags[slot * WAVES + threadIdx.x] = 0;
     }
     return;
   }
@@ -437,7 +547,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
   const int head = wave * HPW + n32;
 
-  int b = rec.b;   // first sequence touching [start, end)
+  int b = b0;   // first sequence touching [start, end)
 
   int64_t pos = start;
   bool first_segment = true;
@@ -446,14 +556,14 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     int64_t seq_begin, seq_endx;
     int off_b;
     if (first_segment) {
-      seq_begin = rec.seq_begin;
-      seq_endx = rec.seq_end;
-      off_b = rec.off_b;
+      seq_begin = seq_begin0;
+      seq_endx = seq_end0;
+      off_b = off0;
     } else {
-      while (a.prefix[b + 1] <= pos) ++b;
-      seq_begin = a.prefix[b];
-      seq_endx = a.prefix[b + 1];
-      off_b = a.offsets[b];
+      while (pre(b + 1) <= pos) ++b;
+      seq_begin = pre(b);
+      seq_endx = pre(b + 1);
+      off_b = off_of(b);
     }
     const int64_t seg_end = end < seq_endx ? end : seq_endx;
     const int t0 = (int)(pos - seq_begin);
@@ -727,9 +837,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       }
       S_cur = S_next;
     }
-    if (__any(ovf_any)) {
-      if (lane == 0) a.ovf[b] = 1;
-    }
+    const size_t slot = (size_t)g + (size_t)b;
     // DMAs issued during the last tiles only fill stages this piece no
     // longer reads; they must land before a next piece reuses the stages.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -749,6 +857,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       if (g32 == 0 && a.lse) a.lse[(size_t)b * NH + head] = (m_ref + log2f(l_tot)) * kLn2;
+      const int flag = __any(ovf_any) ? 1 : 0;
+      if (lane == 0) a.flags[slot * WAVES + wave] = flag;
       pos = seg_end;
       continue;
     }
@@ -759,7 +869,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // flagged for the fallback instead.  The values leave in the
     // accumulator's own lane order (the combine kernel reads that order), so
     // every store instruction writes 512 contiguous bytes.
-    const size_t slot = (size_t)g + (size_t)b;
     _Float16* po = a.part_o + (slot * NH + wave * HPW) * DC;   // this wave's 32 heads
     float amax = 0.f;
 #pragma unroll
@@ -778,9 +887,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // once would need as many VGPRs
         __builtin_amdgcn_sched_barrier(0);
       }
-    if (__any(amax > PART_MAX)) {
-      if (lane == 0) a.ovf[b] = 1;
-    }
+    const int flag = __any(ovf_any || amax > PART_MAX) ? 1 : 0;
+    if (lane == 0) a.flags[slot * WAVES + wave] = flag;
     if (g32 == 0) {
       float* pm = a.part_ml + (slot * NH + head) * 2;
       pm[0] = m_ref;
@@ -798,9 +906,8 @@ struct CombineArgs {
   const __bf16* q_pe;
   const __bf16* cache;
   const int32_t* offsets;
-  const int64_t* prefix;
-  const int2* seqinfo;
-  const int32_t* ovf;
+  const int4* seqinfo;
+  const int32_t* flags;
   const _Float16* part_o;
   const float* part_ml;
   float* o_lat;
@@ -888,64 +995,71 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   constexpr int NCB = DC / CMB_CB;
   const int hb = blockIdx.x / NCB, cb = blockIdx.x % NCB, b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
-  const int2 si = a.seqinfo[b];
+  const int4 si = a.seqinfo[b];   // first range, ranges, valid length
   const int h_r = tid >> 3, c_r = (tid & 7) * 4;   // this lane's output row / columns
   float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r);
-  if (p1 <= p0) {   // invalid length: NaN result (the error flag is set)
+  if (si.z <= 0) {   // invalid length: NaN result (the error flag is set)
     const float nan = __builtin_nanf("");
     *out = make_float4(nan, nan, nan, nan);
     if (cb == 0 && tid < CMB_HB && a.lse) a.lse[(size_t)b * NH + hb * CMB_HB + tid] = nan;
     return;
   }
-  if (a.ovf[b]) {
-    // the NCB blocks of this head block share its heads out, whole rows each
-    for (int k = cb; k < CMB_HB; k += NCB) recompute_head(a, b, hb * CMB_HB + k, (int)(p1 - p0));
+  const int npiece = si.y;
+  const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
+  int flag = 0;
+  for (int k = tid; k < npiece * WAVES; k += CMB_THREADS) flag |= a.flags[slot0 * WAVES + k];
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float M = -INFINITY, L = 0.f;
+  const int n32 = tid & 31, cols = 8 * (tid >> 6) + 4 * ((tid >> 5) & 1);
+  if (npiece > 1) {
+    // One pass, 16 pieces at a time: the running max M moves only between
+    // groups, rescaling what was accumulated so far.
+    const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
+    constexpr size_t SLOT_STRIDE = (size_t)NH * DC;
+    const _Float16* po = a.part_o + slot0 * SLOT_STRIDE + ((size_t)hb * NCB + cb) * (CMB_HB * CMB_CB) + 4 * tid;
+    constexpr int GRP = 16;
+    for (int i = 0; i < npiece; i += GRP) {
+      halfx4 v[GRP];
+      float2 m2[GRP];
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int k = i + j < npiece ? i + j : npiece - 1;   // clamped; weight 0 below
+        v[j] = *(const halfx4*)(po + (size_t)k * SLOT_STRIDE);
+        m2[j] = ml[(size_t)k * NH];
+      }
+      float Mg = M;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j)
+        if (i + j < npiece) Mg = fmaxf(Mg, m2[j].x);
+      if (Mg > M) {   // M = -inf only before any finite piece: nothing to rescale
+        const float r = M == -INFINITY ? 0.f : exp2f(M - Mg);
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+        L *= r;
+        M = Mg;
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const bool use = i + j < npiece && m2[j].x != -INFINITY;
+        const float w = use ? exp2f(m2[j].x - M) * m2[j].y : 0.f;   // 2^(m - M) l
+        L += w;
+        acc.x += w * (float)v[j][0];
+        acc.y += w * (float)v[j][1];
+        acc.z += w * (float)v[j][2];
+        acc.w += w * (float)v[j][3];
+      }
+    }
+  }
+  if (__syncthreads_or(flag)) {
+    // a piece overflowed: the NCB blocks of this head block share its heads
+    // out and recompute whole rows each
+    for (int k = cb; k < CMB_HB; k += NCB) recompute_head(a, b, hb * CMB_HB + k, si.z);
     return;
   }
-  const int npiece = si.y;
   if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
-
-  const int n32 = tid & 31, cols = 8 * (tid >> 6) + 4 * ((tid >> 5) & 1);
-  const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
-  const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
-  float M = -INFINITY;
-  {
-    int i = 0;
-    for (; i + 8 <= npiece; i += 8) {
-      float2 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = ml[(size_t)(i + j) * NH];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) M = fmaxf(M, v[j].x);
-    }
-    for (; i < npiece; ++i) M = fmaxf(M, ml[(size_t)i * NH].x);
-  }
-  constexpr size_t SLOT_STRIDE = (size_t)NH * DC;
-  const _Float16* po = a.part_o + slot0 * SLOT_STRIDE + ((size_t)hb * NCB + cb) * (CMB_HB * CMB_CB) + 4 * tid;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
-  auto add = [&](const float2 mlv, const halfx4 v) {
-    const float w = mlv.x == -INFINITY ? 0.f : exp2f(mlv.x - M) * mlv.y;   // 2^(m - M) l
-    L += w;
-    acc.x += w * (float)v[0];
-    acc.y += w * (float)v[1];
-    acc.z += w * (float)v[2];
-    acc.w += w * (float)v[3];
-  };
-  int i = 0;
-  for (; i + 8 <= npiece; i += 8) {
-    halfx4 v[8];
-    float2 m8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = *(const halfx4*)(po + (size_t)(i + j) * SLOT_STRIDE);
-      m8[j] = ml[(size_t)(i + j) * NH];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) add(m8[j], v[j]);
-  }
-  for (; i < npiece; ++i) add(ml[(size_t)i * NH], *(const halfx4*)(po + (size_t)i * SLOT_STRIDE));
   const float inv = 1.f / L;
   s_out[n32][cols + 0] = acc.x * inv;
   s_out[n32][cols + 1] = acc.y * inv;
@@ -985,14 +1099,15 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   const PartialLayout L = partial_layout(B, G);
   char* w = (char*)ws;
   int64_t* prefix = (int64_t*)(w + L.pre_off);
-  int32_t* ovf = (int32_t*)(w + L.ovf_off);
   WgRec* rec = (WgRec*)(w + L.rec_off);
-  int2* seqinfo = (int2*)(w + L.si_off);
-  k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, ovf, rec, seqinfo, err_flag);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  int4* seqinfo = (int4*)(w + L.si_off);
+  int32_t* flags = (int32_t*)(w + L.flag_off);
   SplitArgs a;
   a.rec = rec;
+  a.lens = lens;
+  a.err_flag = err_flag;
+  a.seqinfo = seqinfo;
+  a.flags = flags;
   a.o_lat = o_lat;
   a.lse = lse;
   a.q_lat = (const __bf16*)q_lat;
@@ -1000,23 +1115,28 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   a.cache = (const char*)cache;
   a.offsets = offsets;
   a.prefix = prefix;
-  a.ovf = ovf;
   a.part_o = (_Float16*)(w + L.o_off);
   a.part_ml = (float*)(w + L.ml_off);
   a.B = B;
   a.G = G;
   a.scale_log2 = s.scale * kLog2e;
-  k_split<<<G, THREADS, 0, st>>>(a);
-  e = hipGetLastError();
+  if (B <= SPL_MAXB) {
+    k_split<true><<<G, THREADS, 0, st>>>(a);
+  } else {
+    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, rec, seqinfo, err_flag);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_split<false><<<G, THREADS, 0, st>>>(a);
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CombineArgs c;
   c.q_lat = a.q_lat;
   c.q_pe = a.q_pe;
   c.cache = (const __bf16*)cache;
   c.offsets = offsets;
-  c.prefix = prefix;
   c.seqinfo = seqinfo;
-  c.ovf = ovf;
+  c.flags = flags;
   c.part_o = a.part_o;
   c.part_ml = a.part_ml;
   c.o_lat = o_lat;

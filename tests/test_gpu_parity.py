@@ -143,6 +143,27 @@ def test_decode_more_workgroups_than_rows():
         compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
 
 
+@pytest.mark.parametrize("B", [1024, 1100])
+def test_decode_large_batch(B):
+    """Many short sequences: B = 1024 is the largest batch whose lengths the
+    split kernel scans itself, B = 1100 goes through the separate scan
+    kernel.  Every 37th sequence and the last ones are checked."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 41, size=B).astype(np.int32)
+    w = small_v3(lens, seed=B)
+    q_lat = I.bf16_bits(rng.standard_normal((B, 128, 512)).astype(np.float32) * 0.05)
+    q_pe = I.bf16_bits(rng.standard_normal((B, 128, 64)).astype(np.float32))
+    say(f"decode-only B={B} lens in [1, 40] total={int(lens.sum())}")
+    got, glse, err = _decode_only(w, q_lat, q_pe)
+    assert err == 0
+    scale = 1 / math.sqrt(192)
+    for b in sorted(set(range(0, B, 37)) | {B - 2, B - 1}):
+        rows = w.f64(w.seq_rows(b))
+        ref, lse = O.latent_attention(w.f64(q_lat[b]), w.f64(q_pe[b]), rows[:, :512], rows[:, 512:], scale)
+        compare(got[b], ref, f"b={b} T={lens[b]} o_lat")
+        compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
+
+
 def test_single_row_is_exact():
     """T = 1: the only weight is exp2(0) = 1, so o_lat is the row itself, bit for bit."""
     w = small_v3([1, 1, 1])
