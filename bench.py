@@ -13,7 +13,7 @@ that consecutive steps do not hit in the 256 MB Infinity Cache.
 
 Prints ONE JSON line on stdout (progress goes to stderr).  ``value`` is
 cache-tokens/s of the whole step; ``roofline`` is for the mla_decode_attn call
-(its three kernels: length scan, split attention, combine), timed with HIP
+(its kernels: split attention with the length scan, combine), timed with HIP
 events on the launch stream inside the timed loop.
 """
 
@@ -250,7 +250,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    # Roofline: mla_decode_attn alone (its scan, split and combine kernels),
+    # Roofline: mla_decode_attn alone (its split and combine kernels),
     # HIP events on the launch stream around each call, same input rotation.
     ev = []
     for i in range(args.steps):
@@ -306,7 +306,7 @@ def main():
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
-                     "kernel": "mla_decode_attn (scan + split attention + combine)",
+                     "kernel": "mla_decode_attn (split attention with length scan + combine)",
                      "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
                      "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,
                      "mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},

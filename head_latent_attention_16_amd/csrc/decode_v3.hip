@@ -284,11 +284,27 @@ struct SplitArgs {
   float scale_log2;
 };
 
+// Wave-uniform values read from LDS or memory arrive in vector registers;
+// these move them to scalar registers so they do not occupy VGPRs.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uniform_i32(int v) { return (int)__builtin_amdgcn_readfirstlane((uint32_t)v); }
+
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = (uint64_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// The same DMA from a per-lane 64-bit address.
+__device__ __forceinline__ void dma_16B_at(uint32_t lds_addr, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src));
 }
 
 __device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const char* base) {
@@ -382,9 +398,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   const int g = (a.G % 8 == 0) ? (int)(blockIdx.x % 8) * (a.G / 8) + (int)(blockIdx.x / 8)
                                : (int)blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int g32 = lane >> 5;          // which half of the wave
-  const int n32 = lane & 31;          // head within the wave / row within the tile
+  const int lane_id = threadIdx.x & 63;
 
   // This workgroup's rows [start, end) and the sequence b holding row start.
   int64_t start, end, seq_begin0, seq_end0;
@@ -417,9 +431,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int64_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      if (lane_id >= o) x += y;
     }
-    if (lane == 63) s_wsum[wave] = x;
+    if (lane_id == 63) s_wsum[wave] = x;
     if (tid == 0) {
       s_pre[0] = 0;
       s_first = 0;
@@ -448,26 +462,28 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     for (int bb = g + tid * G; bb < B; bb += THREADS * G)
       a.seqinfo[bb] = seq_info(s_pre[bb], s_pre[bb + 1], total, G);
     if (total <= 0) return;   // no valid sequence: the combine writes NaN
-    b0 = s_first;
-    seq_begin0 = s_pre[b0];
-    seq_end0 = s_pre[b0 + 1];
-    off0 = s_off[b0];
+    start = uniform_i64(start);
+    end = uniform_i64(end);
+    b0 = uniform_i32(s_first);
+    seq_begin0 = uniform_i64(s_pre[b0]);
+    seq_end0 = uniform_i64(s_pre[b0 + 1]);
+    off0 = uniform_i32(s_off[b0]);
   } else {
     const WgRec rec = a.rec[g];
-    start = rec.start;
-    end = rec.end;
-    seq_begin0 = rec.seq_begin;
-    seq_end0 = rec.seq_end;
-    b0 = rec.b;
-    off0 = rec.off_b;
+    start = uniform_i64(rec.start);
+    end = uniform_i64(rec.end);
+    seq_begin0 = uniform_i64(rec.seq_begin);
+    seq_end0 = uniform_i64(rec.seq_end);
+    b0 = uniform_i32(rec.b);
+    off0 = uniform_i32(rec.off_b);
   }
   auto pre = [&](int i) -> int64_t {
-    if constexpr (SCAN) return s_pre[i];
-    else return a.prefix[i];
+    if constexpr (SCAN) return uniform_i64(s_pre[i]);
+    else return uniform_i64(a.prefix[i]);
   };
   auto off_of = [&](int i) -> int {
-    if constexpr (SCAN) return s_off[i];
-    else return a.offsets[i];
+    if constexpr (SCAN) return uniform_i32(s_off[i]);
+    else return uniform_i32(a.offsets[i]);
   };
 
   if (start >= end) {
@@ -487,25 +503,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
-  // DMA: wave-instruction j = 9 wave + k covers LDS chunks [64 j, 64 j + 64);
-  // lane i fills chunk p = 64 j + i, which holds logical chunk
-  // (p % 72) ^ swz(row) of row p / 72.  The 64 chunks span at most two rows
-  // (72 > 64), so everything but a per-lane select is wave-uniform.
-  // The nine per-lane source offsets (< 36864) are computed once and kept
-  // as 16-bit pairs in five registers; each DMA extracts its own with one
-  // instruction.
-  uint32_t dma_pk[(DMA_PER_WAVE + 1) / 2];
-#pragma unroll
-  for (int j = 0; j < (DMA_PER_WAVE + 1) / 2; ++j) dma_pk[j] = 0;
-#pragma unroll
-  for (int k = 0; k < DMA_PER_WAVE; ++k) {
-    const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
-    const int r = p / CHUNKS;
-    const int c = (p % CHUNKS) ^ swz(r);
-    dma_pk[k >> 1] |= (uint32_t)(r * ROWB + c * 16) << (16 * (k & 1));
-  }
-  auto dma_off = [&](int k) -> uint32_t { return (dma_pk[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
-
   // QK A-fragment (32x32x16): row n32, logical chunk 2 kk + g32 stored at
   // (2 kk + g32) ^ swz(n32).  For kk = 4u + v the low three bits are
   // (2v + g32) ^ swz(n32); the rest is the constant 8u chunks.
@@ -513,7 +510,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   // block from an opaque copy of the lane index (a handful of VALU
   // instructions) rather than kept in registers across the whole loop.
   auto make_qk_off = [&](uint32_t (&o)[4]) {
-    int ln = lane;
+    int ln = lane_id;
     asm volatile("" : "+v"(ln));
     ln &= 63;
     const int n = ln & 31, h = ln >> 5;
@@ -528,7 +525,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   // Logical chunk 4 cb + e sits at (4 cb + e) ^ swz(8 rd + rr)
   //   = 4 (cb ^ bb) + (e ^ ff),  bb = bit 2 of swz, ff = its low two bits.
   auto make_tr_base = [&](uint32_t (&t)[2][2]) {
-    int ln = lane;
+    int ln = lane_id;
     asm volatile("" : "+v"(ln));
     ln &= 63;
     const int Gq = ln >> 4;
@@ -545,13 +542,39 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     }
   };
 
-  const int head = wave * HPW + n32;
-
   int b = b0;   // first sequence touching [start, end)
 
   int64_t pos = start;
   bool first_segment = true;
   while (pos < end) {
+    // Lane-derived values are rebuilt for every piece from an opaque copy of
+    // the lane index, so none of them stays live (and spilled) across the
+    // previous piece's epilogue.
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    lane &= 63;
+    const int g32 = lane >> 5;          // which half of the wave
+    const int n32 = lane & 31;          // head within the wave / row within the tile
+    const int head = wave * HPW + n32;
+
+    // DMA: wave-instruction j = 9 wave + k covers LDS chunks [64 j, 64 j + 64);
+    // lane i fills chunk p = 64 j + i, which holds logical chunk
+    // (p % 72) ^ swz(row) of row p / 72.  The 64 chunks span at most two rows
+    // (72 > 64), so everything but a per-lane select is wave-uniform.
+    // The nine per-lane source offsets (< 36864) are kept as 16-bit pairs in
+    // five registers; each DMA extracts its own with one instruction.
+    uint32_t dma_pk[(DMA_PER_WAVE + 1) / 2];
+  #pragma unroll
+    for (int j = 0; j < (DMA_PER_WAVE + 1) / 2; ++j) dma_pk[j] = 0;
+  #pragma unroll
+    for (int k = 0; k < DMA_PER_WAVE; ++k) {
+      const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
+      const int r = p / CHUNKS;
+      const int c = (p % CHUNKS) ^ swz(r);
+      dma_pk[k >> 1] |= (uint32_t)(r * ROWB + c * 16) << (16 * (k & 1));
+    }
+    auto dma_off = [&](int k) -> uint32_t { return (dma_pk[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
+
     // The record describes the first sequence; later ones are looked up.
     int64_t seq_begin, seq_endx;
     int off_b;
@@ -575,13 +598,30 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     first_segment = false;
 
     // Q fragments (B operand of QK): head n32, features 16 kk + 8 g32 .. +8.
+    // A wave's 32 query rows [q_lat | q_pe] (1152 B each, like cache rows)
+    // are DMA'd into stage `wave` in the tile layout -- whole rows, so every
+    // DMA instruction reads full cache lines -- and then read out with the
+    // QK fragment pattern.  The stages are free until the tiles are issued.
     bf16x8 q[KSTEPS];
     {
-      const bf16x8* ql = (const bf16x8*)(a.q_lat + ((size_t)b * NH + head) * DC);
-      const bf16x8* qp = (const bf16x8*)(a.q_pe + ((size_t)b * NH + head) * DR);
+      const char* qlb = (const char*)(a.q_lat + ((size_t)b * NH + wave * HPW) * DC);
+      const char* qpb = (const char*)(a.q_pe + ((size_t)b * NH + wave * HPW) * DR);
+      const uint32_t qstage = lds0 + (uint32_t)(wave * TILEB);
+#pragma unroll 4
+      for (int j = 0; j < TILEB / 1024; ++j) {
+        const int p = 64 * j + lane;
+        const int r = p / CHUNKS;
+        const int c = (p % CHUNKS) ^ swz(r);
+        const char* src = c < DC / 8 ? qlb + r * (DC * 2) + c * 16 : qpb + r * (DR * 2) + (c - DC / 8) * 16;
+        dma_16B_at(qstage + (uint32_t)(j * 1024), src);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's own stage
+      uint32_t qo[4];
+      make_qk_off(qo);
+      const MLA_LDS char* T = (const MLA_LDS char*)lds + wave * TILEB;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        q[kk] = kk < DC / 16 ? ql[2 * kk + g32] : qp[2 * (kk - DC / 16) + g32];
+      for (int kk = 0; kk < KSTEPS; ++kk) q[kk] = *(const MLA_LDS bf16x8*)(T + qo[kk & 3] + (kk >> 2) * 128);
+      barrier_all_lds();   // every wave has its Q before the tiles overwrite the stages
     }
 
     // Every tile index t gets exactly DMA_PER_WAVE DMA instructions per wave,
@@ -615,14 +655,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // Wait for tile `it`: the tiles it+1 and it+2 were issued after it.
     auto wait_tile = [&]() { wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>(); };
 
-    // Three tiles ahead: tile it+3 goes into the stage of tile it-1.  The Q
-    // loads are consumed (waited for) right after tile 0's DMAs: the compiler
-    // counts only its own loads when it places waits, so a Q use after the
-    // tile 1 and 2 DMAs would make it wait for those tiles too.
-    issue_tile(0);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(q[kk]));
-    for (int t = 1; t < NSTAGE - 1; ++t) issue_tile(t);
+    // Three tiles ahead: tile it+3 goes into the stage of tile it-1.
+    for (int t = 0; t < NSTAGE - 1; ++t) issue_tile(t);
 
     floatx16 O[DC / 32];
 #pragma unroll
