@@ -13,12 +13,18 @@
 // * v_mfma_f32_32x32x16_bf16 with A = X (rows), B = W^T: both operands are
 //   "8 consecutive k per lane", so W fragments come straight from global
 //   memory into registers (64 contiguous bytes per lane per 64-wide k chunk,
-//   PD chunks in flight) and X fragments from LDS.
+//   PD chunks in flight) and X fragments from LDS, read FPF MFMAs ahead.
 // * Within a 64-wide k chunk, lane half g holds k = 32 g + 8 j .. +8 for
 //   k-step j; A and B use the same order, so the dot products are unchanged.
 // * fp32 X (an intermediate such as c^Q, or the attention output o) enters
 //   the bf16 MFMA as hi + lo with hi = bf16(x), lo = bf16(x - hi): two MFMAs
 //   per step, about 16 significant bits of x instead of 8.
+// * X is loaded in whole-row 16-byte pieces (every wave instruction reads
+//   full cache lines) and staged in LDS one chunk ahead.  The X and W loads
+//   of the chunk PD ahead and that staging are spread over the MFMA stream
+//   of the current chunk instead of stalling between chunks.
+// * The K splits are chosen so that all workgroups run in one round on the
+//   256 compute units.
 #include "common.h"
 #include "internal.h"
 
@@ -34,7 +40,8 @@ constexpr int GNT = 4 * GNW;      // columns per workgroup
 constexpr int KC = 64;            // k per chunk
 constexpr int XROWB = KC * 2;     // LDS bytes per row per chunk (bf16)
 constexpr int PD = 4;             // chunks of X and W in flight per wave
-constexpr int TARGET_WG = 384;
+constexpr int SLOTS = 256;        // workgroups per round (one per compute unit)
+constexpr int FPF = 8;            // A fragments read ahead
 
 struct GemmArgs {
   const void* X;        // [M][K], bf16 or fp32
@@ -73,10 +80,13 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   const __bf16* wrow = (nrow < a.N1 ? a.W1 + (size_t)nrow * a.K
                                     : a.W2 + (size_t)(nrow - a.N1) * a.K) + kb + 32 * g32;
 
-  // X staging: thread t fills row t/2, k half t&1 (32 values) of a chunk.
-  const int xr = tid >> 1, xh = tid & 1;
-  const bool xrow_ok = m0 + xr < a.M;
-  const size_t xoff = (size_t)(xrow_ok ? m0 + xr : 0) * a.K + kb + 32 * xh;
+  // X staging, coalesced: load i of thread t covers 16 bytes at flat index
+  // f = 256 i + t of the chunk, so each wave instruction reads whole rows.
+  // fp32: 16 per row (rows 16 i + t / 16); bf16: 8 per row (rows 32 i + t / 8).
+  constexpr int XPR = XF32 ? 16 : 8;   // 16-byte pieces per row per chunk
+  const int xq = tid % XPR;            // this thread's piece within its row
+  const int xrb = tid / XPR;           // its row within each group of 256 pieces
+  constexpr int XRS = 256 / XPR;       // rows per load index
 
   floatx16 acc[GMB];
 #pragma unroll
@@ -89,46 +99,51 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8*)(wrow + (size_t)c * KC + 8 * j);
   };
-  // X staging registers, PD chunks deep: X(k) and W(k) are issued together
-  // (X first), so waiting for X(c+1) before storing it to LDS never forces a
-  // newer W chunk to complete -- vmcnt completes in issue order.
+  // X staging registers, PD chunks deep: X(k) and W(k) are issued in the
+  // same chunk (X first), so waiting for X(c+1) before storing it to LDS
+  // never forces a newer W chunk to complete -- vmcnt completes in issue
+  // order.
   floatx4 xf[XF32 ? PD : 1][8];
   bf16x8 xb[XF32 ? 1 : PD][4];
   // Every global load in the main loop is unconditional (indices are clamped
   // to valid data and rows past M are zeroed when stored to LDS), so that the
   // compiler can count outstanding loads exactly.
+  auto xrow_src = [&](int i) { return (size_t)min(m0 + xrb + XRS * i, a.M - 1) * a.K + kb; };
   auto load_x = [&](int slot, int c) {
     if constexpr (XF32) {
-      const float* src = (const float*)a.X + xoff + (size_t)c * KC;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xf[slot][i] = *(const floatx4*)(src + 4 * i);
+      for (int i = 0; i < 8; ++i)
+        xf[slot][i] = *(const floatx4*)((const float*)a.X + xrow_src(i) + (size_t)c * KC + 4 * xq);
     } else {
-      const __bf16* src = (const __bf16*)a.X + xoff + (size_t)c * KC;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xb[slot][i] = *(const bf16x8*)(src + 8 * i);
+      for (int i = 0; i < 4; ++i)
+        xb[slot][i] = *(const bf16x8*)((const __bf16*)a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
     }
   };
   auto store_x = [&](int slot, int stage) {
-    const int sw = xsw(xr);
     if constexpr (XF32) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8 hi, lo;
+      for (int i = 0; i < 8; ++i) {
+        const int r = xrb + XRS * i;
+        const bool ok = m0 + r < a.M;
+        bf16x4 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = xrow_ok ? xf[slot][2 * q + (e >> 2)][e & 3] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float x = ok ? xf[slot][i][e] : 0.f;
           hi[e] = (__bf16)x;
           lo[e] = (__bf16)(x - (float)hi[e]);
         }
-        const int off = xr * XROWB + (((4 * xh + q) ^ sw) << 4);
-        *(bf16x8*)(xs[stage][0] + off) = hi;
-        *(bf16x8*)(xs[stage][NPLANE - 1] + off) = lo;
+        // k = 4 xq .. +4: 16-byte chunk xq / 2, half xq & 1
+        const int off = r * XROWB + ((((xq >> 1) ^ xsw(r)) << 4) | ((xq & 1) << 3));
+        *(bf16x4*)(xs[stage][0] + off) = hi;
+        *(bf16x4*)(xs[stage][NPLANE - 1] + off) = lo;
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int off = xr * XROWB + (((4 * xh + q) ^ sw) << 4);
-        *(bf16x8*)(xs[stage][0] + off) = xrow_ok ? xb[slot][q] : bf16x8{};
+      for (int i = 0; i < 4; ++i) {
+        const int r = xrb + XRS * i;
+        const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
+        *(bf16x8*)(xs[stage][0] + off) = m0 + r < a.M ? xb[slot][i] : bf16x8{};
       }
     }
   };
@@ -148,34 +163,73 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   for (int mb = 0; mb < GMB; ++mb) aoff[mb] = (uint32_t)((32 * mb + n32) * XROWB);
   const int asw = xsw(n32);   // (32 mb + n32) >> 1 & 7 == n32 >> 1 & 7
 
+  // Per-piece forms of the staging steps, so they can be spread over the
+  // MFMA stream of a chunk.
+  auto load_x_piece = [&](int slot, int c, int i) {
+    if constexpr (XF32)
+      xf[slot][i] = *(const floatx4*)((const float*)a.X + xrow_src(i) + (size_t)c * KC + 4 * xq);
+    else
+      xb[slot][i] = *(const bf16x8*)((const __bf16*)a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
+  };
+  auto store_x_piece = [&](int slot, int stage, int i) {
+    const int r = xrb + XRS * i;
+    const bool ok = m0 + r < a.M;
+    if constexpr (XF32) {
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = ok ? xf[slot][i][e] : 0.f;
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
+      }
+      const int off = r * XROWB + ((((xq >> 1) ^ xsw(r)) << 4) | ((xq & 1) << 3));
+      *(bf16x4*)(xs[stage][0] + off) = hi;
+      *(bf16x4*)(xs[stage][NPLANE - 1] + off) = lo;
+    } else {
+      const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
+      *(bf16x8*)(xs[stage][0] + off) = ok ? xb[slot][i] : bf16x8{};
+    }
+  };
+  constexpr int XPIECES = XF32 ? 8 : 4;     // 16-byte X loads per thread per chunk
+  constexpr int NF = 4 * NPLANE * GMB;      // MFMAs (= A fragments) per chunk
+  constexpr int PER_J = NPLANE * GMB;       // MFMAs per W fragment
+  constexpr int ST0 = NF / 2 - XPIECES;     // first step of the X staging
+  // (steps ST0, ST0 + 2, ... stage X(c + 1); after the last chunk this
+  // rewrites the idle stage with data nobody reads)
+
+  // Chunk c: NF steps, each one MFMA and the A-fragment read FPF ahead; the
+  // loads of chunk c + PD (X pieces first, then each W fragment as soon as
+  // the MFMAs of chunk c are done with its register) and the staging of
+  // X(c + 1) into the other LDS stage ride along in the MFMA gaps.
   // nch is a multiple of PD (K % (KC PD) == 0 and kper is a multiple of
   // KC PD), so the unrolled body has no early exit.
   for (int cb = 0; cb < nch; cb += PD) {
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int c = cb + s;
-      const int stage = c & 1;
+      const int stage = s & 1;   // == c & 1: cb is a multiple of PD (even)
+      const int cn = min(c + PD, nch - 1);
+      auto frag_addr = [&](int f) {
+        const int mb = f % GMB, pl = (f / GMB) % NPLANE, j = f / PER_J;
+        return xs[stage][pl] + aoff[mb] + (((4 * g32 + j) ^ asw) << 4);
+      };
+      bf16x8 fr[FPF];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = ((4 * g32 + j) ^ asw) << 4;
+      for (int f = 0; f < FPF; ++f) fr[f] = *(const bf16x8*)frag_addr(f);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < GMB; ++mb) {
-          const bf16x8 xa = *(const bf16x8*)(xs[stage][0] + aoff[mb] + ch);
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, wf[s][j], acc[mb], 0, 0, 0);
-          if constexpr (XF32) {
-            const bf16x8 xl = *(const bf16x8*)(xs[stage][NPLANE - 1] + aoff[mb] + ch);
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, wf[s][j], acc[mb], 0, 0, 0);
-          }
-        }
+      for (int f = 0; f < NF; ++f) {
+        const int mb = f % GMB, j = f / PER_J;
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % FPF], wf[s][j], acc[mb], 0, 0, 0);
+        if (f + FPF < NF) fr[f % FPF] = *(const bf16x8*)frag_addr(f + FPF);
+        if (f < XPIECES) load_x_piece(s, cn, f);
+        if (f % PER_J == PER_J - 1 && j < 3)   // W fragment j of chunk c is done
+          wf[s][j] = *(const bf16x8*)(wrow + (size_t)cn * KC + 8 * j);
+        if (f >= ST0 && f < ST0 + 2 * XPIECES && (f - ST0) % 2 == 0)
+          store_x_piece((s + 1) % PD, stage ^ 1, (f - ST0) / 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // keep the issue order: MFMAs, then chunk c+PD's loads (X first), then
-      // the staging of X(c+1)
-      __builtin_amdgcn_sched_barrier(0);
-      load_x(s, min(c + PD, nch - 1));
-      load_w(s, min(c + PD, nch - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      // after the last chunk this rewrites the idle stage with data nobody reads
-      store_x((s + 1) % PD, stage ^ 1);
+      wf[s][3] = *(const bf16x8*)(wrow + (size_t)cn * KC + 24);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -218,7 +272,7 @@ Plan plan(int M, int N, int K) {
   p.nblk = (N + GNT - 1) / GNT;
   p.mch = (M + GMR - 1) / GMR;
   const int kgr = K / (KC * PD);   // groups of PD chunks
-  int splits = (TARGET_WG + p.nblk * p.mch - 1) / (p.nblk * p.mch);
+  int splits = SLOTS / (p.nblk * p.mch);   // one round of workgroups
   int cap = kgr / 2;   // every split streams at least 2 groups (512 k)
   if (cap < 1) cap = 1;
   if (splits > cap) splits = cap;
