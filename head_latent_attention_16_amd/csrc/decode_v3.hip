@@ -948,6 +948,7 @@ struct CombineArgs {
   float* lse;
   int B;
   int G;
+  int cpw;   // column blocks per combine workgroup
   float scale_log2;
 };
 
@@ -1011,55 +1012,109 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
   __syncthreads();   // the LDS state is reused by the next head
 }
 
-// One workgroup per (32-head block, 32-column block, sequence).  A piece's
-// partial O is stored in the split kernel's accumulator lane order: for each
-// (piece, head block, column block) 2 KiB of fp16, entry t = 64 q4 + lane
-// holding columns 8 q4 + 4 (lane / 32) + [0, 4) of head lane % 32.  Lane t of
-// this block reads entry t of every piece, so each piece is one contiguous
-// 2 KiB read.  Each lane forms the weights of its own head itself: a first
-// pass over the pieces' m gives the common max M, the second weights every
-// piece by 2^(m - M) l while accumulating.  Pieces over empty ranges carry
-// m = -inf, l = 0 and zero rows.  The result is transposed through LDS so
-// that every head's 32 columns leave as one 128-byte store.
+// One workgroup per (32-head block, CPW 32-column blocks, sequence).  A
+// piece's partial O is stored in the split kernel's accumulator lane order:
+// for each (piece, head block, column block) 2 KiB of fp16, entry t =
+// 64 q4 + lane holding columns 8 q4 + 4 (lane / 32) + [0, 4) of head
+// lane % 32.  Lane t of this block reads entry t of every piece, so each
+// piece is one contiguous 2 KiB read.  Each lane forms the weights of its
+// own head itself: with the common max M of the pieces' m, piece i weighs
+// 2^(m_i - M) l_i.  Pieces over empty ranges carry m = -inf, l = 0 and zero
+// rows.  The result is transposed through LDS so that every head's 32
+// columns leave as one 128-byte store.  CPW > 1 (short sequences spanning
+// few pieces) gives each workgroup more loads in flight.
 constexpr int CMB_HB = HPW;          // heads per block (one split-kernel wave)
 constexpr int CMB_CB = 32;           // columns per block (one accumulator tile)
+constexpr int CMB_NCB = DC / CMB_CB;
+constexpr size_t CMB_SLOT = (size_t)NH * DC;   // fp16 per slot
 
-__global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
-  __shared__ float s_out[CMB_HB][CMB_CB + 1];
-  constexpr int NCB = DC / CMB_CB;
-  const int hb = blockIdx.x / NCB, cb = blockIdx.x % NCB, b = blockIdx.y;
+// Writes the normalised 32 x 32 block through LDS (lane t: head t / 8,
+// columns 4 (t % 8) ..+4 of the block).
+__device__ __forceinline__ void cmb_store(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb,
+                                          int cb, const float4& acc, float inv) {
   const int tid = threadIdx.x;
-  const int4 si = a.seqinfo[b];   // first range, ranges, valid length
-  const int h_r = tid >> 3, c_r = (tid & 7) * 4;   // this lane's output row / columns
-  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r);
-  if (si.z <= 0) {   // invalid length: NaN result (the error flag is set)
-    const float nan = __builtin_nanf("");
-    *out = make_float4(nan, nan, nan, nan);
-    if (cb == 0 && tid < CMB_HB && a.lse) a.lse[(size_t)b * NH + hb * CMB_HB + tid] = nan;
-    return;
-  }
-  const int npiece = si.y;
-  const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
-  int flag = 0;
-  for (int k = tid; k < npiece * WAVES; k += CMB_THREADS) flag |= a.flags[slot0 * WAVES + k];
-
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float M = -INFINITY, L = 0.f;
   const int n32 = tid & 31, cols = 8 * (tid >> 6) + 4 * ((tid >> 5) & 1);
-  if (npiece > 1) {
-    // One pass, 16 pieces at a time: the running max M moves only between
-    // groups, rescaling what was accumulated so far.
-    const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
-    constexpr size_t SLOT_STRIDE = (size_t)NH * DC;
-    const _Float16* po = a.part_o + slot0 * SLOT_STRIDE + ((size_t)hb * NCB + cb) * (CMB_HB * CMB_CB) + 4 * tid;
-    constexpr int GRP = 16;
+  s_out[n32][cols + 0] = acc.x * inv;
+  s_out[n32][cols + 1] = acc.y * inv;
+  s_out[n32][cols + 2] = acc.z * inv;
+  s_out[n32][cols + 3] = acc.w * inv;
+  __syncthreads();
+  const int h_r = tid >> 3, c_r = (tid & 7) * 4;
+  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r);
+  *out = make_float4(s_out[h_r][c_r], s_out[h_r][c_r + 1], s_out[h_r][c_r + 2], s_out[h_r][c_r + 3]);
+  __syncthreads();   // s_out is reused by the next column block
+}
+
+// Up to NP pieces: the (m, l) of all pieces and the entries of the first
+// column block are loaded together, the weights are kept in registers.
+template <int NP>
+__device__ __forceinline__ void cmb_small(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb,
+                                          int cb0, int cpw, int npiece, size_t slot0, float& M, float& L) {
+  const int tid = threadIdx.x, n32 = tid & 31;
+  const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
+  const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * (CMB_HB * CMB_CB) + 4 * tid;
+  float2 m2[NP];
+  float w[NP];
+  halfx4 v[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int k = i < npiece ? i : npiece - 1;   // clamped; weight 0 below
+    m2[i] = ml[(size_t)k * NH];
+    v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)cb0 * (CMB_HB * CMB_CB));
+  }
+  M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    if (i < npiece) M = fmaxf(M, m2[i].x);
+  L = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const bool use = i < npiece && m2[i].x != -INFINITY;
+    w[i] = use ? exp2f(m2[i].x - M) * m2[i].y : 0.f;   // 2^(m - M) l
+    L += w[i];
+  }
+  const float inv = 1.f / L;
+  for (int c = 0; c < cpw; ++c) {
+    if (c > 0) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int k = i < npiece ? i : npiece - 1;
+        v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)(cb0 + c) * (CMB_HB * CMB_CB));
+      }
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      acc.x += w[i] * (float)v[i][0];
+      acc.y += w[i] * (float)v[i][1];
+      acc.z += w[i] * (float)v[i][2];
+      acc.w += w[i] * (float)v[i][3];
+    }
+    cmb_store(a, s_out, b, hb, cb0 + c, acc, inv);
+  }
+}
+
+// Any number of pieces: one pass per column block, 16 pieces at a time,
+// the running max M moving only between groups (rescaling what was
+// accumulated so far).
+__device__ void cmb_large(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb, int cb0, int cpw,
+                          int npiece, size_t slot0, float& M, float& L) {
+  const int tid = threadIdx.x, n32 = tid & 31;
+  const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
+  constexpr int GRP = 16;
+  for (int c = 0; c < cpw; ++c) {
+    const _Float16* po =
+        a.part_o + slot0 * CMB_SLOT + ((size_t)hb * CMB_NCB + cb0 + c) * (CMB_HB * CMB_CB) + 4 * tid;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    M = -INFINITY;
+    L = 0.f;
     for (int i = 0; i < npiece; i += GRP) {
       halfx4 v[GRP];
       float2 m2[GRP];
 #pragma unroll
       for (int j = 0; j < GRP; ++j) {
         const int k = i + j < npiece ? i + j : npiece - 1;   // clamped; weight 0 below
-        v[j] = *(const halfx4*)(po + (size_t)k * SLOT_STRIDE);
+        v[j] = *(const halfx4*)(po + (size_t)k * CMB_SLOT);
         m2[j] = ml[(size_t)k * NH];
       }
       float Mg = M;
@@ -1086,23 +1141,49 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
         acc.w += w * (float)v[j][3];
       }
     }
+    cmb_store(a, s_out, b, hb, cb0 + c, acc, 1.f / L);
   }
+}
+
+__global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
+  __shared__ float s_out[CMB_HB][CMB_CB + 1];
+  const int cpw = a.cpw;
+  const int ngrp = CMB_NCB / cpw;
+  const int hb = blockIdx.x / ngrp, cb0 = (blockIdx.x % ngrp) * cpw, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int4 si = a.seqinfo[b];   // first range, ranges, valid length
+  if (si.z <= 0) {   // invalid length: NaN result (the error flag is set)
+    const float nan = __builtin_nanf("");
+    const int h_r = tid >> 3, c_r = (tid & 7) * 4;
+    for (int c = 0; c < cpw; ++c) {
+      float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + (cb0 + c) * CMB_CB + c_r);
+      *out = make_float4(nan, nan, nan, nan);
+    }
+    if (cb0 == 0 && tid < CMB_HB && a.lse) a.lse[(size_t)b * NH + hb * CMB_HB + tid] = nan;
+    return;
+  }
+  const int npiece = si.y;
+  const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
+  int flag = 0;
+  for (int k = tid; k < npiece * WAVES; k += CMB_THREADS) flag |= a.flags[slot0 * WAVES + k];
   if (__syncthreads_or(flag)) {
-    // a piece overflowed: the NCB blocks of this head block share its heads
-    // out and recompute whole rows each
-    for (int k = cb; k < CMB_HB; k += NCB) recompute_head(a, b, hb * CMB_HB + k, si.z);
+    // a piece overflowed: the blocks of this head block share its heads out
+    // and recompute whole rows each
+    for (int k = blockIdx.x % ngrp; k < CMB_HB; k += ngrp) recompute_head(a, b, hb * CMB_HB + k, si.z);
     return;
   }
   if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
-  const float inv = 1.f / L;
-  s_out[n32][cols + 0] = acc.x * inv;
-  s_out[n32][cols + 1] = acc.y * inv;
-  s_out[n32][cols + 2] = acc.z * inv;
-  s_out[n32][cols + 3] = acc.w * inv;
-  __syncthreads();
-  *out = make_float4(s_out[h_r][c_r], s_out[h_r][c_r + 1], s_out[h_r][c_r + 2], s_out[h_r][c_r + 3]);
-  if (cb == 0 && tid < CMB_HB && a.lse)
+  float M, L;
+  if (npiece <= 4)
+    cmb_small<4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
+  else if (npiece <= 16)
+    cmb_small<16>(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
+  else
+    cmb_large(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
+  if (cb0 == 0 && tid < CMB_HB && a.lse) {
+    // lanes 0..31 hold heads 0..31 (n32 = tid); M, L are per head
     a.lse[(size_t)b * NH + hb * CMB_HB + tid] = (M + log2f(L)) * kLn2;
+  }
 }
 
 constexpr int MAX_G = 256;   // split workgroups per call (one per compute unit)
@@ -1178,7 +1259,12 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   c.B = B;
   c.G = G;
   c.scale_log2 = a.scale_log2;
-  k_combine<<<dim3((NH / CMB_HB) * (DC / CMB_CB), B), CMB_THREADS, 0, st>>>(c);
+  // about G / B pieces per sequence: fewer pieces, more column blocks per
+  // workgroup (CPW * pieces loads in flight per lane)
+  int cpw = 1;
+  while (cpw < CMB_NCB && cpw * G < 8 * B) cpw *= 2;
+  c.cpw = cpw;
+  k_combine<<<dim3((NH / CMB_HB) * (CMB_NCB / cpw), B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();
 }
 
