@@ -87,6 +87,7 @@ struct PartialLayout {
   size_t flag_off; // int32 [slots][WAVES] the piece needs the fallback recompute
   size_t rec_off;  // WgRec [G] each workgroup's row range and first sequence
   size_t si_off;   // int4 [B] first range holding the sequence, ranges, valid length
+  size_t cnt_off;  // int32 [B + 1] charged sequence starts before b (scan kernel path)
   size_t bytes;
 };
 
@@ -111,41 +112,64 @@ __host__ __device__ inline PartialLayout partial_layout(int B, int G) {
   L.ml_off = L.o_off + align256(slots * NH * DC * sizeof(_Float16));
   L.rec_off = L.ml_off + align256(slots * NH * 2 * sizeof(float));
   L.si_off = L.rec_off + align256(sizeof(WgRec) * (size_t)G);
-  L.bytes = L.si_off + align256(sizeof(int4) * (size_t)B);
+  L.cnt_off = L.si_off + align256(sizeof(int4) * (size_t)B);
+  L.bytes = L.cnt_off + align256(sizeof(int32_t) * ((size_t)B + 1));
   return L;
 }
 
-// Ranges: workgroup g owns rows [floor(g total / G), floor((g + 1) total / G)).
-// Below 2^40 rows (G <= 1024) the quotients are formed in fp64: numerator
-// and divisor are exact, and the rounding error of the quotient (relative
-// 2^-53) is far below the distance 1 / divisor from the true quotient to the
-// next integer, so the floor is the exact integer quotient.
-constexpr int64_t FP64_EXACT_ROWS = (int64_t)1 << 40;
-
-__device__ __forceinline__ int64_t floor_div(int64_t n, int64_t d, bool fp64) {
-  return fp64 ? (int64_t)floor((double)n / (double)d) : n / d;
+// Ranges: workgroup g owns positions [floor(g n / G), floor((g + 1) n / G))
+// of a line of n positions.  All quantities are integers below 2^52, held
+// exactly in fp64; quotients come from a reciprocal and are corrected to the
+// exact floor by one comparison each way (the estimate is off by at most one).
+__device__ __forceinline__ double floor_q(double x, double d, double inv_d) {
+  double q = floor(x * inv_d);
+  if (q * d > x) q -= 1.0;
+  else if ((q + 1.0) * d <= x) q += 1.0;
+  return q;
 }
 
-__device__ __forceinline__ int64_t range_start(int g, int64_t total, int G) {
-  return floor_div((int64_t)g * total, G, total < FP64_EXACT_ROWS);
+struct Line {
+  double n, G, inv_n, inv_G;
+  int Gi;
+  __device__ Line(int64_t n_, int G_)
+      : n((double)n_), G((double)G_), inv_n(1.0 / (double)n_), inv_G(1.0 / (double)G_), Gi(G_) {}
+  __device__ int64_t start(int g) const { return (int64_t)floor_q((double)g * n, G, inv_G); }
+  // the range holding position p (0 <= p < n): the largest g with
+  // start(g) <= p, i.e. g n < (p + 1) G
+  __device__ int range_of(int64_t p) const {
+    const int g = (int)floor_q(((double)p + 1.0) * G - 1.0, n, inv_n);
+    return g < Gi - 1 ? g : Gi - 1;
+  }
+};
+
+// Cost-balanced ranges.  A workgroup pays a fixed setup for every piece it
+// processes (query load, pipeline fill, partial store: about SEG_ROWS rows
+// of loop time).  Under the plain even split of the rows, a sequence start
+// strictly inside a range adds a piece to that range; each such start is
+// charged SEG_ROWS virtual rows placed just before the sequence's first real
+// row, and the virtual line (rows plus charges) is split evenly instead.
+// Sequence b then spans [V_b - SEG_ROWS f_b, V_b + len_b) of the virtual
+// line, V_b = prefix[b] + SEG_ROWS c_b, with f_b its charge flag and c_b the
+// number of charged starts up to and including b.  When every sequence start
+// falls on a range boundary (equal lengths) nothing is charged and the split
+// is the plain one.
+constexpr int64_t SEG_ROWS = 224;
+
+// Whether the plain split of the rows puts the sequence start p0 strictly
+// inside a range.
+__device__ __forceinline__ bool interior_start(int64_t p0, const Line& rows) {
+  if (p0 <= 0) return false;
+  const double gs = floor_q((double)p0 * rows.G + rows.n - 1.0, rows.n, rows.inv_n);   // ceil(p0 G / n)
+  return !(gs < rows.G && rows.start((int)gs) == p0);
 }
 
-// Largest g in [0, G) with range_start(g) <= p (p < total).
-__device__ __forceinline__ int wg_of(int64_t p, int64_t total, int G) {
-  int g = (int)floor_div(p * (int64_t)G, total, total < FP64_EXACT_ROWS);
-  if (g > G - 1) g = G - 1;
-  while (g + 1 < G && range_start(g + 1, total, G) <= p) ++g;
-  while (g > 0 && range_start(g, total, G) > p) --g;
-  return g;
-}
-
-// What the combine needs of sequence b (rows [p0, p1) of the concatenated
-// valid lengths): the first range holding it, how many ranges it spans, and
-// its valid length (0: invalid, the result is NaN).
-__device__ __forceinline__ int4 seq_info(int64_t p0, int64_t p1, int64_t total, int G) {
-  if (p1 <= p0) return make_int4(0, 0, 0, 0);
-  const int lo = wg_of(p0, total, G);
-  return make_int4(lo, wg_of(p1 - 1, total, G) - lo + 1, (int)(p1 - p0), 0);
+// What the combine needs of a valid sequence whose real rows sit at virtual
+// [vb, vb + len): the first range holding it, how many ranges it spans, and
+// its length (0: invalid, the result is NaN).
+__device__ __forceinline__ int4 seq_info(int64_t vb, int64_t len, const Line& vline) {
+  if (len <= 0) return make_int4(0, 0, 0, 0);
+  const int lo = vline.range_of(vb);
+  return make_int4(lo, vline.range_of(vb + len - 1) - lo + 1, (int)len, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -157,26 +181,56 @@ constexpr int SCHED_LDS_B = 4096;   // prefix kept in LDS up to this many sequen
 
 // One workgroup of 1024 threads, four sequences per thread per chunk.
 // (1) Inclusive scan of the valid lengths (wave scans, then a scan of the 16
-// wave totals), written to prefix[] and, for B up to
-// SCHED_LDS_B, to LDS.  (2) One lane per range g: its bounds and, by binary
-// search over the prefix, the sequence holding its first row.  (3) One lane
-// per sequence: the first range holding it and how many ranges it spans.
+// wave totals), written to prefix[] and, for B up to SCHED_LDS_B, to LDS.
+// (2) The same scan of the charge flags of the sequence starts (exclusive
+// counts in cnt[]).  (3) One lane per range g: its virtual bounds, mapped to
+// rows through the sequence whose virtual span holds them (binary search).
+// (4) One lane per sequence: the first range holding it and how many ranges
+// it spans.
+__device__ __forceinline__ int64_t block_scan_1024(int64_t tsum, int64_t* wsum, int lane, int wave,
+                                                   int64_t& chunk_total) {
+  int64_t x = tsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int64_t w = lane < SCHED_THREADS / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < SCHED_THREADS / 64; o <<= 1) {
+      const int64_t y = __shfl_up(w, o, 64);
+      if (lane >= o) w += y;
+    }
+    if (lane < SCHED_THREADS / 64) wsum[lane] = w;   // inclusive over waves
+  }
+  __syncthreads();
+  const int64_t excl = (wave > 0 ? wsum[wave - 1] : 0) + x - tsum;
+  chunk_total = wsum[SCHED_THREADS / 64 - 1];
+  __syncthreads();   // wsum is reused by the next chunk
+  return excl;
+}
+
 __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ lens,
                                                          int64_t* __restrict__ prefix,
+                                                         int32_t* __restrict__ cnt,
                                                          WgRec* __restrict__ rec,
                                                          int4* __restrict__ seqinfo, int32_t* err_flag) {
   __shared__ int64_t wsum[SCHED_THREADS / 64];
-  __shared__ int64_t carry;
   __shared__ int64_t s_pre[SCHED_LDS_B + 1];
+  __shared__ int32_t s_cnt[SCHED_LDS_B + 1];
   const bool in_lds = B <= SCHED_LDS_B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
-    carry = 0;
     prefix[0] = 0;
     s_pre[0] = 0;
+    cnt[0] = 0;
+    s_cnt[0] = 0;
   }
-  __syncthreads();
+  int64_t carry = 0;
   for (int base = 0; base < B; base += SCHED_THREADS * SCHED_PER) {
     int64_t v[SCHED_PER];
     int64_t tsum = 0;
@@ -194,26 +248,8 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
       }
       tsum += v[j];
     }
-    // inclusive scan of tsum over the wave
-    int64_t x = tsum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-      int64_t w = lane < SCHED_THREADS / 64 ? wsum[lane] : 0;
-#pragma unroll
-      for (int o = 1; o < SCHED_THREADS / 64; o <<= 1) {
-        const int64_t y = __shfl_up(w, o, 64);
-        if (lane >= o) w += y;
-      }
-      if (lane < SCHED_THREADS / 64) wsum[lane] = w;   // inclusive over waves
-    }
-    __syncthreads();
-    int64_t run = carry + (wave > 0 ? wsum[wave - 1] : 0) + x - tsum;   // exclusive
+    int64_t ct;
+    int64_t run = carry + block_scan_1024(tsum, wsum, lane, wave, ct);
 #pragma unroll
     for (int j = 0; j < SCHED_PER; ++j) {
       const int b = base + SCHED_PER * tid + j;
@@ -223,9 +259,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
         if (in_lds) s_pre[b + 1] = run;
       }
     }
-    __syncthreads();
-    if (tid == 0) carry += wsum[SCHED_THREADS / 64 - 1];
-    __syncthreads();
+    carry += ct;
   }
   const int64_t total = carry;
   if (total <= 0) {   // no valid sequence: the combine writes NaN everywhere
@@ -236,10 +270,55 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     for (int b = tid; b < B; b += SCHED_THREADS) seqinfo[b] = make_int4(0, 0, 0, 0);
     return;
   }
+  __syncthreads();   // prefix[] written by every lane
   auto pre = [&](int i) -> int64_t { return in_lds ? s_pre[i] : prefix[i]; };
+  const Line rows_line(total, G);
+  // charged starts: exclusive counts cnt[b], cnt[B] = all of them
+  int64_t fcarry = 0;
+  for (int base = 0; base < B; base += SCHED_THREADS * SCHED_PER) {
+    int f[SCHED_PER];
+    int64_t fsum = 0;
+#pragma unroll
+    for (int j = 0; j < SCHED_PER; ++j) {
+      const int b = base + SCHED_PER * tid + j;
+      f[j] = b < B && pre(b + 1) > pre(b) && interior_start(pre(b), rows_line) ? 1 : 0;
+      fsum += f[j];
+    }
+    int64_t ct;
+    int64_t run = fcarry + block_scan_1024(fsum, wsum, lane, wave, ct);
+#pragma unroll
+    for (int j = 0; j < SCHED_PER; ++j) {
+      const int b = base + SCHED_PER * tid + j;
+      run += f[j];
+      if (b < B) {
+        cnt[b + 1] = (int32_t)run;   // charged starts among 0 .. b
+        if (in_lds) s_cnt[b + 1] = (int32_t)run;
+      }
+    }
+    fcarry += ct;
+  }
+  __syncthreads();
+  auto cnt_of = [&](int i) -> int64_t { return in_lds ? s_cnt[i] : cnt[i]; };
+  const int64_t tv = total + SEG_ROWS * fcarry;
+  const Line vline(tv, G);
+  // virtual span of sequence b starts at prefix[b] + SEG_ROWS cnt[b] (the
+  // charge, if any, comes first); its rows start at V_b = prefix[b] + SEG_ROWS cnt[b + 1]
+  auto span_start = [&](int b) -> int64_t { return pre(b) + SEG_ROWS * cnt_of(b); };
+  auto to_row = [&](int64_t vpos) -> int64_t {
+    if (vpos >= tv) return total;
+    int lo = 0, hi = B - 1;   // largest b with span_start(b) <= vpos: a valid sequence
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (span_start(mid) <= vpos) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t vb = pre(lo) + SEG_ROWS * cnt_of(lo + 1);
+    return pre(lo) + (vpos > vb ? vpos - vb : 0);
+  };
   for (int g = tid; g < G; g += SCHED_THREADS) {
-    const int64_t start = range_start(g, total, G);
-    // largest b with prefix[b] <= start; start < total, so prefix[b + 1] > start
+    const int64_t start = to_row(vline.start(g));
+    // the sequence holding row start (start < total: a charge is always
+    // followed by its sequence's rows)
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -248,7 +327,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     }
     WgRec r;
     r.start = start;
-    r.end = range_start(g + 1, total, G);
+    r.end = to_row(vline.start(g + 1));
     r.seq_begin = pre(lo);
     r.seq_end = pre(lo + 1);
     r.b = lo;
@@ -256,9 +335,8 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     r.pad[0] = r.pad[1] = 0;
     rec[g] = r;
   }
-  for (int b = tid; b < B; b += SCHED_THREADS) {
-    seqinfo[b] = seq_info(pre(b), pre(b + 1), total, G);
-  }
+  for (int b = tid; b < B; b += SCHED_THREADS)
+    seqinfo[b] = seq_info(pre(b) + SEG_ROWS * cnt_of(b + 1), pre(b + 1) - pre(b), vline);
 }
 
 // ---------------------------------------------------------------------------
@@ -389,7 +467,10 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ int64_t s_pre[SCAN ? SPL_MAXB + 1 : 1];
   __shared__ int32_t s_off[SCAN ? SPL_MAXB : 1];
   __shared__ int64_t s_wsum[WAVES];
+  __shared__ int32_t s_fsum[WAVES];
+  __shared__ int16_t s_c[SCAN ? SPL_MAXB + 1 : 1];   // charge flags, then counts
   __shared__ int32_t s_first;
+  __shared__ int64_t s_rows[2];   // this workgroup's first row, end row
 
   // Range index of this workgroup.  Workgroups are dealt to the 8 XCDs
   // round-robin (block i runs on XCD i % 8); giving each XCD a contiguous
@@ -408,23 +489,24 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // sequences per lane, a wave scan, then the four wave totals.
     const int tid = threadIdx.x;
     const int B = a.B, G = a.G;
+    // all loads first (indices clamped), so they share one round trip
+    int lenj[SPL_PER], offj[SPL_PER + 1];
+#pragma unroll
+    for (int j = 0; j < SPL_PER; ++j) lenj[j] = a.lens[min(tid * SPL_PER + j, B - 1)];
+#pragma unroll
+    for (int j = 0; j <= SPL_PER; ++j) offj[j] = a.offsets[min(tid * SPL_PER + j, B)];   // B + 1 entries
     int64_t v[SPL_PER];
     int64_t tsum = 0;
     int bad = 0;
 #pragma unroll
     for (int j = 0; j < SPL_PER; ++j) {
       const int bb = tid * SPL_PER + j;
-      v[j] = 0;
-      if (bb < B) {
-        const int len = a.lens[bb];
-        const int o0 = a.offsets[bb];
-        const int cap = a.offsets[bb + 1] - o0;
-        if (len >= 1 && len <= cap)
-          v[j] = len;
-        else
-          bad = 1;
-        s_off[bb] = o0;
-      }
+      const int cap = offj[j + 1] - offj[j];
+      const bool in = bb < B;
+      const bool ok = lenj[j] >= 1 && lenj[j] <= cap;
+      v[j] = in && ok ? lenj[j] : 0;
+      bad |= in && !ok ? 1 : 0;
+      if (in) s_off[bb] = offj[j];
       tsum += v[j];
     }
     int64_t x = tsum;
@@ -437,6 +519,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     if (tid == 0) {
       s_pre[0] = 0;
       s_first = 0;
+      s_rows[0] = 0;
+      s_rows[1] = -1;   // set below: the end row, or the total when the end is the line's end
     }
     __syncthreads();
     int64_t total = 0, run = x - tsum;
@@ -445,22 +529,94 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       total += s_wsum[w];
       if (w < wave) run += s_wsum[w];
     }
-    start = total > 0 ? range_start(g, total, G) : 0;
-    end = total > 0 ? range_start(g + 1, total, G) : 0;
 #pragma unroll
     for (int j = 0; j < SPL_PER; ++j) {
       const int bb = tid * SPL_PER + j;
-      if (bb < B) {
-        s_pre[bb + 1] = run + v[j];
-        if (v[j] > 0 && run <= start && start < run + v[j]) s_first = bb;   // one writer
-      }
       run += v[j];
+      if (bb < B) s_pre[bb + 1] = run;
+    }
+    __syncthreads();
+    // Charged sequence starts (see SEG_ROWS).  The per-sequence work below
+    // takes sequence tid + THREADS k on lane tid, so that a small batch
+    // spreads over many lanes; the scans take SPL_PER consecutive sequences
+    // per lane.  s_c[b + 1] first holds the flag of sequence b, then the
+    // number of charged starts among 0 .. b.
+    {
+      const Line rows_line(total > 0 ? total : 1, G);
+#pragma unroll
+      for (int k = 0; k < SPL_PER; ++k) {
+        const int bb = tid + THREADS * k;
+        if (bb < B)
+          s_c[bb + 1] = (int16_t)(s_pre[bb + 1] > s_pre[bb] && interior_start(s_pre[bb], rows_line) ? 1 : 0);
+      }
+    }
+    __syncthreads();
+    int f[SPL_PER];
+    int fsum = 0;
+#pragma unroll
+    for (int j = 0; j < SPL_PER; ++j) {
+      const int bb = tid * SPL_PER + j;
+      f[j] = bb < B ? s_c[bb + 1] : 0;
+      fsum += f[j];
+    }
+    int fx = fsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(fx, o, 64);
+      if (lane_id >= o) fx += y;
+    }
+    if (lane_id == 63) s_fsum[wave] = fx;
+    __syncthreads();
+    int nchg = 0, c = fx - fsum;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      nchg += s_fsum[w];
+      if (w < wave) c += s_fsum[w];
+    }
+#pragma unroll
+    for (int j = 0; j < SPL_PER; ++j) {
+      const int bb = tid * SPL_PER + j;
+      c += f[j];
+      if (bb < B) s_c[bb + 1] = (int16_t)c;
+    }
+    if (tid == 0) s_c[0] = 0;
+    const int64_t tv = total + SEG_ROWS * nchg;   // the virtual line
+    const Line vline(tv > 0 ? tv : 1, G);
+    const int64_t vs = total > 0 ? vline.start(g) : 0;
+    const int64_t ve = total > 0 ? vline.start(g + 1) : 0;
+    __syncthreads();
+    // each lane maps the virtual bounds through its sequences, whose spans
+    // [V - SEG_ROWS f, V + len) tile the virtual line
+    int4 sinfo[SPL_PER];
+#pragma unroll
+    for (int k = 0; k < SPL_PER; ++k) {
+      const int bb = tid + THREADS * k;
+      if (bb < B) {
+        const int64_t p0 = s_pre[bb], len = s_pre[bb + 1] - p0;
+        const int cb = s_c[bb + 1], fb = cb - s_c[bb];
+        const int64_t vb = p0 + SEG_ROWS * cb;
+        if (len > 0) {
+          const int64_t lo = vb - SEG_ROWS * fb, hi = vb + len;
+          if (lo <= vs && vs < hi) {   // one writer each
+            s_first = bb;
+            s_rows[0] = p0 + (vs > vb ? vs - vb : 0);
+          }
+          if (lo <= ve && ve < hi) s_rows[1] = p0 + (ve > vb ? ve - vb : 0);
+        }
+        if (bb % G == g) sinfo[k] = seq_info(vb, len, vline);   // one workgroup per sequence
+      }
     }
     bad = __syncthreads_or(bad);
     if (g == 0 && tid == 0 && bad && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_LENS);
-    // what the combine needs of sequences g, g + G, g + 2G, ...
-    for (int bb = g + tid * G; bb < B; bb += THREADS * G)
-      a.seqinfo[bb] = seq_info(s_pre[bb], s_pre[bb + 1], total, G);
+    // what the combine needs of each sequence (written by one workgroup;
+    // stored after the barrier, which would otherwise wait for the stores)
+#pragma unroll
+    for (int k = 0; k < SPL_PER; ++k) {
+      const int bb = tid + THREADS * k;
+      if (bb < B && bb % G == g) a.seqinfo[bb] = sinfo[k];
+    }
+    start = s_rows[0];
+    end = ve >= tv ? total : s_rows[1];   // ve == tv lies in no span
     if (total <= 0) return;   // no valid sequence: the combine writes NaN
     start = uniform_i64(start);
     end = uniform_i64(end);
@@ -1238,7 +1394,8 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   if (B <= SPL_MAXB) {
     k_split<true><<<G, THREADS, 0, st>>>(a);
   } else {
-    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, rec, seqinfo, err_flag);
+    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
+                                         err_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_split<false><<<G, THREADS, 0, st>>>(a);
