@@ -916,6 +916,18 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
       bf16x8 P[2];
       floatx16 S_next;
+      // PV A-fragments of tile it, PV_PF pairs ahead of their MFMAs.  The
+      // first pairs are read during the last QK steps (tile it is resident
+      // throughout), so PV starts without waiting on transpose reads.
+      uint32_t tr_base[2][2];
+      bf16x4 pa[PV_PF][2];
+      auto pv_pair = [&](int j) {
+        const int kk2 = j / (DC / 32), cb = j % (DC / 32);
+        const MLA_LDS char* p0 = T + tr_base[0][cb & 1] + kk2 * 16 * ROWB + cb * 64;
+        const MLA_LDS char* p1 = T + tr_base[1][cb & 1] + kk2 * 16 * ROWB + cb * 64;
+        pa[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
+        pa[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
+      };
       // (The empty asm statements pin the softmax inside each branch: the
       // compiler would otherwise hoist the common code above the branch, out
       // of reach of the QK MFMAs it is meant to overlap.)
@@ -923,6 +935,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // Tile it+1 landed (only tile it+2 was issued after it); the barrier
         // also means every wave is past PV(it-1), so that tile's stage may be
         // refilled below.
+        uint32_t qk_off[4];
+        make_qk_off(qk_off);   // lane arithmetic only: ahead of the wait
         wait_vm_then_barrier<(NSTAGE - 3) * DMA_PER_WAVE>();
         floatx16 Sc = S_cur;
         asm volatile("" : "+v"(Sc));
@@ -931,8 +945,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // scheduling barriers keep every step where it is written, so the
         // fragment prefetch and the VALU placement stay as planned.
         const MLA_LDS char* Tn = (const MLA_LDS char*)lds + ((it + 1) % NSTAGE) * TILEB;
-        uint32_t qk_off[4];
-        make_qk_off(qk_off);
         bf16x8 kf[QK_PF];
 #pragma unroll
         for (int j = 0; j < QK_PF; ++j)
@@ -963,6 +975,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
             P[j >> 2][2 * (j & 3) + 1] = (__bf16)e[2 * j + 1];
           }
           if (kk >= 26 && kk < 34) sm_sum(P, kk - 26);
+          if (kk == KSTEPS - PV_PF - 2) make_tr_base(tr_base);
+          if (kk >= KSTEPS - PV_PF - 1 && kk < KSTEPS - 1) pv_pair(kk - (KSTEPS - PV_PF - 1));
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_drain(S_next);
@@ -972,20 +986,11 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         floatx16 Sc = S_cur;
         asm volatile("" : "+v"(Sc));
         softmax(Sc, nvalid, P);
+        make_tr_base(tr_base);
+#pragma unroll
+        for (int j = 0; j < PV_PF; ++j) pv_pair(j);
       }
 
-      // ---- PV fragments for the first column blocks ----
-      uint32_t tr_base[2][2];
-      make_tr_base(tr_base);
-      bf16x4 pa[PV_PF][2];
-#pragma unroll
-      for (int j = 0; j < PV_PF; ++j) {
-        const int kk2 = j / (DC / 32), cb = j % (DC / 32);
-        const MLA_LDS char* p0 = T + tr_base[0][cb & 1] + kk2 * 16 * ROWB + cb * 64;
-        const MLA_LDS char* p1 = T + tr_base[1][cb & 1] + kk2 * 16 * ROWB + cb * 64;
-        pa[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p0);
-        pa[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
-      }
 
       // ---- O^T += C^T . P^T over 2 row halves x 16 column blocks ----
       // Tile it+3 goes into the stage of tile it-1; its nine DMA instructions
