@@ -23,14 +23,31 @@ constexpr int NH = 128, DH = 128, DC = 512, DR = 64, DV = 128;
 constexpr int QW = DH + DR;   // per-head width of the given query [q^C | q^R]
 
 // ---------------------------------------------------------------------------
-// absorb: one workgroup per (head, half of the 512 latent columns).
+// absorb: one workgroup per (head, quarter of the 512 latent columns).
 //   q_lat^T[cols x batch] = W_UK[h]^T[cols x k] . q_C^T[k x batch]   (32x32x16)
-// LDS holds W_UK[h][0:128][256 columns] with rows padded to 544 bytes so the
-// 4-row x 32-byte transpose reads of a 16-lane group fall in distinct banks.
+// LDS holds W_UK[h][0:128][128 columns] with rows padded to 288 bytes so the
+// 4-row x 32-byte transpose reads of a 16-lane group fall in distinct banks;
+// wave w owns column block w of the quarter.  The weight and query loads are
+// issued first and the workgroup's share of the RoPE (pairs 8 qt .. 8 qt + 7 of
+// this head, every batch row) is computed while they are in flight.
 // ---------------------------------------------------------------------------
-constexpr int ABS_COLS = 256;
-constexpr int ABS_ROWB = ABS_COLS * 2 + 32;   // 544
+constexpr int ABS_COLS = 128;
+constexpr int ABS_ROWB = ABS_COLS * 2 + 32;   // 288
 constexpr int ABS_THREADS = 256;
+constexpr int ABS_WPT = DH * ABS_COLS / 8 / ABS_THREADS;   // 16-byte weight pieces per thread
+
+// cos and sin of pos * base^(-2i/d_r): the angle is formed in double and
+// reduced modulo 2 pi in double (2 pi as a sum of two doubles), and the
+// reduced angle, at most pi in magnitude, goes to single-precision sincos.
+__device__ __forceinline__ void rope_cs_reduced(int64_t pos, int i, int d_r, double log2_base, float* c,
+                                                float* s) {
+  const double theta = exp2(-2.0 * (double)i / (double)d_r * log2_base);
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0.15915494309189535);   // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, ang);
+  r = fma(-k, 2.4492935982947064e-16, r);
+  sincosf((float)r, s, c);
+}
 
 // q is bf16, or fp32 (QF32: the query computed from the hidden state), which
 // enters the bf16 product as hi + lo (two MFMAs per step).
@@ -42,33 +59,23 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
                                                            __bf16* __restrict__ q_lat,
                                                            __bf16* __restrict__ q_pe) {
   __shared__ __attribute__((aligned(16))) char w[DH * ABS_ROWB];
-  const int h = blockIdx.x, half = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = blockIdx.x, qt = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g32 = lane >> 5;
 
-  // Stage W_UK[h][:, 256 half .. +256] (128 rows x 32 chunks of 16 B).
-  const __bf16* src = W_UK + (size_t)h * DH * DC + half * ABS_COLS;
+  // W_UK[h][:, 128 qt .. +128]: 128 rows x 16 pieces of 16 B, into registers
+  const __bf16* src = W_UK + (size_t)h * DH * DC + qt * ABS_COLS;
+  floatx4 wv[ABS_WPT];
 #pragma unroll
-  for (int j = 0; j < DH * (ABS_COLS / 8) / ABS_THREADS; ++j) {
-    const int idx = j * ABS_THREADS + tid;
-    const int r = idx >> 5, c = idx & 31;
-    const floatx4 v = *(const floatx4*)(src + (size_t)r * DC + c * 8);
-    *(floatx4*)(w + r * ABS_ROWB + c * 16) = v;
+  for (int j = 0; j < ABS_WPT; ++j) {
+    const int idx = j * ABS_THREADS + tid, r = idx >> 4, c = idx & 15;
+    wv[j] = *(const floatx4*)(src + (size_t)r * DC + c * 8);
   }
-  __syncthreads();
 
-  // Transpose-read addressing (see the decode kernel): in 16-lane group G,
-  // lane i reads 8 bytes of row r0 + i/4 at columns c0 + 4 (i & 3); lane j of
-  // the group then holds column c0 + j for rows r0 .. r0+3.
-  const int G = lane >> 4, i16 = lane & 15, g32 = lane >> 5;
-  const int h16 = G & 1;
-  const uint32_t tr_off = (uint32_t)((i16 >> 2) * ABS_ROWB + 32 * h16 + 8 * (i16 & 3));
-
-  // Each wave owns two 32-column blocks; loop over 32-wide batch blocks.
-  for (int nb = 0; nb * 32 < B; ++nb) {
+  // B operand: q_C[bq][h][16 ks + 8 g32 .. +8] (and its low part)
+  bf16x8 qb[DH / 16], ql[QF32 ? DH / 16 : 1];
+  auto load_q = [&](int nb) {
     const int bq = nb * 32 + (lane & 31);
     const bool bok = bq < B;
-    // B operand: q_C[bq][h][16 ks + 8 g32 .. +8] (and its low part)
-    bf16x8 qb[DH / 16], ql[QF32 ? DH / 16 : 1];
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
       const size_t e0 = ((size_t)(bok ? bq : 0) * NH + h) * QW + 16 * ks + 8 * g32;
@@ -85,41 +92,14 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
         qb[ks] = bok ? *(const bf16x8*)((const __bf16*)qv + e0) : bf16x8{};
       }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int cb = wave * 2 + t;   // column block within this half
-      floatx16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        const char* p = w + (16 * ks + 8 * g32) * ABS_ROWB + 64 * cb + tr_off;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)p);
-        const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
-        if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], acc, 0, 0, 0);
-      }
-      // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
-      if (bok) {
-        __bf16* dst = q_lat + ((size_t)bq * NH + h) * DC + half * ABS_COLS + 32 * cb + 4 * g32;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const bf16x4 v = {(__bf16)acc[4 * q4 + 0], (__bf16)acc[4 * q4 + 1],
-                            (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
-          *(bf16x4*)(dst + 8 * q4) = v;
-        }
-      }
-    }
-  }
+  };
+  load_q(0);
 
-  // RoPE on the decoupled part (first half only): q_pe = rotate(q^R, pos[b]).
-  if (half == 0) {
-    for (int idx = tid; idx < B * (DR / 2); idx += ABS_THREADS) {
-      const int b = idx / (DR / 2), i = idx % (DR / 2);
-      float cs, sn;
-      rope_cos_sin(pos[b], i, DR, rope_base, &cs, &sn);
+  // RoPE on the decoupled part: q_pe = rotate(q^R, pos[b]), pairs 8 qt .. +8.
+  {
+    const double log2_base = log2(rope_base);
+    for (int idx = tid; idx < B * 8; idx += ABS_THREADS) {
+      const int b = idx >> 3, i = 8 * qt + (idx & 7);
       const size_t e0 = ((size_t)b * NH + h) * QW + DH;
       float lo, hi;
       if constexpr (QF32) {
@@ -129,9 +109,53 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
         lo = (float)((const __bf16*)qv)[e0 + i];
         hi = (float)((const __bf16*)qv)[e0 + DR / 2 + i];
       }
+      float cs, sn;
+      rope_cs_reduced(pos[b], i, DR, log2_base, &cs, &sn);
       __bf16* out = q_pe + ((size_t)b * NH + h) * DR;
       out[i] = (__bf16)(lo * cs - hi * sn);
       out[DR / 2 + i] = (__bf16)(hi * cs + lo * sn);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < ABS_WPT; ++j) {
+    const int idx = j * ABS_THREADS + tid, r = idx >> 4, c = idx & 15;
+    *(floatx4*)(w + r * ABS_ROWB + c * 16) = wv[j];
+  }
+  __syncthreads();
+
+  // Transpose-read addressing (see the decode kernel): in 16-lane group G,
+  // lane i reads 8 bytes of row r0 + i/4 at columns c0 + 4 (i & 3); lane j of
+  // the group then holds column c0 + j for rows r0 .. r0+3.
+  const int G = lane >> 4, i16 = lane & 15;
+  const int h16 = G & 1;
+  const uint32_t tr_off = (uint32_t)((i16 >> 2) * ABS_ROWB + 32 * h16 + 8 * (i16 & 3));
+
+  for (int nb = 0; nb * 32 < B; ++nb) {
+    if (nb > 0) load_q(nb);
+    const int bq = nb * 32 + (lane & 31);
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      const char* p = w + (16 * ks + 8 * g32) * ABS_ROWB + 64 * wave + tr_off;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)p);
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
+      if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], acc, 0, 0, 0);
+    }
+    // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
+    if (bq < B) {
+      __bf16* dst = q_lat + ((size_t)bq * NH + h) * DC + qt * ABS_COLS + 32 * wave + 4 * g32;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const bf16x4 v = {(__bf16)acc[4 * q4 + 0], (__bf16)acc[4 * q4 + 1],
+                          (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
+        *(bf16x4*)(dst + 8 * q4) = v;
+      }
     }
   }
 }
