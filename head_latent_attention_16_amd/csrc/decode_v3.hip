@@ -1207,31 +1207,45 @@ __device__ __forceinline__ void cmb_store(const CombineArgs& a, float (*s_out)[C
 }
 
 // Up to NP pieces: the (m, l) of all pieces and the entries of the first
-// column block are loaded together, the weights are kept in registers.
+// column block are loaded together (cmb_small_load, issued before the
+// fallback flags are examined, so both share one round trip), the weights
+// are kept in registers (cmb_small_finish).
 template <int NP>
-__device__ __forceinline__ void cmb_small(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb,
-                                          int cb0, int cpw, int npiece, size_t slot0, float& M, float& L) {
+struct SmallLoad {
+  float2 m2[NP];
+  halfx4 v[NP];
+};
+
+template <int NP>
+__device__ __forceinline__ void cmb_small_load(const CombineArgs& a, int hb, int cb0, int npiece,
+                                               size_t slot0, SmallLoad<NP>& d) {
   const int tid = threadIdx.x, n32 = tid & 31;
   const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
   const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * (CMB_HB * CMB_CB) + 4 * tid;
-  float2 m2[NP];
-  float w[NP];
-  halfx4 v[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int k = i < npiece ? i : npiece - 1;   // clamped; weight 0 below
-    m2[i] = ml[(size_t)k * NH];
-    v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)cb0 * (CMB_HB * CMB_CB));
+    d.m2[i] = ml[(size_t)k * NH];
+    d.v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)cb0 * (CMB_HB * CMB_CB));
   }
+}
+
+template <int NP>
+__device__ __forceinline__ void cmb_small_finish(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b,
+                                                 int hb, int cb0, int cpw, int npiece, size_t slot0,
+                                                 SmallLoad<NP>& d, float& M, float& L) {
+  const int tid = threadIdx.x;
+  const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * (CMB_HB * CMB_CB) + 4 * tid;
+  float w[NP];
   M = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    if (i < npiece) M = fmaxf(M, m2[i].x);
+    if (i < npiece) M = fmaxf(M, d.m2[i].x);
   L = 0.f;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const bool use = i < npiece && m2[i].x != -INFINITY;
-    w[i] = use ? exp2f(m2[i].x - M) * m2[i].y : 0.f;   // 2^(m - M) l
+    const bool use = i < npiece && d.m2[i].x != -INFINITY;
+    w[i] = use ? exp2f(d.m2[i].x - M) * d.m2[i].y : 0.f;   // 2^(m - M) l
     L += w[i];
   }
   const float inv = 1.f / L;
@@ -1240,16 +1254,16 @@ __device__ __forceinline__ void cmb_small(const CombineArgs& a, float (*s_out)[C
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int k = i < npiece ? i : npiece - 1;
-        v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)(cb0 + c) * (CMB_HB * CMB_CB));
+        d.v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)(cb0 + c) * (CMB_HB * CMB_CB));
       }
     }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      acc.x += w[i] * (float)v[i][0];
-      acc.y += w[i] * (float)v[i][1];
-      acc.z += w[i] * (float)v[i][2];
-      acc.w += w[i] * (float)v[i][3];
+      acc.x += w[i] * (float)d.v[i][0];
+      acc.y += w[i] * (float)d.v[i][1];
+      acc.z += w[i] * (float)d.v[i][2];
+      acc.w += w[i] * (float)d.v[i][3];
     }
     cmb_store(a, s_out, b, hb, cb0 + c, acc, inv);
   }
@@ -1327,20 +1341,27 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
   int flag = 0;
   for (int k = tid; k < npiece * WAVES; k += CMB_THREADS) flag |= a.flags[slot0 * WAVES + k];
-  if (__syncthreads_or(flag)) {
-    // a piece overflowed: the blocks of this head block share its heads out
-    // and recompute whole rows each
+  // a piece overflowed: the blocks of this head block share its heads out
+  // and recompute whole rows each
+  auto fallback = [&]() {
     for (int k = blockIdx.x % ngrp; k < CMB_HB; k += ngrp) recompute_head(a, b, hb * CMB_HB + k, si.z);
-    return;
-  }
-  if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
+  };
   float M, L;
-  if (npiece <= 4)
-    cmb_small<4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
-  else if (npiece <= 16)
-    cmb_small<16>(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
-  else
+  if (npiece <= 4) {
+    SmallLoad<4> d;
+    cmb_small_load<4>(a, hb, cb0, npiece, slot0, d);
+    if (__syncthreads_or(flag)) return fallback();
+    if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
+    cmb_small_finish<4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, d, M, L);
+  } else if (npiece <= 16) {
+    SmallLoad<16> d;
+    cmb_small_load<16>(a, hb, cb0, npiece, slot0, d);
+    if (__syncthreads_or(flag)) return fallback();
+    cmb_small_finish<16>(a, s_out, b, hb, cb0, cpw, npiece, slot0, d, M, L);
+  } else {
+    if (__syncthreads_or(flag)) return fallback();
     cmb_large(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
+  }
   if (cb0 == 0 && tid < CMB_HB && a.lse) {
     // lanes 0..31 hold heads 0..31 (n32 = tid); M, L are per head
     a.lse[(size_t)b * NH + hb * CMB_HB + tid] = (M + log2f(L)) * kLn2;
