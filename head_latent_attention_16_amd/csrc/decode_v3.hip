@@ -484,7 +484,76 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   // This workgroup's rows [start, end) and the sequence b holding row start.
   int64_t start, end, seq_begin0, seq_end0;
   int b0, off0;
-  if constexpr (SCAN) {
+  if (SCAN && a.B <= 64) {
+    // Up to 64 sequences: wave 0 does all of it, one sequence per lane, with
+    // wave-level scans and no workgroup barrier until the results are in LDS.
+    const int B = a.B, G = a.G;
+    int bad = 0;
+    int4 sinfo = make_int4(0, 0, 0, 0);
+    bool own_info = false;
+    if (wave == 0) {
+      const int l = lane_id;
+      const bool in = l < B;
+      const int len = a.lens[min(l, B - 1)];
+      const int o0 = a.offsets[min(l, B)], o1 = a.offsets[min(l + 1, B)];
+      const bool ok = len >= 1 && len <= o1 - o0;
+      const int64_t v = in && ok ? len : 0;
+      bad = in && !ok ? 1 : 0;
+      int64_t x = v;   // inclusive prefix of the valid lengths
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, 64);
+        if (l >= o) x += y;
+      }
+      const int64_t total = __shfl(x, 63, 64);
+      const int64_t p0 = x - v;   // first row of sequence l
+      if (in) {
+        s_off[l] = o0;
+        s_pre[l + 1] = x;
+      }
+      if (l == 0) s_pre[0] = 0;
+      const Line rows_line(total > 0 ? total : 1, G);
+      const int f = v > 0 && interior_start(p0, rows_line) ? 1 : 0;
+      int c = f;   // charged starts up to and including l
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(c, o, 64);
+        if (l >= o) c += y;
+      }
+      const int nchg = __shfl(c, 63, 64);
+      const int64_t tv = total + SEG_ROWS * nchg;   // the virtual line
+      const Line vline(tv > 0 ? tv : 1, G);
+      const int64_t vs = total > 0 ? vline.start(g) : 0;
+      const int64_t ve = total > 0 ? vline.start(g + 1) : 0;
+      const int64_t vb = p0 + SEG_ROWS * c;
+      const int64_t lo = vb - SEG_ROWS * f, hi = vb + v;
+      const bool hs = v > 0 && lo <= vs && vs < hi;   // at most one lane each
+      const bool he = v > 0 && lo <= ve && ve < hi;
+      if (l == 0) {
+        s_first = 0;
+        s_rows[0] = 0;
+        s_rows[1] = ve >= tv ? total : -1;   // ve == tv lies in no span
+        s_wsum[0] = total;
+      }
+      if (hs) {
+        s_first = l;
+        s_rows[0] = p0 + (vs > vb ? vs - vb : 0);
+      }
+      if (he && ve < tv) s_rows[1] = p0 + (ve > vb ? ve - vb : 0);
+      own_info = in && l % G == g;   // one workgroup per sequence
+      if (own_info) sinfo = seq_info(vb, v, vline);
+    }
+    bad = __syncthreads_or(bad);
+    if (g == 0 && threadIdx.x == 0 && bad && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_LENS);
+    if (own_info) a.seqinfo[lane_id] = sinfo;
+    if (s_wsum[0] <= 0) return;   // no valid sequence: the combine writes NaN
+    start = uniform_i64(s_rows[0]);
+    end = uniform_i64(s_rows[1]);
+    b0 = uniform_i32(s_first);
+    seq_begin0 = uniform_i64(s_pre[b0]);
+    seq_end0 = uniform_i64(s_pre[b0 + 1]);
+    off0 = uniform_i32(s_off[b0]);
+  } else if constexpr (SCAN) {
     // Every workgroup scans the (at most SPL_MAXB) lengths itself: four
     // sequences per lane, a wave scan, then the four wave totals.
     const int tid = threadIdx.x;

@@ -90,6 +90,24 @@ def test_absorb_query_v3():
         assert np.max(np.abs(host_f64(r["q_pe"][b]) - pe)) <= 2.0 ** -7 * np.max(np.abs(pe))
 
 
+def test_absorb_query_large_positions():
+    """Query RoPE at positions up to 2^31 - 1 (angles up to about 2e9 rad,
+    reduced modulo 2 pi in double before the single-precision sine and cosine):
+    q_pe within one bf16 rounding of the fp64 rotation; q_lat unaffected."""
+    w = small_v3([5, 9, 17, 33])
+    u = Uploaded(w)
+    pos = np.array([131072, 1048577, 123456789, 2 ** 31 - 1], np.int32)
+    q_lat = torch.empty(w.B, 128, 512, dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(w.B, 128, 64, dtype=torch.bfloat16, device="cuda")
+    L.absorb_q(u.dims, q_lat, q_pe, u.W["W_UK"], dev(pos), q=u.q)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        pe = O.rope(w.f64(w.q_R[b]), int(pos[b]))
+        assert np.max(np.abs(host_f64(q_pe[b]) - pe)) <= 2.0 ** -7 * np.max(np.abs(pe)), (b, int(pos[b]))
+        want = O.absorb_query(w.f64(w.q_C[b]), w.f64(w.W["W_UK"]))
+        assert np.max(np.abs(host_f64(q_lat[b]) - want)) <= 2.0 ** -7 * np.max(np.abs(want))
+
+
 def _decode_only(w, q_lat_bits, q_pe_bits, hint=None):
     u = Uploaded(w)
     d = u.dims
