@@ -242,6 +242,25 @@ def test_dominant_row_and_fallback():
     assert np.allclose(got[0], w.f64(w.seq_rows(0))[600, :512][None], atol=1e-5)
 
 
+def test_partial_outside_fp16_range_falls_back():
+    """A piece whose normalised partial exceeds the fp16 range (one row of
+    3e7 among N(0,1) rows, zero query so every weight is 1) is flagged and the
+    sequence recomputed: the result is the exact mean of its rows."""
+    w = small_v3([3000, 500])
+    o0 = int(w.offsets[0])
+    w.cache[o0 + 1500, :512] = I.bf16_bits(np.full(512, 3.0e7, np.float32))
+    q_lat = I.bf16_bits(np.zeros((2, 128, 512), np.float32))
+    q_pe = I.bf16_bits(np.zeros((2, 128, 64), np.float32))
+    got, glse, err = _decode_only(w, q_lat, q_pe)
+    assert err == 0
+    for b in range(2):
+        rows = w.f64(w.seq_rows(b))[:, :512]
+        mean = rows.mean(axis=0)
+        assert np.all(np.isfinite(got[b])), b
+        assert np.max(np.abs(got[b] - mean[None])) <= 1e-5 * np.max(np.abs(mean)) + 1e-4, b
+        assert np.max(np.abs(glse[b] - math.log(rows.shape[0]))) < 1e-4, b
+
+
 def test_invalid_lengths_flagged():
     w = small_v3([40, 50, 60])
     u = Uploaded(w)
