@@ -35,6 +35,7 @@ constexpr int ABS_COLS = 128;
 constexpr int ABS_ROWB = ABS_COLS * 2 + 32;   // 288
 constexpr int ABS_THREADS = 256;
 constexpr int ABS_WPT = DH * ABS_COLS / 8 / ABS_THREADS;   // 16-byte weight pieces per thread
+constexpr int ABS_QROWB = DH * 2 + 16;                      // staged query row (bf16) + pad
 
 // cos and sin of pos * base^(-2i/d_r): the angle is formed in double and
 // reduced modulo 2 pi in double (2 pi as a sum of two doubles), and the
@@ -59,6 +60,9 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
                                                            __bf16* __restrict__ q_lat,
                                                            __bf16* __restrict__ q_pe) {
   __shared__ __attribute__((aligned(16))) char w[DH * ABS_ROWB];
+  // fp32 query: one batch block's q_C of this head as bf16 hi and lo planes,
+  // split once per workgroup instead of once per wave
+  __shared__ __attribute__((aligned(16))) char qs[QF32 ? 2 : 1][QF32 ? 32 * ABS_QROWB : 16];
   const int h = blockIdx.x, qt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g32 = lane >> 5;
 
@@ -72,25 +76,42 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
   }
 
   // B operand: q_C[bq][h][16 ks + 8 g32 .. +8] (and its low part)
-  bf16x8 qb[DH / 16], ql[QF32 ? DH / 16 : 1];
+  bf16x8 qb[DH / 16];
+  // fp32: the batch block's 32 x 128 query values, 16 per thread, read here
+  // and split into the LDS planes by stage_q (after the previous block's
+  // fragment reads); bf16: the B fragments straight into registers.
+  floatx4 qf[QF32 ? 4 : 1];
   auto load_q = [&](int nb) {
-    const int bq = nb * 32 + (lane & 31);
-    const bool bok = bq < B;
+    if constexpr (QF32) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
-      const size_t e0 = ((size_t)(bok ? bq : 0) * NH + h) * QW + 16 * ks + 8 * g32;
-      if constexpr (QF32) {
-        const float* qf = (const float*)qv + e0;
-        const floatx4 x0 = *(const floatx4*)qf, x1 = *(const floatx4*)(qf + 4);
+      for (int u = 0; u < 4; ++u) {
+        const int idx = u * ABS_THREADS + tid, r = idx >> 5, c4 = idx & 31;   // row, 4-float piece
+        const int bq = nb * 32 + r;
+        qf[u] = bq < B ? *(const floatx4*)((const float*)qv + ((size_t)bq * NH + h) * QW + 4 * c4)
+                       : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      const int bq = nb * 32 + (lane & 31);
+      const bool bok = bq < B;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = bok ? (e < 4 ? x0[e] : x1[e - 4]) : 0.f;
-          qb[ks][e] = (__bf16)x;
-          ql[ks][e] = (__bf16)(x - (float)qb[ks][e]);
-        }
-      } else {
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        const size_t e0 = ((size_t)(bok ? bq : 0) * NH + h) * QW + 16 * ks + 8 * g32;
         qb[ks] = bok ? *(const bf16x8*)((const __bf16*)qv + e0) : bf16x8{};
       }
+    }
+  };
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = u * ABS_THREADS + tid, r = idx >> 5, c4 = idx & 31;
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)qf[u][e];
+        lo[e] = (__bf16)(qf[u][e] - (float)hi[e]);
+      }
+      *(bf16x4*)(qs[0] + r * ABS_QROWB + 8 * c4) = hi;
+      *(bf16x4*)(qs[QF32 ? 1 : 0] + r * ABS_QROWB + 8 * c4) = lo;
     }
   };
   load_q(0);
@@ -122,6 +143,7 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
     const int idx = j * ABS_THREADS + tid, r = idx >> 4, c = idx & 15;
     *(floatx4*)(w + r * ABS_ROWB + c * 16) = wv[j];
   }
+  if constexpr (QF32) stage_q();
   __syncthreads();
 
   // Transpose-read addressing (see the decode kernel): in 16-lane group G,
@@ -132,7 +154,14 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
   const uint32_t tr_off = (uint32_t)((i16 >> 2) * ABS_ROWB + 32 * h16 + 8 * (i16 & 3));
 
   for (int nb = 0; nb * 32 < B; ++nb) {
-    if (nb > 0) load_q(nb);
+    if (nb > 0) {
+      load_q(nb);
+      if constexpr (QF32) {
+        __syncthreads();   // every wave is done with the previous block's planes
+        stage_q();
+        __syncthreads();
+      }
+    }
     const int bq = nb * 32 + (lane & 31);
     floatx16 acc;
 #pragma unroll
@@ -144,8 +173,16 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
       const bf16x4 hi =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
-      if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[ks], acc, 0, 0, 0);
+      if constexpr (QF32) {
+        // B fragment: batch row lane & 31, k = 16 ks + 8 g32 .. +8, from both planes
+        const int off = (lane & 31) * ABS_QROWB + (16 * ks + 8 * g32) * 2;
+        const bf16x8 bh = *(const bf16x8*)(qs[0] + off);
+        const bf16x8 bl = *(const bf16x8*)(qs[1] + off);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
+      }
     }
     // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
     if (bq < B) {
