@@ -32,10 +32,12 @@
 //   reference, so the result is exact.  If a later score exceeds the
 //   reference by more than 2^64 the piece is flagged and the combine kernel
 //   recomputes that sequence with a plain online-softmax loop.
-// * Split-T: the sum of all lengths is divided evenly over G workgroups
-//   (one per CU); a workgroup's range may cross sequence boundaries and emits
-//   one partial (O, m, l) per sequence piece; a combine kernel merges the
-//   pieces of each sequence by log-sum-exp.
+// * Split-T: the rows of the whole batch are divided over G workgroups (one
+//   per CU) by cost -- each sequence start that would fall inside a range is
+//   charged a fixed setup cost, and without such starts the split is the
+//   even one; a workgroup's range may cross sequence boundaries and emits one
+//   partial (O, m, l) per sequence piece; a combine kernel merges the pieces
+//   of each sequence by log-sum-exp.
 #include <math.h>
 
 #include "common.h"
