@@ -384,7 +384,8 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 __device__ __forceinline__ void dma_16B_at(uint32_t lds_addr, const char* src) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src));
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "m0");
 }
 
 __device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const char* base) {
@@ -397,7 +398,8 @@ __device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const 
   // first use, and without it LDS reads may be scheduled across the DMA.
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base)));
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
+               : "m0");
 }
 
 template <int N>
