@@ -30,7 +30,7 @@ absorbed route used by the GPU path is an exact re-association of this
 ([MLA-struct], section "为什么矩阵吸收很关键", the two associativity identities),
 so the two must agree up to rounding.
 
-Readings of points the pages leave open (each is listed in the design doc too):
+Readings of points the pages leave open:
 
 * softmax scale = 1 / sqrt(d_h + d_R) applied to the sum of the content and
   RoPE scores (the pages write "x scale" without a value);
@@ -38,8 +38,10 @@ Readings of points the pages leave open (each is listed in the design doc too):
   (i, i + d_R/2); angles pos * theta_i are formed in fp64;
 * the cache always holds the already-rotated k^R (the worked example writes the
   RoPE'd k_pe into pe_cache);
-* no causal mask is applied: a single decode query sits at a position >= every
-  cached row, so the mask passes everything;
+* no causal mask is applied to a single decode query: it sits at a position
+  >= every cached row, so the mask passes everything; with n_q new tokens
+  (latent_attention_causal) they are the last n_q cached rows and token i
+  sees rows 0 .. T - n_q + i;
 * the latent ``norm(...)`` of the reference code path is not applied (its type
   and epsilon are not stated; c^KV = W^DKV h_t is the equation's definition);
 * weights are [out, in] row-major: W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c],
@@ -64,6 +66,7 @@ __all__ = [
     "decode_explicit",
     "absorb_query",
     "latent_attention",
+    "latent_attention_causal",
     "append_rows",
     "query_path",
     "project_out",
@@ -181,6 +184,30 @@ def latent_attention(q_lat, q_pe, c, k_rot, scale):
          + np.asarray(q_pe, np.float64) @ np.asarray(k_rot, np.float64).T) * scale
     p, lse = softmax_two_pass(s)
     return p @ np.asarray(c, np.float64), lse
+
+
+# ---------------------------------------------------------------------------
+# Several new tokens in one step.  [MLA-struct], worked example step 4 and the
+# inference code's mask: with more than one new token the score matrix gets a
+# causal mask before the softmax, so a token sees every earlier row and itself
+# but none of the tokens after it.  Reading: the n_q new tokens are the last
+# n_q of the T cached rows (appended before the attention), token i sits at
+# row T - n_q + i, and a masked score is -inf (weight exactly 0).
+# ---------------------------------------------------------------------------
+def latent_attention_causal(q_lat, q_pe, c, k_rot, scale):
+    """o_lat [n_q, n_h, d_c] and lse [n_q, n_h] for q_lat [n_q, n_h, d_c],
+    q_pe [n_q, n_h, d_R] (rotated) over the T rows c [T, d_c], k_rot [T, d_R]."""
+    q_lat = np.asarray(q_lat, np.float64)
+    q_pe = np.asarray(q_pe, np.float64)
+    c = np.asarray(c, np.float64)
+    k_rot = np.asarray(k_rot, np.float64)
+    n_q, T = q_lat.shape[0], c.shape[0]
+    s = (q_lat @ c.T + q_pe @ k_rot.T) * scale                       # [n_q, n_h, T]
+    row = np.arange(T)[None, :]
+    tok = (T - n_q + np.arange(n_q))[:, None]
+    s = np.where((row <= tok)[:, None, :], s, -np.inf)                # causal mask
+    p, lse = softmax_two_pass(s)
+    return p @ c, lse
 
 
 # ---------------------------------------------------------------------------

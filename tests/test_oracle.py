@@ -472,6 +472,62 @@ def test_layer_step_consistent_and_shapes(golden_dir):
 # A planted mistake must be caught (mutations applied to a copy of the oracle
 # on the CPU; the suite above must reject each of them).
 # ---------------------------------------------------------------------------
+# Several new tokens per step (causal mask).
+def _causal_case(rng, T, n_q, n_h=3, d_c=12, d_r=6):
+    return (rng.standard_normal((n_q, n_h, d_c)), rng.standard_normal((n_q, n_h, d_r)),
+            rng.standard_normal((T, d_c)), rng.standard_normal((T, d_r)), 0.3)
+
+
+def test_causal_matches_torch_sdpa_mask_fp64():
+    # torch's attention with a boolean lower-triangular mask, offset so that
+    # query i of n_q keeps keys j <= T - n_q + i; keys [c | k^R], values c.
+    rng = np.random.default_rng(21)
+    for T, n_q in ((1, 1), (5, 5), (9, 3), (64, 4), (300, 7)):
+        ql, qp, c, kr, scale = _causal_case(rng, T, n_q)
+        n_h = ql.shape[1]
+        o, lse = O.latent_attention_causal(ql, qp, c, kr, scale)
+        K = torch.from_numpy(np.concatenate([c, kr], 1)).unsqueeze(0).expand(n_h, -1, -1)
+        V = torch.from_numpy(c).unsqueeze(0).expand(n_h, -1, -1)
+        q = torch.from_numpy(np.concatenate([ql, qp], 2)).transpose(0, 1).contiguous()   # [n_h, n_q, D]
+        mask = torch.ones(n_q, T, dtype=torch.bool).tril(T - n_q)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=mask, scale=scale)
+        assert rel_err(o, ref.transpose(0, 1).numpy()) < 1e-12
+        sc = torch.matmul(q, K.transpose(1, 2).contiguous()) * scale
+        ref_lse = torch.logsumexp(sc.masked_fill(~mask, float("-inf")), dim=-1)           # [n_h, n_q]
+        assert rel_err(lse, ref_lse.transpose(0, 1).numpy()) < 1e-12
+
+
+def test_causal_token_equals_decode_over_its_prefix():
+    # token i of the step is a single-query decode over rows 0 .. T - n_q + i;
+    # with n_q = 1 the step is the plain decode over all T rows
+    rng = np.random.default_rng(22)
+    for T, n_q in ((7, 1), (12, 4), (6, 6)):
+        ql, qp, c, kr, scale = _causal_case(rng, T, n_q)
+        o, lse = O.latent_attention_causal(ql, qp, c, kr, scale)
+        for i in range(n_q):
+            n = T - n_q + i + 1
+            oi, lsei = O.latent_attention(ql[i], qp[i], c[:n], kr[:n], scale)
+            assert rel_err(o[i], oi) < RTOL and rel_err(lse[i], lsei) < RTOL
+        # an off-by-one mask (token i seeing one row fewer) is a different result
+        if n_q > 1 and T > n_q:
+            n = T - n_q + 1
+            oi, _ = O.latent_attention(ql[1], qp[1], c[:n], kr[:n], scale)
+            assert rel_err(o[1], oi) > 1e-3
+
+
+def test_causal_first_token_of_fresh_sequence_sees_one_row():
+    # a sequence whose cache holds only the step's tokens: token 0 attends to
+    # row 0 alone, so its output is that row and its lse is that score
+    rng = np.random.default_rng(23)
+    ql, qp, c, kr, scale = _causal_case(rng, 4, 4)
+    o, lse = O.latent_attention_causal(ql, qp, c, kr, scale)
+    for h in range(ql.shape[1]):
+        assert rel_err(o[0, h], c[0]) < RTOL
+        s0 = (ql[0, h] @ c[0] + qp[0, h] @ kr[0]) * scale
+        assert abs(lse[0, h] - s0) < 1e-12 * max(1.0, abs(s0))
+
+
+# ---------------------------------------------------------------------------
 def test_planted_mistakes_are_caught(monkeypatch):
     rng = np.random.default_rng(18)
     k = rand_case(rng, n_h=4, d_c=32, d_r=8, d_h=16, d_v=16, T=40)
