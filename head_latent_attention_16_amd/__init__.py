@@ -6,8 +6,9 @@ tensors to that ABI; they load the library on first use and raise if it is
 missing.  ``inputs`` (seeded synthetic workloads) imports nothing from here.
 """
 
-__all__ = ["absorb_q", "append_cache", "decode_attn", "project_out", "cache_row_bytes",
-           "decode_attn_workspace", "Dims", "MLAError", "lib"]
+__all__ = ["absorb_q", "append_cache", "decode_attn", "decode_attn_causal", "project_out",
+           "cache_row_bytes", "decode_attn_workspace", "decode_attn_causal_workspace", "Dims",
+           "MLAError", "lib"]
 
 
 def __getattr__(name):

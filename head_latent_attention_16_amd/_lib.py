@@ -27,6 +27,7 @@ DT_BF16, DT_F32 = 0, 1
 
 EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_append_cache_workspace", "mla_decode_attn", "mla_decode_attn_workspace",
+           "mla_decode_attn_causal", "mla_decode_attn_causal_workspace",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
            "mla_status_string", "mla_abi_version")
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "mla_append_cache_workspace": ([D, i32, i32, i32], sz),
         "mla_decode_attn": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_workspace": ([D, i32, i64], sz),
+        "mla_decode_attn_causal": ([D, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
+        "mla_decode_attn_causal_workspace": ([D, i32, i32, i64], sz),
         "mla_project_out": ([D, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "mla_project_out_workspace": ([D, i32, i32], sz),
         "mla_cache_row_bytes": ([D], sz),
@@ -150,6 +153,10 @@ def cache_row_bytes(dims: Dims) -> int:
 
 def decode_attn_workspace(dims: Dims, B: int, total_rows_hint: int) -> int:
     return int(lib().mla_decode_attn_workspace(ctypes.byref(dims), B, int(total_rows_hint)))
+
+
+def decode_attn_causal_workspace(dims: Dims, B: int, n_q: int, total_rows_hint: int) -> int:
+    return int(lib().mla_decode_attn_causal_workspace(ctypes.byref(dims), B, n_q, int(total_rows_hint)))
 
 
 def absorb_q(dims: Dims, q_lat, q_pe, W_UK, pos, q=None, h_t=None, W_DQ=None, W_UQ=None,
@@ -238,3 +245,29 @@ def project_out(dims: Dims, o_lat, W_UV, o=None, u=None, W_O=None, ws=None, stre
     st = L.mla_project_out(ctypes.byref(dims), B, _ptr(o_lat), _ptr(W_UV), _ptr(W_O), _ptr(o),
                            _ptr(u), w, wn, _stream(stream))
     _check("mla_project_out", st)
+
+
+def decode_attn_causal(dims: Dims, n_q: int, q_lat, q_pe, cache, offsets, lens, o_lat, lse=None,
+                       total_rows_hint: Optional[int] = None, err_flag=None, ws=None, stream=None):
+    """n_q new tokens per sequence (the last n_q cached rows): token i of
+    sequence b attends to rows 0 .. lens[b] - n_q + i.  q_lat, q_pe, o_lat,
+    lse are [B, n_q, n_h, ...]."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(q_lat, q_pe, cache, offsets, lens, o_lat, lse, err_flag)
+    _need(q_lat, B * n_q * dims.n_h * dims.d_c, dt, "q_lat")
+    _need(q_pe, B * n_q * dims.n_h * dims.d_r, dt, "q_pe")
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(o_lat, B * n_q * dims.n_h * dims.d_c, torch.float32, "o_lat")
+    _need(lse, B * n_q * dims.n_h, torch.float32, "lse")
+    if cache.dtype != dt:
+        raise ValueError("cache dtype")
+    hint = int(total_rows_hint) if total_rows_hint is not None else max(1, cache.shape[0])
+    nbytes = decode_attn_causal_workspace(dims, B, n_q, hint)
+    ws = _workspace(nbytes, ws, cache.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_decode_attn_causal(ctypes.byref(dims), B, n_q, _ptr(q_lat), _ptr(q_pe), _ptr(cache),
+                                  _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse),
+                                  _ptr(err_flag), w, wn, _stream(stream))
+    _check("mla_decode_attn_causal", st)

@@ -116,9 +116,46 @@ size_t project_ws(const Shape& s, int B, bool with_u) {
   return align256((size_t)B * s.n_h * s.d_v * sizeof(float)) +
          align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v));
 }
-size_t decode_ws(const Shape& s, int B, int64_t hint, int num_cu) {
-  if (!force_generic() && decode_v3_supported(s)) return decode_v3_workspace(s, B, hint, num_cu);
+// Query tokens per call (B n_q): the combine and generic decode grids index
+// them in their second dimension.
+constexpr int64_t kMaxQueryTokens = 65535;
+// Only sizes the launch; clamped so that hint * n_q stays far from overflow.
+int64_t clamp_hint(int64_t hint) { return hint < 1 ? 1 : (hint > (int64_t(1) << 40) ? int64_t(1) << 40 : hint); }
+
+size_t decode_ws(const Shape& s, int B, int n_q, int64_t hint, int num_cu) {
+  if (!force_generic() && decode_v3_supported(s))
+    return decode_v3_workspace(s, B, n_q, clamp_hint(hint), num_cu);
   return 0;
+}
+
+mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
+                           const void* q_pe, const void* cache, const int32_t* offsets,
+                           const int32_t* lens, int64_t total_rows_hint, float* o_lat, float* lse,
+                           int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0 || n_q < 1 || (int64_t)B * n_q > kMaxQueryTokens) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (total_rows_hint < 1) return MLA_ERR_SHAPE;
+  if (!q_lat || !q_pe || !cache || !offsets || !lens || !o_lat) return MLA_ERR_NULL;
+  total_rows_hint = clamp_hint(total_rows_hint);
+  DeviceInfo info;
+  const bool fast = !force_generic() && decode_v3_supported(s);
+  // The workspace requirement depends on the device's CU count; size it
+  // before touching the device only when the fast path needs it.
+  if (fast) {
+    if (!ws) return MLA_ERR_WORKSPACE;
+    if ((st = device_ready(&info)) != MLA_OK) return st;
+    const size_t need = decode_v3_workspace(s, B, n_q, total_rows_hint, info.num_cu);
+    if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+    return launched(launch_decode_v3(s, B, n_q, q_lat, q_pe, cache, offsets, lens, total_rows_hint,
+                                     o_lat, lse, err_flag, ws, ws_bytes, info.num_cu,
+                                     (hipStream_t)stream));
+  }
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  return launched(launch_decode_generic(s, B, n_q, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
+                                        err_flag, (hipStream_t)stream));
 }
 
 int num_cu_or_default() {
@@ -295,10 +332,7 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
 }
 
 size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint) {
-  Shape s;
-  if (check_dims(dims, &s) != MLA_OK || B < 0) return 0;
-  if (total_rows_hint < 1) total_rows_hint = 1;
-  return decode_ws(s, B, total_rows_hint, num_cu_or_default());
+  return mla_decode_attn_causal_workspace(dims, B, 1, total_rows_hint);
 }
 
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_lat,
@@ -306,29 +340,24 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_la
                              const int32_t* lens, int64_t total_rows_hint, float* o_lat,
                              float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
                              void* stream) {
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+                       err_flag, ws, ws_bytes, stream);
+}
+
+size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q,
+                                        int64_t total_rows_hint) {
   Shape s;
-  mla_status_t st = check_dims(dims, &s);
-  if (st != MLA_OK) return st;
-  if (B < 0) return MLA_ERR_SHAPE;
-  if (B == 0) return MLA_OK;
-  if (total_rows_hint < 1) return MLA_ERR_SHAPE;
-  if (!q_lat || !q_pe || !cache || !offsets || !lens || !o_lat) return MLA_ERR_NULL;
-  DeviceInfo info;
-  const bool fast = !force_generic() && decode_v3_supported(s);
-  // The workspace requirement depends on the device's CU count; size it
-  // before touching the device only when the fast path needs it.
-  if (fast) {
-    if (!ws) return MLA_ERR_WORKSPACE;
-    if ((st = device_ready(&info)) != MLA_OK) return st;
-    const size_t need = decode_v3_workspace(s, B, total_rows_hint, info.num_cu);
-    if (ws_bytes < need) return MLA_ERR_WORKSPACE;
-    return launched(launch_decode_v3(s, B, q_lat, q_pe, cache, offsets, lens, total_rows_hint,
-                                     o_lat, lse, err_flag, ws, ws_bytes, info.num_cu,
-                                     (hipStream_t)stream));
-  }
-  if ((st = device_ready(&info)) != MLA_OK) return st;
-  return launched(launch_decode_generic(s, B, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
-                                        err_flag, (hipStream_t)stream));
+  if (check_dims(dims, &s) != MLA_OK || B < 0 || n_q < 1 || (int64_t)B * n_q > kMaxQueryTokens) return 0;
+  return decode_ws(s, B, n_q, total_rows_hint, num_cu_or_default());
+}
+
+mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n_q,
+                                    const void* q_lat, const void* q_pe, const void* cache,
+                                    const int32_t* offsets, const int32_t* lens,
+                                    int64_t total_rows_hint, float* o_lat, float* lse,
+                                    int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+  return decode_common(dims, B, n_q, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+                       err_flag, ws, ws_bytes, stream);
 }
 
 size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {

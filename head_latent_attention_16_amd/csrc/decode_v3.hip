@@ -177,6 +177,20 @@ __device__ __forceinline__ int4 seq_info(int64_t vb, int64_t len, const Line& vl
 // ---------------------------------------------------------------------------
 // Scheduler: validate lengths, prefix-sum the valid ones (invalid -> 0).
 // ---------------------------------------------------------------------------
+// Several new tokens per step: query token i < n_q of sequence b is handled as
+// sequence v = b n_q + i with its own queries and outputs.  The step's tokens
+// are the last n_q of the lens[b] cached rows, and token i sees rows
+// 0 .. lens[b] - n_q + i (causal mask).  Sequence b is valid when
+// n_q <= lens[b] <= offsets[b+1] - offsets[b]; n_q = 1 is the plain decode.
+__device__ __forceinline__ int seq_of(int v, int n_q) { return n_q == 1 ? v : v / n_q; }
+
+// Rows seen by sequence v (>= 1), or 0 if its sequence is invalid.
+__device__ __forceinline__ int vseq_len(const int32_t* lens, const int32_t* offsets, int v, int n_q) {
+  const int b = seq_of(v, n_q);
+  const int len = lens[b], cap = offsets[b + 1] - offsets[b];
+  return len >= n_q && len <= cap ? len - (n_q - 1 - (v - b * n_q)) : 0;
+}
+
 constexpr int SCHED_THREADS = 1024;
 constexpr int SCHED_PER = 4;
 constexpr int SCHED_LDS_B = 4096;   // prefix kept in LDS up to this many sequences
@@ -215,7 +229,8 @@ __device__ __forceinline__ int64_t block_scan_1024(int64_t tsum, int64_t* wsum, 
   return excl;
 }
 
-__global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int32_t* __restrict__ offsets,
+__global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int n_q, int G,
+                                                         const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ lens,
                                                          int64_t* __restrict__ prefix,
                                                          int32_t* __restrict__ cnt,
@@ -241,9 +256,8 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
       const int b = base + SCHED_PER * tid + j;
       v[j] = 0;
       if (b < B) {
-        const int len = lens[b];
-        const int cap = offsets[b + 1] - offsets[b];
-        if (len >= 1 && len <= cap)
+        const int len = vseq_len(lens, offsets, b, n_q);
+        if (len > 0)
           v[j] = len;
         else if (err_flag)
           atomicOr(err_flag, MLA_DEVERR_LENS);
@@ -333,7 +347,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int G, const int
     r.seq_begin = pre(lo);
     r.seq_end = pre(lo + 1);
     r.b = lo;
-    r.off_b = offsets[lo];
+    r.off_b = offsets[seq_of(lo, n_q)];
     r.pad[0] = r.pad[1] = 0;
     rec[g] = r;
   }
@@ -359,7 +373,8 @@ struct SplitArgs {
   const int64_t* prefix;
   _Float16* part_o;
   float* part_ml;
-  int B;
+  int B;     // sequences as the kernels see them: one per query token
+  int n_q;   // query tokens per sequence of the caller
   int G;
   float scale_log2;
 };
@@ -498,9 +513,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     if (wave == 0) {
       const int l = lane_id;
       const bool in = l < B;
-      const int len = a.lens[min(l, B - 1)];
-      const int o0 = a.offsets[min(l, B)], o1 = a.offsets[min(l + 1, B)];
-      const bool ok = len >= 1 && len <= o1 - o0;
+      const int len = vseq_len(a.lens, a.offsets, min(l, B - 1), a.n_q);
+      const int o0 = a.offsets[seq_of(min(l, B - 1), a.n_q)];
+      const bool ok = len > 0;
       const int64_t v = in && ok ? len : 0;
       bad = in && !ok ? 1 : 0;
       int64_t x = v;   // inclusive prefix of the valid lengths
@@ -563,20 +578,21 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int tid = threadIdx.x;
     const int B = a.B, G = a.G;
     // all loads first (indices clamped), so they share one round trip
-    int lenj[SPL_PER], offj[SPL_PER + 1];
+    int lenj[SPL_PER], offj[SPL_PER];
 #pragma unroll
-    for (int j = 0; j < SPL_PER; ++j) lenj[j] = a.lens[min(tid * SPL_PER + j, B - 1)];
-#pragma unroll
-    for (int j = 0; j <= SPL_PER; ++j) offj[j] = a.offsets[min(tid * SPL_PER + j, B)];   // B + 1 entries
+    for (int j = 0; j < SPL_PER; ++j) {
+      const int bb = min(tid * SPL_PER + j, B - 1);
+      lenj[j] = vseq_len(a.lens, a.offsets, bb, a.n_q);
+      offj[j] = a.offsets[seq_of(bb, a.n_q)];
+    }
     int64_t v[SPL_PER];
     int64_t tsum = 0;
     int bad = 0;
 #pragma unroll
     for (int j = 0; j < SPL_PER; ++j) {
       const int bb = tid * SPL_PER + j;
-      const int cap = offj[j + 1] - offj[j];
       const bool in = bb < B;
-      const bool ok = lenj[j] >= 1 && lenj[j] <= cap;
+      const bool ok = lenj[j] > 0;
       v[j] = in && ok ? lenj[j] : 0;
       bad |= in && !ok ? 1 : 0;
       if (in) s_off[bb] = offj[j];
@@ -712,7 +728,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   };
   auto off_of = [&](int i) -> int {
     if constexpr (SCAN) return uniform_i32(s_off[i]);
-    else return uniform_i32(a.offsets[i]);
+    else return uniform_i32(a.offsets[seq_of(i, a.n_q)]);
   };
 
   if (start >= end) {
@@ -1180,7 +1196,8 @@ struct CombineArgs {
   const float* part_ml;
   float* o_lat;
   float* lse;
-  int B;
+  int B;     // one per query token, as in the split kernel
+  int n_q;
   int G;
   int cpw;   // column blocks per combine workgroup
   float scale_log2;
@@ -1207,7 +1224,7 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
 #pragma unroll
   for (int k = 0; k < DC / 64; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const __bf16* rows = a.cache + (size_t)a.offsets[b] * DK;
+  const __bf16* rows = a.cache + (size_t)a.offsets[seq_of(b, a.n_q)] * DK;
   for (int j = wave; j < len; j += CMB_WAVES) {
     const __bf16* r = rows + (size_t)j * DK;
     float sdot = 0.f;
@@ -1457,15 +1474,18 @@ bool decode_v3_supported(const Shape& s) {
   return s.bf16 && s.n_h == NH && s.d_c == DC && s.d_r == DR;
 }
 
-size_t decode_v3_workspace(const Shape&, int B, int64_t total_rows_hint, int num_cu) {
-  return partial_layout(B, choose_groups(total_rows_hint, num_cu)).bytes;
+// B sequences of n_q query tokens each run as B n_q sequences (one per token,
+// see seq_of); the rows they process add up to about n_q times the hint.
+size_t decode_v3_workspace(const Shape&, int B, int n_q, int64_t total_rows_hint, int num_cu) {
+  return partial_layout(B * n_q, choose_groups(total_rows_hint * n_q, num_cu)).bytes;
 }
 
-hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void* q_pe,
+hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_lat, const void* q_pe,
                             const void* cache, const int32_t* offsets, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t, int num_cu, hipStream_t st) {
-  const int G = choose_groups(total_rows_hint, num_cu);
+  const int B = B_seq * n_q;
+  const int G = choose_groups(total_rows_hint * n_q, num_cu);
   const PartialLayout L = partial_layout(B, G);
   char* w = (char*)ws;
   int64_t* prefix = (int64_t*)(w + L.pre_off);
@@ -1488,12 +1508,13 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   a.part_o = (_Float16*)(w + L.o_off);
   a.part_ml = (float*)(w + L.ml_off);
   a.B = B;
+  a.n_q = n_q;
   a.G = G;
   a.scale_log2 = s.scale * kLog2e;
   if (B <= SPL_MAXB) {
     k_split<true><<<G, THREADS, 0, st>>>(a);
   } else {
-    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, G, offsets, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
+    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, n_q, G, offsets, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
                                          err_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1513,6 +1534,7 @@ hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void
   c.o_lat = o_lat;
   c.lse = lse;
   c.B = B;
+  c.n_q = n_q;
   c.G = G;
   c.scale_log2 = a.scale_log2;
   // about G / B pieces per sequence: fewer pieces, more column blocks per

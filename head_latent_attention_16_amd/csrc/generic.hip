@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(256) k_append(int n_new, int d_c, int d_r, dou
 // keeps an online softmax (running max m, sum l, accumulator), and the four
 // partial states are merged through LDS at the end.
 template <typename T>
-__global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, float scale_log2,
+__global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n_q, float scale_log2,
                                                 const T* __restrict__ q_lat, const T* __restrict__ q_pe,
                                                 const T* __restrict__ cache,
                                                 const int32_t* __restrict__ offsets,
@@ -124,30 +124,34 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, float
                                                 float* __restrict__ o_lat, float* __restrict__ lse,
                                                 int32_t* err_flag) {
   extern __shared__ float smem[];
-  const int h = blockIdx.x, b = blockIdx.y;
+  // block (h, v): head h of query token i = v % n_q of sequence b = v / n_q,
+  // which sees rows 0 .. lens[b] - n_q + i of the sequence
+  const int h = blockIdx.x, v = blockIdx.y;
+  const int b = v / n_q, tok = v - b * n_q;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
   const int D = d_c + d_r;
-  const int len = lens[b];
+  const int all = lens[b];
   const int off = offsets[b];
   const int cap = offsets[b + 1] - off;
-  float* out = o_lat + ((size_t)b * n_h + h) * d_c;
-  if (len < 1 || len > cap) {
+  float* out = o_lat + ((size_t)v * n_h + h) * d_c;
+  if (all < n_q || all > cap) {
     for (int c = threadIdx.x; c < d_c; c += blockDim.x) out[c] = __builtin_nanf("");
     if (threadIdx.x == 0) {
-      if (lse) lse[(size_t)b * n_h + h] = __builtin_nanf("");
+      if (lse) lse[(size_t)v * n_h + h] = __builtin_nanf("");
       if (err_flag) atomicOr(err_flag, MLA_DEVERR_LENS);
     }
     return;
   }
+  const int len = all - (n_q - 1 - tok);
   float q[kMaxRowPerLane];
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     int f = lane + 64 * k;
-    float v = 0.f;
-    if (f < d_c) v = ld(q_lat, ((size_t)b * n_h + h) * d_c + f);
-    else if (f < D) v = ld(q_pe, ((size_t)b * n_h + h) * d_r + (f - d_c));
-    q[k] = v;
+    float x = 0.f;
+    if (f < d_c) x = ld(q_lat, ((size_t)v * n_h + h) * d_c + f);
+    else if (f < D) x = ld(q_pe, ((size_t)v * n_h + h) * d_r + (f - d_c));
+    q[k] = x;
   }
   float acc[kMaxLatPerLane];
 #pragma unroll
@@ -189,12 +193,12 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, float
   float L = 0.f;
   for (int w = 0; w < nw; ++w) L += (sm[w] == -INFINITY) ? 0.f : sl[w] * exp2f(sm[w] - M);
   for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    float v = 0.f;
+    float acc_c = 0.f;
     for (int w = 0; w < nw; ++w)
-      if (sm[w] != -INFINITY) v += sacc[w * d_c + c] * exp2f(sm[w] - M);
-    out[c] = v / L;
+      if (sm[w] != -INFINITY) acc_c += sacc[w * d_c + c] * exp2f(sm[w] - M);
+    out[c] = acc_c / L;
   }
-  if (threadIdx.x == 0 && lse) lse[(size_t)b * n_h + h] = (M + log2f(L)) * kLn2;
+  if (threadIdx.x == 0 && lse) lse[(size_t)v * n_h + h] = (M + log2f(L)) * kLn2;
 }
 
 // o[b,h,v] = sum_c W_UV[h,v,c] o_lat[b,h,c]; one wave per (v-group of 4, h, b).
@@ -252,19 +256,19 @@ hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c
   return hipGetLastError();
 }
 
-hipError_t launch_decode_generic(const Shape& s, int B, const void* q_lat, const void* q_pe,
+hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
                                  const void* cache, const int32_t* offsets, const int32_t* lens,
                                  float* o_lat, float* lse, int32_t* err_flag, hipStream_t st) {
   const int threads = 256, nw = threads / 64;
   size_t smem = sizeof(float) * (2 * nw + (size_t)nw * s.d_c);
-  dim3 grid(s.n_h, B);
+  dim3 grid(s.n_h, B * n_q);
   float sl2 = s.scale * kLog2e;
   if (s.bf16)
-    k_decode<__bf16><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, sl2, (const __bf16*)q_lat,
+    k_decode<__bf16><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const __bf16*)q_lat,
                                                   (const __bf16*)q_pe, (const __bf16*)cache, offsets,
                                                   lens, o_lat, lse, err_flag);
   else
-    k_decode<float><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, sl2, (const float*)q_lat,
+    k_decode<float><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const float*)q_lat,
                                                  (const float*)q_pe, (const float*)cache, offsets,
                                                  lens, o_lat, lse, err_flag);
   return hipGetLastError();

@@ -30,7 +30,10 @@ hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c
                                  size_t c_stride, const void* k_src, size_t k_stride, bool src_f32,
                                  void* cache, const int32_t* offsets, int32_t* lens,
                                  int32_t* err_flag, hipStream_t st);
-hipError_t launch_decode_generic(const Shape& s, int B, const void* q_lat, const void* q_pe,
+// B sequences with n_q query tokens each (n_q = 1: one decode query; n_q > 1:
+// the last n_q cached rows are the step's tokens, token i sees rows up to
+// lens[b] - n_q + i).  q_lat, q_pe, o_lat, lse are [B, n_q, n_h, ...].
+hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
                                  const void* cache, const int32_t* offsets, const int32_t* lens,
                                  float* o_lat, float* lse, int32_t* err_flag, hipStream_t st);
 // o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 out)
@@ -39,8 +42,8 @@ hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const vo
 
 // ---- V3 fast path (bf16, d_c = 512, d_r = 64, n_h = 128) --------------------
 bool decode_v3_supported(const Shape& s);
-size_t decode_v3_workspace(const Shape& s, int B, int64_t total_rows_hint, int num_cu);
-hipError_t launch_decode_v3(const Shape& s, int B, const void* q_lat, const void* q_pe,
+size_t decode_v3_workspace(const Shape& s, int B, int n_q, int64_t total_rows_hint, int num_cu);
+hipError_t launch_decode_v3(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
                             const void* cache, const int32_t* offsets, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t ws_bytes, int num_cu, hipStream_t st);

@@ -14,6 +14,8 @@
  *                     latent query q_lat = W^UK^T q^C per head and q_pe = RoPE(q^R)
  *   mla_append_cache  new row [c^KV | RoPE(k^R)] written at each sequence's end
  *   mla_decode_attn   o_lat = softmax(scale (q_lat.c + q_pe.k^R)) . c  (the hot loop)
+ *                     (mla_decode_attn_causal: n_q new tokens per sequence,
+ *                     causally masked among themselves)
  *   mla_project_out   o = W^UV o_lat per head, u = W^O flatten(o)
  *
  * Conventions shared by every entry point
@@ -136,8 +138,9 @@ size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_n
  * q_lat [B, n_h, d_c], q_pe [B, n_h, d_r] in dims->dtype; o_lat [B, n_h, d_c] fp32.
  * No mask: every cached row precedes the query.  lens[b] must be in
  * [1, offsets[b+1]-offsets[b]]; a sequence violating it gets NaN outputs and
- * MLA_DEVERR_LENS.  total_rows_hint (> 0) is the expected sum of lens and only
- * sizes the launch; results do not depend on it.
+ * MLA_DEVERR_LENS.  B <= 65535 (else MLA_ERR_SHAPE).  total_rows_hint (> 0) is
+ * the expected sum of lens and only sizes the launch; results do not depend
+ * on it.
  * ws: at least mla_decode_attn_workspace(dims, B, total_rows_hint) bytes. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_lat,
                              const void* q_pe, const void* cache, const int32_t* offsets,
@@ -145,6 +148,32 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_la
                              float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
                              void* stream);
 size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint);
+
+/* Several new tokens per sequence in one step ("MLA模型结构详解", worked
+ * example step 4: with more than one new token the inference code masks the
+ * scores causally before the softmax).  The step's n_q tokens are the last
+ * n_q of the lens[b] cached rows (appended first, e.g. by mla_append_cache
+ * with n_new = n_q), and token i < n_q attends to rows 0 .. lens[b] - n_q + i:
+ *   o_lat[b,i,h,:] = sum_{j <= lens[b]-n_q+i} p_j c_j,
+ *   p = softmax_j( scale * (q_lat[b,i,h,:].c_j + q_pe[b,i,h,:].kR_j) ),
+ *   lse[b,i,h] as in mla_decode_attn.
+ * q_lat [B, n_q, n_h, d_c], q_pe [B, n_q, n_h, d_r] in dims->dtype; o_lat
+ * [B, n_q, n_h, d_c] fp32; lse [B, n_q, n_h] fp32 or NULL.  n_q = 1 is exactly
+ * mla_decode_attn.  Needs 1 <= n_q and B * n_q <= 65535 (else MLA_ERR_SHAPE);
+ * lens[b] must be in [n_q, offsets[b+1]-offsets[b]], else all n_q tokens of
+ * sequence b get NaN outputs and MLA_DEVERR_LENS.  total_rows_hint (> 0) is
+ * the expected sum of lens.  Each token is run as a sequence of its own over
+ * its rows (so a row is streamed once per token that sees it; neighbouring
+ * tokens of a sequence share the reads through the cache hierarchy).
+ * ws: at least mla_decode_attn_causal_workspace(dims, B, n_q, total_rows_hint)
+ * bytes. */
+mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n_q,
+                                    const void* q_lat, const void* q_pe, const void* cache,
+                                    const int32_t* offsets, const int32_t* lens,
+                                    int64_t total_rows_hint, float* o_lat, float* lse,
+                                    int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
+size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q,
+                                        int64_t total_rows_hint);
 
 /* Output side ("MLA模型结构详解", worked example step 5: multiply by the value
  * part of wkv_b per head, flatten heads, output projection).

@@ -126,3 +126,26 @@ def test_decode_workspace_sizes(lib):
     # generic path (fp32 tiny dims) needs none
     tiny = L.Dims.make(4, 32, 8, 16, 16, dtype="f32")
     assert lib.mla_decode_attn_workspace(ctypes.byref(tiny), 1, 64) == 0
+
+
+def call_causal(lib, dims, B=2, n_q=3, ptr=P, hint=100, ws=P, ws_bytes=1 << 40):
+    return lib.mla_decode_attn_causal(ctypes.byref(dims), B, n_q, ptr, ptr, ptr, ptr, ptr, hint, ptr,
+                                      None, None, ws, ws_bytes, None)
+
+
+def test_causal_validation_and_workspace(lib):
+    d = v3()
+    assert call_causal(lib, d, n_q=0) == 2
+    assert call_causal(lib, d, n_q=-3) == 2
+    assert call_causal(lib, d, B=65535 // 3 + 1) == 2    # more than 65535 query tokens
+    assert call_decode(lib, d, B=65536) == 2             # the same bound for one token each
+    assert call_causal(lib, d, B=0) == 0
+    assert call_causal(lib, d, ptr=None) == 1
+    assert call_causal(lib, d, ws=None) == 4
+    assert call_causal(lib, d) == 6                      # valid call, no GPU here
+    # n_q = 1 is the plain decode; n_q tokens need the scratch of B n_q sequences
+    one = lib.mla_decode_attn_causal_workspace(ctypes.byref(d), 16, 1, 65536)
+    assert one == lib.mla_decode_attn_workspace(ctypes.byref(d), 16, 65536)
+    four = lib.mla_decode_attn_causal_workspace(ctypes.byref(d), 16, 4, 65536)
+    assert four >= lib.mla_decode_attn_workspace(ctypes.byref(d), 64, 4 * 65536) > 0
+    assert lib.mla_decode_attn_causal_workspace(ctypes.byref(d), 16, 0, 65536) == 0
