@@ -1,12 +1,14 @@
 """Benchmark one MLA decode step on one MI355X through the C ABI.
 
-    python bench.py [--steps K] [--warmup W] [--workload uniform|ragged|long|layer]
+    python bench.py [--steps K] [--warmup W] [--workload uniform|ragged|long|layer|causal]
 
 A step is one pass of the decode hot path over one batch:
   attention-only workloads (uniform, ragged, long):
       mla_absorb_q (q given) -> mla_decode_attn -> mla_project_out (o)
   layer workload: mla_absorb_q (from h_t) -> mla_append_cache (from h_t)
       -> mla_decode_attn -> mla_project_out (o and u)
+  causal workload (--n-q new tokens per sequence, the cache's last rows):
+      mla_absorb_q (B n_q queries) -> mla_decode_attn_causal -> mla_project_out (o)
 Inputs are seeded synthetic tensors of the DeepSeek-V3 shapes, resident in
 HBM before timing; several independent copies of all inputs are rotated so
 that consecutive steps do not hit in the 256 MB Infinity Cache.
@@ -46,7 +48,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="uniform", choices=["uniform", "ragged", "long", "layer"])
+    p.add_argument("--workload", default="uniform", choices=["uniform", "ragged", "long", "layer", "causal"])
+    p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
     p.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,11 +61,14 @@ def parse():
 
 
 def algorithmic(w):
-    """Bytes and FLOPs of one mla_decode_attn call (cache read once, q in, o_lat out)."""
-    n_h, d_c, d_r = w.dims["n_h"], w.dims["d_c"], w.dims["d_r"]
+    """Bytes and FLOPs of one attention call: the cache read once, q in, o_lat
+    out; with n_q tokens per sequence token i scores T - n_q + i + 1 rows."""
+    n_h, d_c, d_r, n_q = w.dims["n_h"], w.dims["d_c"], w.dims["d_r"], w.n_q
     tokens = int(w.total_rows)
-    byts = tokens * (d_c + d_r) * 2 + w.B * n_h * (d_c + d_r) * 2 + w.B * n_h * d_c * 4
-    flops = tokens * 2 * n_h * ((d_c + d_r) + d_c)
+    nq_tok = w.B * n_q
+    byts = tokens * (d_c + d_r) * 2 + nq_tok * n_h * (d_c + d_r) * 2 + nq_tok * n_h * d_c * 4
+    scored = n_q * tokens - w.B * (n_q * (n_q - 1) // 2)     # rows seen, summed over tokens
+    flops = scored * 2 * n_h * ((d_c + d_r) + d_c)
     return tokens, byts, flops
 
 
@@ -158,7 +164,9 @@ def main():
     spare = args.warmup + args.steps + 2
     log(f"generating workload {name} ...")
     t0 = time.perf_counter()
-    w = I.layer(spare=spare) if name == "layer" else I.make(name)
+    w = (I.layer(spare=spare) if name == "layer"
+         else I.causal(n_q=args.n_q) if name == "causal" else I.make(name))
+    n_q = w.n_q
     log(f"  done in {time.perf_counter() - t0:.1f}s: B={w.B} total_rows={w.total_rows}")
     d = w.dims
     layer = name == "layer"
@@ -183,15 +191,27 @@ def main():
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
 
     B, n_h = w.B, d["n_h"]
+    BQ = B * n_q   # query tokens
     hint = int(w.total_rows) + (B if layer else 0)
-    q_lat = torch.empty(B, n_h, d["d_c"], dtype=torch.bfloat16, device="cuda")
-    q_pe = torch.empty(B, n_h, d["d_r"], dtype=torch.bfloat16, device="cuda")
-    o_lat = torch.empty(B, n_h, d["d_c"], dtype=torch.float32, device="cuda")
-    lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
-    o = torch.empty(B, n_h, d["d_v"], dtype=torch.float32, device="cuda")
+    q_lat = torch.empty(BQ, n_h, d["d_c"], dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(BQ, n_h, d["d_r"], dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty(BQ, n_h, d["d_c"], dtype=torch.float32, device="cuda")
+    lse = torch.empty(BQ, n_h, dtype=torch.float32, device="cuda")
+    o = torch.empty(BQ, n_h, d["d_v"], dtype=torch.float32, device="cuda")
+    # causal: token i of sequence b sits at position lens[b] - n_q + i
+    tok_pos = torch.from_numpy((np.repeat(w.lens.astype(np.int64), n_q) - n_q
+                                + np.tile(np.arange(n_q), B)).astype(np.int32)).cuda()
     u = torch.empty(B, d["d_model"], dtype=torch.float32, device="cuda") if layer else None
     pos = [s["lens"].clone() for s in sets]
-    ws_dec = torch.empty(L.decode_attn_workspace(dims, B, hint), dtype=torch.uint8, device="cuda")
+    ws_dec = torch.empty(L.decode_attn_causal_workspace(dims, B, n_q, hint), dtype=torch.uint8, device="cuda")
+
+    def attend(s):
+        if n_q > 1:
+            L.decode_attn_causal(dims, n_q, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
+                                 total_rows_hint=hint, ws=ws_dec)
+        else:
+            L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
+                          total_rows_hint=hint, ws=ws_dec)
     lib = L.lib()
     import ctypes
     ws_abs = torch.empty(max(1, lib.mla_absorb_q_workspace(ctypes.byref(dims), B, int(layer))),
@@ -211,9 +231,8 @@ def main():
             L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
                            W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
         else:
-            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["lens"], q=s["q"])
-        L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
-                      total_rows_hint=hint, ws=ws_dec)
+            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], tok_pos if n_q > 1 else s["lens"], q=s["q"])
+        attend(s)
         if layer:
             L.project_out(dims, o_lat, s["W_UV"], o=o, u=u, W_O=s["W_O"], ws=ws_prj)
         else:
@@ -257,8 +276,7 @@ def main():
         s = sets[(args.warmup + i) % copies]
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        L.decode_attn(dims, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
-                      total_rows_hint=hint, ws=ws_dec)
+        attend(s)
         b.record()
         ev.append((a, b))
     torch.cuda.synchronize()
@@ -284,7 +302,8 @@ def main():
     wl = {"uniform": f"uniform B={w.B} T={int(w.lens[0])}",
           "ragged": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows}",
           "long": f"long-context B={w.B} T={int(w.lens[0])}",
-          "layer": f"full layer step B={w.B} prior T~U[512,8192] sum={w.total_rows}"}[name]
+          "layer": f"full layer step B={w.B} prior T~U[512,8192] sum={w.total_rows}",
+          "causal": f"causal B={w.B} T={int(w.lens[0])} n_q={n_q} new tokens per sequence"}[name]
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -301,18 +320,20 @@ def main():
         "config": {"workload": wl + " (DeepSeek-V3 dims n_h=128 d_c=512 d_R=64)",
                    "B": w.B, "cache_tokens": tokens,
                    "step": "absorb_q+append+decode_attn+project_out(o,u)" if layer
+                   else "absorb_q+decode_attn_causal+project_out(o)" if n_q > 1
                    else "absorb_q+decode_attn+project_out(o)",
                    "input_copies_rotated": copies,
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
-                     "kernel": "mla_decode_attn (split attention with length scan + combine)",
+                     "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn")
+                     + " (split attention with length scan + combine)",
                      "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
                      "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,
                      "mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and n_q == 1:
         log(f"oracle baseline on the host ({args.cpu_seconds:.0f} s budget) ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -89,6 +89,7 @@ class Workload:
     h_t: Optional[np.ndarray] = None       # [B, d_model]
     kv_raw: Optional[np.ndarray] = None    # tiny: [B, T, d_c + d_R] un-rotated rows
     seed: int = 0
+    n_q: int = 1                 # query tokens per sequence (q_C, q_R hold B n_q rows)
 
     @property
     def row_elems(self) -> int:
@@ -186,6 +187,22 @@ def long_context(seed: int = 0, B: int = 8, T: int = 131072) -> Workload:
     return attention_only("long", B, np.full(B, T, dtype=np.int32), rng, seed)
 
 
+def causal(seed: int = 0, B: int = 16, T: int = 4096, n_q: int = 4) -> Workload:
+    """Several new tokens per sequence: the uniform cache, whose last n_q rows
+    are the step's tokens, and queries for B n_q tokens (q_C [B n_q, n_h, d_h],
+    token i of sequence b in row b n_q + i, at position T - n_q + i)."""
+    d = dict(V3_DIMS)
+    rng = np.random.default_rng(seed)
+    lens = np.full(B, T, dtype=np.int32)
+    offsets, cache = _cache(rng, lens, lens.astype(np.int64), d["d_c"], d["d_r"], "bf16")
+    q_C = bf16_bits(_normal(rng, (B * n_q, d["n_h"], d["d_h"]), 1.0))
+    q_R = bf16_bits(_normal(rng, (B * n_q, d["n_h"], d["d_r"]), 1.0))
+    W_UK = bf16_bits(_normal(rng, (d["n_h"], d["d_h"], d["d_c"]), d["d_c"] ** -0.5))
+    W_UV = bf16_bits(_normal(rng, (d["n_h"], d["d_v"], d["d_c"]), d["d_c"] ** -0.5))
+    return Workload("causal", "bf16", d, B, lens, offsets, cache, q_C=q_C, q_R=q_R,
+                    W=dict(W_UK=W_UK, W_UV=W_UV), seed=seed, n_q=n_q)
+
+
 def layer(seed: int = 0, B: int = 128, lo: int = 512, hi: int = 8192, spare: int = 1) -> Workload:
     """Full decode-layer step: prior cache, weights and h_t; ``spare`` free rows per sequence."""
     d = dict(V3_DIMS)
@@ -212,6 +229,7 @@ WORKLOADS = {
     "ragged": ragged,
     "long": long_context,
     "layer": layer,
+    "causal": causal,
 }
 
 

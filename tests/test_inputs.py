@@ -31,6 +31,9 @@ def test_workloads_deterministic_and_laid_out():
     assert L.W["W_UQ"].shape == (128 * 192, 1536) and L.W["W_O"].shape == (7168, 16384)
     t = I.tiny()
     assert t.dtype == "f32" and t.kv_raw.shape == (1, 64, 40) and t.q_C.shape == (1, 4, 16)
+    c = I.causal(B=3, T=10, n_q=4)
+    assert c.n_q == 4 and c.q_C.shape == (12, 128, 128) and c.q_R.shape == (12, 128, 64)
+    assert c.cache.shape == (30, 576) and list(c.lens) == [10, 10, 10]
 
 
 def test_weight_std_is_fan_in_inverse_sqrt():
