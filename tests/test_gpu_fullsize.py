@@ -2,7 +2,8 @@
 benchmark times (same seeded workloads, total-rows hint, split kernel and
 combine), on sampled (sequence, head) outputs that the fp64 oracle computes
 one by one: uniform B=16 T=4096, ragged B=64 T in [1024, 32768], long context
-B=8 T=131072, and the full layer step at B=128."""
+B=8 T=131072, the full layer step at B=128, and the several-new-tokens step
+(B=16, T=4096, n_q=4)."""
 
 import numpy as np
 import pytest
@@ -82,3 +83,43 @@ def test_full_size_layer_step():
         compare(host_f64(lse[b]), rb["lse"], f"layer b={b} lse", max_abs=2e-2, mean_abs=2e-3,
                 norm_max=1e-2, norm_mean=2e-3)
         compare(host_f64(u[b]), rb["u"], f"layer b={b} u")
+
+
+def test_full_size_causal_step():
+    """Several new tokens, as bench.py --workload causal times them: B=16,
+    T=4096, n_q=4; absorb (token i of sequence b at position T - 4 + i),
+    mla_decode_attn_causal, up-projection.  Sampled (sequence, token, heads)
+    against the oracle's explicit route over each token's prefix."""
+    w = I.causal()
+    n_q, B, T = w.n_q, w.B, int(w.lens[0])
+    d = dims_of(w)
+    say(f"full size causal: B={B} T={T} n_q={n_q}")
+    u = Uploaded(w)
+    BQ = B * n_q
+    q_lat = torch.empty(BQ, 128, 512, dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(BQ, 128, 64, dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty(BQ, 128, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(BQ, 128, dtype=torch.float32, device="cuda")
+    o = torch.empty(BQ, 128, 128, dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = torch.tensor([T - n_q + i for _ in range(B) for i in range(n_q)], dtype=torch.int32, device="cuda")
+    L.absorb_q(d, q_lat, q_pe, u.W["W_UK"], pos, q=u.q)
+    L.decode_attn_causal(d, n_q, q_lat, q_pe, u.cache, u.offsets, u.lens, o_lat, lse,
+                         total_rows_hint=w.total_rows, err_flag=err)
+    L.project_out(d, o_lat, u.W["W_UV"], o=o)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    o, o_lat, lse = host_f64(o), host_f64(o_lat), host_f64(lse)
+    assert np.all(np.isfinite(o_lat)) and np.all(np.isfinite(lse))
+    W_UK, W_UV = w.f64(w.W["W_UK"]), w.f64(w.W["W_UV"])
+    scale = O.scale_for(128, 64)
+    for b, i, heads in ((0, 0, [0, 77]), (0, 3, [5]), (9, 1, [31, 100]), (15, 2, [127])):
+        n = T - n_q + i + 1
+        rows = w.f64(w.seq_rows(b))[:n]
+        t = b * n_q + i
+        ro, ro_lat, rlse = O.decode_explicit(w.f64(w.q_C[t])[heads], w.f64(w.q_R[t])[heads], T - n_q + i,
+                                             rows[:, :512], rows[:, 512:], W_UK[heads], W_UV[heads], scale)
+        tag = f"causal b={b} token={i} rows={n} heads={heads}"
+        compare(o_lat[t][heads], ro_lat, f"{tag} o_lat")
+        compare(o[t][heads], ro, f"{tag} o")
+        compare(lse[t][heads], rlse, f"{tag} lse", max_abs=2e-2, mean_abs=2e-3, norm_max=1e-2, norm_mean=2e-3)
