@@ -42,8 +42,11 @@ Readings of points the pages leave open:
   >= every cached row, so the mask passes everything; with n_q new tokens
   (latent_attention_causal) they are the last n_q cached rows and token i
   sees rows 0 .. T - n_q + i;
-* the latent ``norm(...)`` of the reference code path is not applied (its type
-  and epsilon are not stated; c^KV = W^DKV h_t is the equation's definition);
+* the latent ``norm(...)`` of the inference code is not applied by default
+  (c^KV = W^DKV h_t is the equation's definition); when asked for, it is a
+  root-mean-square norm with a per-feature weight and eps = 1e-6 (the pages
+  name neither its kind nor its epsilon), on c^KV before caching and on c^Q
+  before its up-projection;
 * weights are [out, in] row-major: W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c],
   W_UQ rows head-major with [d_h content | d_R rope] per head, W_O input index
   h * d_v + v ("flatten head").
@@ -68,6 +71,7 @@ __all__ = [
     "latent_attention",
     "latent_attention_causal",
     "append_rows",
+    "rms_norm",
     "query_path",
     "project_out",
     "layer_step",
@@ -217,26 +221,46 @@ def latent_attention_causal(q_lat, q_pe, c, k_rot, scale):
 # [128 content | 64 rope]; kv_and_pe split into latent and k_pe; RoPE(k_pe);
 # write at index start_pos).
 # ---------------------------------------------------------------------------
-def append_rows(x, W_DKV, W_KR, pos, base=10000.0):
+def append_rows(x, W_DKV, W_KR, pos, base=10000.0, kv_norm_w=None, eps=1e-6):
     """Cache rows for new tokens: (c_new [n, d_c], k_rot [n, d_R]).
 
     x [n, d_model] are the new tokens' hidden states, pos [n] their positions.
+    With ``kv_norm_w`` the latent is normalised before it is cached (rms_norm).
     """
     x = np.asarray(x, np.float64)
     c_new = x @ np.asarray(W_DKV, np.float64).T
+    if kv_norm_w is not None:
+        c_new = rms_norm(c_new, kv_norm_w, eps)
     k_raw = x @ np.asarray(W_KR, np.float64).T
     return c_new, rope(k_raw, np.asarray(pos), base)
 
 
-def query_path(h, W_DQ, W_UQ, n_h, d_h, d_r):
+# ---------------------------------------------------------------------------
+# The latent norms.  [MLA-struct], inference code: the compressed latent is
+# passed through a norm before it is cached (and the compressed query before
+# its up-projection); the pages name neither the kind of norm nor its epsilon.
+# Reading: root-mean-square norm over the latent's features with a learned
+# per-feature weight, y = x / sqrt(mean(x^2) + eps) * w, eps = 1e-6.
+# ---------------------------------------------------------------------------
+def rms_norm(x, w, eps=1e-6):
+    """Row-wise x / sqrt(mean(x^2) + eps) * w over the last axis."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, np.float64)
+
+
+def query_path(h, W_DQ, W_UQ, n_h, d_h, d_r, q_norm_w=None, eps=1e-6):
     """q_C [n, n_h, d_h] and q_R [n, n_h, d_R] (un-rotated) from hidden states h [n, d].
 
     With ``W_DQ`` None the query is projected directly (q = W_UQ h), as in a
-    configuration without query compression.
+    configuration without query compression.  With ``q_norm_w`` the compressed
+    query c^Q is normalised (rms_norm) before the up-projection.
     """
     c_Q = np.asarray(h, np.float64)
     if W_DQ is not None:
         c_Q = c_Q @ np.asarray(W_DQ, np.float64).T
+        if q_norm_w is not None:
+            c_Q = rms_norm(c_Q, q_norm_w, eps)
     q = (c_Q @ np.asarray(W_UQ, np.float64).T).reshape(len(c_Q), n_h, d_h + d_r)
     return q[..., :d_h], q[..., d_h:]
 

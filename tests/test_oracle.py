@@ -472,6 +472,42 @@ def test_layer_step_consistent_and_shapes(golden_dir):
 # A planted mistake must be caught (mutations applied to a copy of the oracle
 # on the CPU; the suite above must reject each of them).
 # ---------------------------------------------------------------------------
+# The latent norms (root-mean-square reading).
+def test_rms_norm_matches_torch_and_closed_forms():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((5, 512)) * 3.0
+    w = 1.0 + 0.1 * rng.standard_normal(512)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), torch.from_numpy(w), eps=1e-6)
+    assert rel_err(O.rms_norm(x, w, 1e-6), ref.numpy()) < 1e-12
+    # a constant row a: every output is a / sqrt(a^2 + eps) times its weight
+    a = 0.37
+    y = O.rms_norm(np.full((1, 8), a), np.arange(1.0, 9.0), 1e-6)
+    assert rel_err(y[0], a / math.sqrt(a * a + 1e-6) * np.arange(1.0, 9.0)) < RTOL
+    # unit weight, eps 0: the output's root mean square is exactly 1 and
+    # rescaling the input changes nothing
+    z = O.rms_norm(x, np.ones(512), 0.0)
+    assert np.allclose(np.sqrt(np.mean(z * z, axis=1)), 1.0, rtol=1e-14, atol=0)
+    assert rel_err(O.rms_norm(5.5 * x, np.ones(512), 0.0), z) < RTOL
+
+
+def test_norms_sit_on_the_latents():
+    # the kv norm acts on c^KV only (k^R untouched); the query norm on c^Q
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((3, 40))
+    W_DKV, W_KR = rng.standard_normal((12, 40)), rng.standard_normal((6, 40))
+    g = 1.0 + 0.2 * rng.standard_normal(12)
+    c0, k0 = O.append_rows(x, W_DKV, W_KR, [4, 5, 6])
+    c1, k1 = O.append_rows(x, W_DKV, W_KR, [4, 5, 6], kv_norm_w=g)
+    assert rel_err(k1, k0) == 0.0
+    assert rel_err(c1, O.rms_norm(x @ W_DKV.T, g)) < RTOL
+    W_DQ, W_UQ = rng.standard_normal((10, 40)), rng.standard_normal((2 * 7, 10))
+    gq = 1.0 + 0.2 * rng.standard_normal(10)
+    qc, qr = O.query_path(x, W_DQ, W_UQ, 2, 4, 3, q_norm_w=gq)
+    q = O.rms_norm(x @ W_DQ.T, gq) @ W_UQ.T
+    assert rel_err(np.concatenate([qc, qr], -1).reshape(3, -1), q) < RTOL
+
+
+# ---------------------------------------------------------------------------
 # Several new tokens per step (causal mask).
 def _causal_case(rng, T, n_q, n_h=3, d_c=12, d_r=6):
     return (rng.standard_normal((n_q, n_h, d_c)), rng.standard_normal((n_q, n_h, d_r)),
