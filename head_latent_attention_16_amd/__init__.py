@@ -8,7 +8,7 @@ missing.  ``inputs`` (seeded synthetic workloads) imports nothing from here.
 
 __all__ = ["absorb_q", "append_cache", "decode_attn", "decode_attn_causal", "project_out",
            "cache_row_bytes", "decode_attn_workspace", "decode_attn_causal_workspace", "Dims",
-           "MLAError", "lib"]
+           "MLAError", "lib", "absorb_q_normed", "append_cache_normed"]
 
 
 def __getattr__(name):

@@ -28,6 +28,7 @@ DT_BF16, DT_F32 = 0, 1
 EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_append_cache_workspace", "mla_decode_attn", "mla_decode_attn_workspace",
            "mla_decode_attn_causal", "mla_decode_attn_causal_workspace",
+           "mla_absorb_q_normed", "mla_append_cache_normed",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
            "mla_status_string", "mla_abi_version")
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
     sig = {
         "mla_absorb_q": ([D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "mla_absorb_q_workspace": ([D, i32, i32], sz),
+        "mla_absorb_q_normed": ([D, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "mla_append_cache_normed": ([D, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz,
+                                     vp], i32),
         "mla_append_cache": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "mla_append_cache_workspace": ([D, i32, i32, i32], sz),
         "mla_decode_attn": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
@@ -271,3 +275,43 @@ def decode_attn_causal(dims: Dims, n_q: int, q_lat, q_pe, cache, offsets, lens, 
                                   _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse),
                                   _ptr(err_flag), w, wn, _stream(stream))
     _check("mla_decode_attn_causal", st)
+
+
+def absorb_q_normed(dims: Dims, q_lat, q_pe, W_UK, pos, h_t, W_DQ, q_norm_w, W_UQ, eps=1e-6,
+                    ws=None, stream=None):
+    """absorb_q from h_t with c^Q normalised (root-mean-square, weight q_norm_w)
+    between W_DQ and W_UQ."""
+    L = lib()
+    B = q_lat.shape[0]
+    dt = dims.torch_dtype
+    _dev(q_lat, q_pe, W_UK, pos, h_t, W_DQ, q_norm_w, W_UQ)
+    _need(q_lat, B * dims.n_h * dims.d_c, dt, "q_lat")
+    _need(q_pe, B * dims.n_h * dims.d_r, dt, "q_pe")
+    _need(pos, B, torch.int32, "pos")
+    _need(h_t, B * dims.d_model, dt, "h_t")
+    _need(q_norm_w, dims.d_q, dt, "q_norm_w")
+    ws = _workspace(int(L.mla_absorb_q_workspace(ctypes.byref(dims), B, 1)), ws, q_lat.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_absorb_q_normed(ctypes.byref(dims), B, _ptr(h_t), _ptr(W_DQ), _ptr(q_norm_w), float(eps),
+                               _ptr(W_UQ), _ptr(W_UK), _ptr(pos), _ptr(q_lat), _ptr(q_pe), w, wn,
+                               _stream(stream))
+    _check("mla_absorb_q_normed", st)
+
+
+def append_cache_normed(dims: Dims, cache, offsets, lens, n_new: int, h_t, W_DKV, kv_norm_w, W_KR,
+                        eps=1e-6, err_flag=None, ws=None, stream=None):
+    """append_cache from h_t with c^KV normalised (root-mean-square, weight
+    kv_norm_w) before it is written."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(cache, offsets, lens, h_t, W_DKV, kv_norm_w, W_KR, err_flag)
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(h_t, B * n_new * dims.d_model, dt, "h_t")
+    _need(kv_norm_w, dims.d_c, dt, "kv_norm_w")
+    ws = _workspace(int(L.mla_append_cache_workspace(ctypes.byref(dims), B, n_new, 1)), ws, cache.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_append_cache_normed(ctypes.byref(dims), B, n_new, _ptr(h_t), _ptr(W_DKV), _ptr(kv_norm_w),
+                                   float(eps), _ptr(W_KR), _ptr(cache), _ptr(offsets), _ptr(lens),
+                                   _ptr(err_flag), w, wn, _stream(stream))
+    _check("mla_append_cache_normed", st)

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
+
 #include <mutex>
 
 #include "../../include/mla.h"
@@ -219,9 +221,15 @@ size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hi
   return absorb_ws(s, B, from_hidden != 0);
 }
 
-mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
-                          const void* W_UQ, const void* q, const void* W_UK, const int32_t* pos,
-                          void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// q_norm_w != NULL: c^Q is normalised in place (root-mean-square, eps) between
+// the two query projections.
+mla_status_t absorb_common(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
+                           const void* q_norm_w, float eps, const void* W_UQ, const void* q,
+                           const void* W_UK, const int32_t* pos, void* q_lat, void* q_pe, void* ws,
+                           size_t ws_bytes, void* stream) {
   Shape s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
@@ -261,6 +269,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
     if (s.d_q > 0) {
       hipError_t e = linear(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, part, hs);
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
+      if (q_norm_w && launch_rmsnorm(s, cq, B, s.d_q, (size_t)s.d_q, q_norm_w, eps, hs) != hipSuccess)
+        return MLA_ERR_LAUNCH;
       x = cq;
       x_f32 = true;
       K = s.d_q;
@@ -274,6 +284,29 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
     return launched(launch_absorb_v3(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
   return launched(launch_absorb_generic(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
 }
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
+                          const void* W_UQ, const void* q, const void* W_UK, const int32_t* pos,
+                          void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream) {
+  return absorb_common(dims, B, h_t, W_DQ, nullptr, 0.f, W_UQ, q, W_UK, pos, q_lat, q_pe, ws, ws_bytes,
+                       stream);
+}
+
+mla_status_t mla_absorb_q_normed(const mla_dims_t* dims, int32_t B, const void* h_t, const void* W_DQ,
+                                 const void* q_norm_w, float eps, const void* W_UQ, const void* W_UK,
+                                 const int32_t* pos, void* q_lat, void* q_pe, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (!(eps >= 0.f) || !std::isfinite(eps) || s.d_q < 1) return MLA_ERR_SHAPE;
+  if (B > 0 && (!h_t || !W_DQ || !q_norm_w)) return MLA_ERR_NULL;
+  return absorb_common(dims, B, h_t, W_DQ, q_norm_w, eps, W_UQ, nullptr, W_UK, pos, q_lat, q_pe, ws,
+                       ws_bytes, stream);
+}
 
 size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_new,
                                   int32_t from_hidden) {
@@ -282,10 +315,15 @@ size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_n
   return append_ws(s, B, n_new, from_hidden != 0);
 }
 
-mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
-                              const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
-                              const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
-                              size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// kv_norm_w != NULL: the new latents c^KV are normalised in place
+// (root-mean-square, eps) before they are written.
+mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                           const void* W_DKV, const void* kv_norm_w, float eps, const void* W_KR,
+                           const void* kv_raw, void* cache, const int32_t* offsets, int32_t* lens,
+                           int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
@@ -314,12 +352,16 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
       // one [M, d_c + d_r] product: row i = [c_i | k_i]
       hipError_t e = launch_gemm_v3(M, (int)D, s.d_c, s.d_model, h_t, false, W_DKV, W_KR, kc, part, hs);
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
+      if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, D, kv_norm_w, eps, hs) != hipSuccess)
+        return MLA_ERR_LAUNCH;
       return launched(launch_append_generic(s, B, n_new, kc, D, kc + s.d_c, D, true, cache, offsets,
                                             lens, err_flag, hs));
     }
     float* kr = kc + (size_t)M * s.d_c;
     hipError_t e = linear(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
+    if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, (size_t)s.d_c, kv_norm_w, eps, hs) != hipSuccess)
+      return MLA_ERR_LAUNCH;
     e = linear(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
     return launched(launch_append_generic(s, B, n_new, kc, (size_t)s.d_c, kr, (size_t)s.d_r, true,
@@ -329,6 +371,31 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
   // kv_raw is in the storage type: fp32 rows are read as fp32, bf16 rows as bf16.
   return launched(launch_append_generic(s, B, n_new, raw, D, raw + (size_t)s.d_c * elem_bytes(s), D,
                                         !s.bf16, cache, offsets, lens, err_flag, hs));
+}
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                              const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
+                              const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache, offsets, lens,
+                       err_flag, ws, ws_bytes, stream);
+}
+
+mla_status_t mla_append_cache_normed(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                                     const void* W_DKV, const void* kv_norm_w, float eps,
+                                     const void* W_KR, void* cache, const int32_t* offsets,
+                                     int32_t* lens, int32_t* err_flag, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return MLA_ERR_SHAPE;
+  if (B > 0 && n_new > 0 && (!h_t || !kv_norm_w)) return MLA_ERR_NULL;
+  return append_common(dims, B, n_new, h_t, W_DKV, kv_norm_w, eps, W_KR, nullptr, cache, offsets, lens,
+                       err_flag, ws, ws_bytes, stream);
 }
 
 size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint) {

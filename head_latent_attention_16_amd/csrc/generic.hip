@@ -274,6 +274,36 @@ hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_l
   return hipGetLastError();
 }
 
+// Root-mean-square norm of the first `cols` fp32 values of each row (row
+// stride `stride`), in place: x / sqrt(mean(x^2) + eps) * w, w in the storage type.
+// One block of 256 per row: a sum of squares per lane, wave sums, four waves.
+template <typename T>
+__global__ void __launch_bounds__(256) k_rmsnorm(float* __restrict__ x, int cols, size_t stride,
+                                                 const T* __restrict__ w, float eps) {
+  __shared__ float red[4];
+  float* row = x + (size_t)blockIdx.x * stride;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    const float v = row[c];
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)cols + eps);
+  for (int c = threadIdx.x; c < cols; c += 256) row[c] = row[c] * r * ld(w, c);
+}
+
+hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
+                          float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (s.bf16)
+    k_rmsnorm<__bf16><<<rows, 256, 0, st>>>(x, cols, ld, (const __bf16*)w, eps);
+  else
+    k_rmsnorm<float><<<rows, 256, 0, st>>>(x, cols, ld, (const float*)w, eps);
+  return hipGetLastError();
+}
+
 hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
                              hipStream_t st) {
   dim3 grid((s.d_v + 3) / 4, s.n_h, B);

@@ -36,6 +36,9 @@ hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c
 hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
                                  const void* cache, const int32_t* offsets, const int32_t* lens,
                                  float* o_lat, float* lse, int32_t* err_flag, hipStream_t st);
+// In place on fp32 rows (stride ld): x[:cols] / sqrt(mean(x[:cols]^2) + eps) * w.
+hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
+                          float eps, hipStream_t st);
 // o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 out)
 hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
                              hipStream_t st);

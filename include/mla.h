@@ -109,6 +109,18 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
                           void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream);
 size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hidden);
 
+/* mla_absorb_q from h_t with the query-side latent norm of the inference code
+ * ("MLA模型结构详解", the compressed query passes through a norm before its
+ * up-projection; the page names neither its kind nor its epsilon):
+ *   c^Q = W_DQ h_t,  c^Q <- c^Q / sqrt(mean(c^Q^2) + eps) * q_norm_w,  q = W_UQ c^Q,
+ * then as mla_absorb_q.  q_norm_w [d_q] in dims->dtype; the norm runs in fp32
+ * on the fp32 c^Q.  Needs d_q >= 1, h_t, W_DQ, q_norm_w (MLA_ERR_NULL), and a
+ * finite eps >= 0 (MLA_ERR_SHAPE).  ws: mla_absorb_q_workspace(dims, B, 1). */
+mla_status_t mla_absorb_q_normed(const mla_dims_t* dims, int32_t B, const void* h_t,
+                                 const void* W_DQ, const void* q_norm_w, float eps,
+                                 const void* W_UQ, const void* W_UK, const int32_t* pos,
+                                 void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream);
+
 /* Append n_new tokens per sequence ("MLA模型结构详解", worked example steps 2-3:
  * kv_and_pe = wkv_a(x) split into the latent and k_pe, RoPE(k_pe), written at
  * index start_pos; c^KV = W^DKV h_t, k^R = RoPE(W^KR h_t)).
@@ -127,6 +139,20 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
                               size_t ws_bytes, void* stream);
 size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_new,
                                   int32_t from_hidden);
+
+/* mla_append_cache from h_t with the latent norm of the inference code
+ * ("MLA模型结构详解": the compressed latent passes through a norm before it is
+ * cached; kind and epsilon unstated there):
+ *   c^KV = W_DKV x,  c^KV <- c^KV / sqrt(mean(c^KV^2) + eps) * kv_norm_w,
+ * k^R = RoPE(W_KR x) as in mla_append_cache (not normalised).  kv_norm_w [d_c]
+ * in dims->dtype; the norm runs in fp32 before the row is rounded to the
+ * storage type.  Needs h_t, W_DKV, W_KR, kv_norm_w (MLA_ERR_NULL) and a finite
+ * eps >= 0 (MLA_ERR_SHAPE).  ws: mla_append_cache_workspace(dims, B, n_new, 1). */
+mla_status_t mla_append_cache_normed(const mla_dims_t* dims, int32_t B, int32_t n_new,
+                                     const void* h_t, const void* W_DKV, const void* kv_norm_w,
+                                     float eps, const void* W_KR, void* cache,
+                                     const int32_t* offsets, int32_t* lens, int32_t* err_flag,
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /* Latent-space attention of one query per sequence ("MLA模型结构详解", worked
  * example steps 4-5: score = (score_C + score_R) x scale, softmax, z = A . kv_cache;

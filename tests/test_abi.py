@@ -149,3 +149,26 @@ def test_causal_validation_and_workspace(lib):
     four = lib.mla_decode_attn_causal_workspace(ctypes.byref(d), 16, 4, 65536)
     assert four >= lib.mla_decode_attn_workspace(ctypes.byref(d), 64, 4 * 65536) > 0
     assert lib.mla_decode_attn_causal_workspace(ctypes.byref(d), 16, 0, 65536) == 0
+
+
+def test_normed_validation(lib):
+    d = v3()
+    f = ctypes.c_float
+    ab = lambda **kw: lib.mla_absorb_q_normed(ctypes.byref(kw.pop("dims", d)), 2, kw.pop("h_t", P),  # noqa: E731
+                                             kw.pop("W_DQ", P), kw.pop("g", P), f(kw.pop("eps", 1e-6)), P, P, P,
+                                             P, P, kw.pop("ws", P), 1 << 40, None)
+    assert ab(g=None) == 1
+    assert ab(h_t=None) == 1
+    assert ab(W_DQ=None) == 1
+    assert ab(eps=-1.0) == 2
+    assert ab(eps=float("nan")) == 2
+    assert ab(dims=v3(d_q=0)) == 2                       # no compressed query to normalise
+    assert ab() == 6
+    ap = lambda **kw: lib.mla_append_cache_normed(ctypes.byref(d), 2, kw.pop("n_new", 1), kw.pop("h_t", P), P,  # noqa: E731
+                                                 kw.pop("g", P), f(kw.pop("eps", 1e-6)), P, P, P, P, None,
+                                                 P, 1 << 40, None)
+    assert ap(g=None) == 1
+    assert ap(h_t=None) == 1
+    assert ap(eps=float("inf")) == 2
+    assert ap(n_new=0) == 0
+    assert ap() == 6
