@@ -6,7 +6,8 @@ A step is one pass of the decode hot path over one batch:
   attention-only workloads (uniform, ragged, long):
       mla_absorb_q (q given) -> mla_decode_attn -> mla_project_out (o)
   layer workload: mla_absorb_q (from h_t) -> mla_append_cache (from h_t)
-      -> mla_decode_attn -> mla_project_out (o and u)
+      -> mla_decode_attn -> mla_project_out (o and u); with --norms the
+      _normed variants of the first two (latent norms on c^Q and c^KV)
   causal workload (--n-q new tokens per sequence, the cache's last rows):
       mla_absorb_q (B n_q queries) -> mla_decode_attn_causal -> mla_project_out (o)
 Inputs are seeded synthetic tensors of the DeepSeek-V3 shapes, resident in
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="uniform", choices=["uniform", "ragged", "long", "layer", "causal"])
     p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
+    p.add_argument("--norms", action="store_true",
+                   help="layer workload: root-mean-square latent norms on c^Q and c^KV")
     p.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -226,10 +229,16 @@ def main():
         s = sets[c]
         if layer:
             pos[c].copy_(s["lens"])   # query position = current length
-            L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[c], h_t=s["h_t"], W_DQ=s["W_DQ"],
-                       W_UQ=s["W_UQ"], ws=ws_abs)
-            L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
-                           W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
+            if args.norms:
+                L.absorb_q_normed(dims, q_lat, q_pe, s["W_UK"], pos[c], s["h_t"], s["W_DQ"], s["q_norm_w"],
+                                  s["W_UQ"], ws=ws_abs)
+                L.append_cache_normed(dims, s["cache"], s["offsets"], s["lens"], 1, s["h_t"], s["W_DKV"],
+                                      s["kv_norm_w"], s["W_KR"], ws=ws_app)
+            else:
+                L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[c], h_t=s["h_t"], W_DQ=s["W_DQ"],
+                           W_UQ=s["W_UQ"], ws=ws_abs)
+                L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
+                               W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
         else:
             L.absorb_q(dims, q_lat, q_pe, s["W_UK"], tok_pos if n_q > 1 else s["lens"], q=s["q"])
         attend(s)
@@ -319,7 +328,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl + " (DeepSeek-V3 dims n_h=128 d_c=512 d_R=64)",
                    "B": w.B, "cache_tokens": tokens,
-                   "step": "absorb_q+append+decode_attn+project_out(o,u)" if layer
+                   "step": ("absorb_q_normed+append_normed+decode_attn+project_out(o,u)" if args.norms
+                            else "absorb_q+append+decode_attn+project_out(o,u)") if layer
                    else "absorb_q+decode_attn_causal+project_out(o)" if n_q > 1
                    else "absorb_q+decode_attn+project_out(o)",
                    "input_copies_rotated": copies,

@@ -220,6 +220,10 @@ def layer(seed: int = 0, B: int = 128, lo: int = 512, hi: int = 8192, spare: int
     W["W_UV"] = bf16_bits(_normal(rng, (n_h, d_v, d_c), d_c ** -0.5))
     W["W_O"] = bf16_bits(_normal(rng, (dm, n_h * d_v), (n_h * d_v) ** -0.5))
     h_t = bf16_bits(_normal(rng, (B, dm), 1.0))
+    # weights of the optional latent norms, 1 + N(0, 0.1^2) per feature (drawn
+    # last, so that every other input is the same with or without them)
+    W["q_norm_w"] = bf16_bits(1.0 + _normal(rng, (dq,), 0.1))
+    W["kv_norm_w"] = bf16_bits(1.0 + _normal(rng, (d_c,), 0.1))
     return Workload("layer", "bf16", d, B, lens, offsets, cache, W=W, h_t=h_t, seed=seed)
 
 
