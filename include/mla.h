@@ -52,7 +52,9 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+/* 2: adds mla_decode_attn_causal, mla_absorb_q_normed, mla_append_cache_normed;
+ * the decode entry points reject more than 65535 query tokens up front. */
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,

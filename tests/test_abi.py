@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for st in range(7):
         s = lib.mla_status_string(st)
         assert isinstance(s, bytes) and len(s) > 0
