@@ -144,7 +144,7 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
