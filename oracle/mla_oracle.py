@@ -279,14 +279,15 @@ def project_out(o_lat, W_UV, W_O=None):
     return o, u
 
 
-def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None):
+def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None, norms=False, eps=1e-6):
     """One full MLA decode layer step for selected sequences, explicit route.
 
     h_t [B, d_model]; W: dict with W_DQ, W_UQ, W_DKV, W_KR, W_UK, W_UV, W_O;
     prior_c[b] [T_b, d_c], prior_k[b] [T_b, d_R] (rotated).  The new token of
     sequence b sits at position t_b = T_b: its row is appended at that index,
     and the query uses the same position ([MLA-struct], worked example step 3:
-    write at start_pos, visible length start_pos + 1).
+    write at start_pos, visible length start_pos + 1).  With ``norms`` the
+    latent norms (rms_norm with W["q_norm_w"], W["kv_norm_w"]) are applied.
     Returns dict of per-sequence results keyed by b.
     """
     n_h, d_h, d_r = dims["n_h"], dims["d_h"], dims["d_r"]
@@ -295,8 +296,10 @@ def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None):
     for b in seqs:
         x = np.asarray(h_t[b:b + 1], np.float64)
         t = len(prior_c[b])
-        q_C, q_R = query_path(x, W["W_DQ"], W["W_UQ"], n_h, d_h, d_r)
-        c_new, k_new = append_rows(x, W["W_DKV"], W["W_KR"], [t], base)
+        q_C, q_R = query_path(x, W["W_DQ"], W["W_UQ"], n_h, d_h, d_r,
+                              q_norm_w=W["q_norm_w"] if norms else None, eps=eps)
+        c_new, k_new = append_rows(x, W["W_DKV"], W["W_KR"], [t], base,
+                                   kv_norm_w=W["kv_norm_w"] if norms else None, eps=eps)
         c_all = np.concatenate([np.asarray(prior_c[b], np.float64), c_new])
         k_all = np.concatenate([np.asarray(prior_k[b], np.float64), k_new])
         o, o_lat, lse = decode_explicit(q_C[0], q_R[0], t, c_all, k_all,

@@ -44,24 +44,32 @@ def test_full_size_attention(name):
         compare(lse[b][heads], rlse, f"{tag} lse", max_abs=2e-2, mean_abs=2e-3, norm_max=1e-2, norm_mean=2e-3)
 
 
-def test_full_size_layer_step():
+@pytest.mark.parametrize("norms", [False, True])
+def test_full_size_layer_step(norms):
     """B=128, prior T in [512, 8192]: query path from h_t, append, attention,
-    up-projection and output projection; sequences 0, 64 and 127 checked."""
+    up-projection and output projection (with norms: the latent norms on c^Q
+    and c^KV, as bench.py --workload layer --norms); sequences 0, 64 and 127
+    checked."""
     w = I.layer()
     check = [0, 64, 127]
     d = dims_of(w)
     dd = w.dims
     B = w.B
-    say(f"full size layer: B={B} prior rows={w.total_rows}")
+    say(f"full size layer: B={B} prior rows={w.total_rows} norms={norms}")
     cache, offsets, lens = dev(w.cache), dev(w.offsets), dev(w.lens)
     W = {k: dev(v) for k, v in w.W.items()}
     h_t = dev(w.h_t)
     pos = lens.clone()
     q_lat = torch.empty(B, dd["n_h"], dd["d_c"], dtype=torch.bfloat16, device="cuda")
     q_pe = torch.empty(B, dd["n_h"], dd["d_r"], dtype=torch.bfloat16, device="cuda")
-    L.absorb_q(d, q_lat, q_pe, W["W_UK"], pos, h_t=h_t, W_DQ=W["W_DQ"], W_UQ=W["W_UQ"])
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    L.append_cache(d, cache, offsets, lens, 1, h_t=h_t, W_DKV=W["W_DKV"], W_KR=W["W_KR"], err_flag=err)
+    if norms:
+        L.absorb_q_normed(d, q_lat, q_pe, W["W_UK"], pos, h_t, W["W_DQ"], W["q_norm_w"], W["W_UQ"])
+        L.append_cache_normed(d, cache, offsets, lens, 1, h_t, W["W_DKV"], W["kv_norm_w"], W["W_KR"],
+                              err_flag=err)
+    else:
+        L.absorb_q(d, q_lat, q_pe, W["W_UK"], pos, h_t=h_t, W_DQ=W["W_DQ"], W_UQ=W["W_UQ"])
+        L.append_cache(d, cache, offsets, lens, 1, h_t=h_t, W_DKV=W["W_DKV"], W_KR=W["W_KR"], err_flag=err)
     o_lat = torch.empty(B, dd["n_h"], dd["d_c"], dtype=torch.float32, device="cuda")
     lse = torch.empty(B, dd["n_h"], dtype=torch.float32, device="cuda")
     L.decode_attn(d, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
@@ -75,7 +83,8 @@ def test_full_size_layer_step():
     Wf = {k: w.f64(v) for k, v in w.W.items()}
     prior_c = {b: w.f64(w.seq_rows(b))[:, :dd["d_c"]] for b in check}
     prior_k = {b: w.f64(w.seq_rows(b))[:, dd["d_c"]:] for b in check}
-    ref = O.layer_step(w.f64(w.h_t), Wf, prior_c, prior_k, dd, O.scale_for(dd["d_h"], dd["d_r"]), seqs=check)
+    ref = O.layer_step(w.f64(w.h_t), Wf, prior_c, prior_k, dd, O.scale_for(dd["d_h"], dd["d_r"]), seqs=check,
+                       norms=norms)
     for b in check:
         rb = ref[b]
         compare(host_f64(o_lat[b]), rb["o_lat"], f"layer b={b} o_lat")
