@@ -1,6 +1,9 @@
 """Benchmark one MLA decode step on one MI355X through the C ABI.
 
-    python bench.py [--steps K] [--warmup W] [--workload uniform|ragged|long|layer|causal]
+    python bench.py [--steps K] [--warmup W] [--workload ragged|uniform|long|layer|causal]
+
+The default workload is the ragged batch (B=64, T uniform in [1024, 32768]),
+the largest attention-only workload that fits one GPU.
 
 A step is one pass of the decode hot path over one batch:
   attention-only workloads (uniform, ragged, long):
@@ -49,7 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="uniform", choices=["uniform", "ragged", "long", "layer", "causal"])
+    # default: the largest single-GPU attention workload (ragged, 1.29 GB of cache per step)
+    p.add_argument("--workload", default="ragged", choices=["uniform", "ragged", "long", "layer", "causal"])
     p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
     p.add_argument("--norms", action="store_true",
                    help="layer workload: root-mean-square latent norms on c^Q and c^KV")
@@ -105,9 +109,13 @@ def measured_traffic(workload):
 def cpu_baseline(w, budget_s):
     """Time the fp64 oracle (explicit route) on whole sequences until the budget is used."""
     import oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('architecture')})"
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     d = w.dims
@@ -135,7 +143,8 @@ def cpu_baseline(w, budget_s):
     dt = time.perf_counter() - t0
     per_token_heads = done_tokens / d["n_h"]        # cache-tokens with all heads processed
     return {"value": per_token_heads / dt, "unit": "cache-tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "blas": blas,
             "sample": f"fp64 explicit route, {heads_done} (sequence, head) pairs over "
                       f"{b} sequence(s) of the same workload in {dt:.1f} s; value = "
                       f"head-weighted cache tokens / s"}

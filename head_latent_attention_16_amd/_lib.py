@@ -9,7 +9,6 @@ kernels of the library; if the library is missing the calls raise.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -54,10 +53,6 @@ class Dims(ctypes.Structure):
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == DT_BF16 else torch.float32
-
-    @property
-    def scale(self) -> float:
-        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.d_h + self.d_r)
 
 
 _lib = None

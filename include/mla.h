@@ -25,8 +25,12 @@
  *   keeps no per-call state; it caches device properties per device only.
  * - ``stream`` is a hipStream_t (NULL = the null stream).  Every call only
  *   enqueues work on it and returns; there is no host synchronisation inside.
- * - Every call validates its arguments on the host first.  On any return other
- *   than MLA_OK nothing was enqueued and no output was touched.
+ * - Every call validates its arguments on the host first.  A return of
+ *   MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_WORKSPACE or
+ *   MLA_ERR_DEVICE means nothing was enqueued and no output was touched.
+ *   MLA_ERR_LAUNCH (the HIP runtime refused a launch) can come after earlier
+ *   kernels of the same call were already enqueued: scratch, and outputs
+ *   those kernels write, are then unspecified until the call succeeds.
  * - Element types follow ``dims->dtype``: with MLA_DT_BF16 every ``void*``
  *   tensor is bf16, with MLA_DT_F32 it is float32.  Outputs typed ``float*``
  *   are always float32.  Index arrays are int32.
@@ -111,9 +115,12 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* h_t, co
                           void* q_lat, void* q_pe, void* ws, size_t ws_bytes, void* stream);
 size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hidden);
 
-/* mla_absorb_q from h_t with the query-side latent norm of the inference code
- * ("MLA模型结构详解", the compressed query passes through a norm before its
- * up-projection; the page names neither its kind nor its epsilon):
+/* mla_absorb_q from h_t with a norm on the compressed query.  No page prints
+ * this norm: "MLA模型结构详解" (section "结合 DeepSeek 推理代码看 MLA" and
+ * worked example step 3) shows norm(kv_latent) on the latent side only.  It
+ * is a reading beyond the pages that completes a DeepSeek-V3-style query path
+ * with the same root-mean-square norm as the latent side (kind and epsilon
+ * are readings too):
  *   c^Q = W_DQ h_t,  c^Q <- c^Q / sqrt(mean(c^Q^2) + eps) * q_norm_w,  q = W_UQ c^Q,
  * then as mla_absorb_q.  q_norm_w [d_q] in dims->dtype; the norm runs in fp32
  * on the fp32 c^Q.  Needs d_q >= 1, h_t, W_DQ, q_norm_w (MLA_ERR_NULL), and a
@@ -143,8 +150,9 @@ size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_n
                                   int32_t from_hidden);
 
 /* mla_append_cache from h_t with the latent norm of the inference code
- * ("MLA模型结构详解": the compressed latent passes through a norm before it is
- * cached; kind and epsilon unstated there):
+ * ("MLA模型结构详解", section "结合 DeepSeek 推理代码看 MLA" and worked example
+ * step 3: cache(norm(kv_latent)); kind and epsilon unstated there, read as a
+ * root-mean-square norm):
  *   c^KV = W_DKV x,  c^KV <- c^KV / sqrt(mean(c^KV^2) + eps) * kv_norm_w,
  * k^R = RoPE(W_KR x) as in mla_append_cache (not normalised).  kv_norm_w [d_c]
  * in dims->dtype; the norm runs in fp32 before the row is rounded to the
@@ -167,8 +175,10 @@ mla_status_t mla_append_cache_normed(const mla_dims_t* dims, int32_t B, int32_t 
  * No mask: every cached row precedes the query.  lens[b] must be in
  * [1, offsets[b+1]-offsets[b]]; a sequence violating it gets NaN outputs and
  * MLA_DEVERR_LENS.  B <= 65535 (else MLA_ERR_SHAPE).  total_rows_hint (> 0) is
- * the expected sum of lens and only sizes the launch; results do not depend
- * on it.
+ * the expected sum of lens and only sizes the launch (the number of row
+ * ranges the batch is split into): any hint gives a correct result, but the
+ * split points, and with them the low-order bits of o_lat and lse, can change
+ * with it (within the same rounding bounds).
  * ws: at least mla_decode_attn_workspace(dims, B, total_rows_hint) bytes. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_lat,
                              const void* q_pe, const void* cache, const int32_t* offsets,
@@ -209,8 +219,11 @@ size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32
  *   u[b,:]   = W_O flatten(o[b])          W_O [d_model, n_h*d_v] (input index h*d_v + v),
  *                                         u [B, d_model] fp32
  * o or u may be NULL to skip storing it (W_O may be NULL when u is NULL).  With
- * bf16 weights the products run in bf16 with fp32 accumulation (o_lat and o are
- * rounded to bf16 as operands).
+ * bf16 weights the products run on bf16 matrix cores with fp32 accumulation;
+ * the fp32 activations (o_lat, and o for W_O) enter as two bf16 operands, the
+ * rounded value hi = bf16(x) and the remainder lo = bf16(x - hi), both
+ * multiplied by the weight, so the activation keeps about 16 significant
+ * bits.
  * ws: at least mla_project_out_workspace(dims, B, u != NULL) bytes. */
 mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_lat,
                              const void* W_UV, const void* W_O, float* o, float* u, void* ws,

@@ -45,8 +45,11 @@ Readings of points the pages leave open:
 * the latent ``norm(...)`` of the inference code is not applied by default
   (c^KV = W^DKV h_t is the equation's definition); when asked for, it is a
   root-mean-square norm with a per-feature weight and eps = 1e-6 (the pages
-  name neither its kind nor its epsilon), on c^KV before caching and on c^Q
-  before its up-projection;
+  name neither its kind nor its epsilon) on c^KV before caching, which is
+  where the pages print it.  The same norm on the compressed query c^Q
+  before its up-projection is a reading BEYOND the pages (no page prints a
+  norm on c^Q; it completes the query path of a DeepSeek-V3-style layer by
+  symmetry with the latent side) and is applied only when asked for;
 * weights are [out, in] row-major: W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c],
   W_UQ rows head-major with [d_h content | d_R rope] per head, W_O input index
   h * d_v + v ("flatten head").
@@ -236,11 +239,14 @@ def append_rows(x, W_DKV, W_KR, pos, base=10000.0, kv_norm_w=None, eps=1e-6):
 
 
 # ---------------------------------------------------------------------------
-# The latent norms.  [MLA-struct], inference code: the compressed latent is
-# passed through a norm before it is cached (and the compressed query before
-# its up-projection); the pages name neither the kind of norm nor its epsilon.
-# Reading: root-mean-square norm over the latent's features with a learned
-# per-feature weight, y = x / sqrt(mean(x^2) + eps) * w, eps = 1e-6.
+# The latent norms.  [MLA-struct], section "结合 DeepSeek 推理代码看 MLA" (both
+# branches of the pseudocode) and worked example step 3: the compressed latent
+# is passed through norm(kv_latent) before it is cached; the pages name
+# neither the kind of norm nor its epsilon.  Reading: root-mean-square norm
+# over the latent's features with a learned per-feature weight,
+# y = x / sqrt(mean(x^2) + eps) * w, eps = 1e-6.
+# The norm on the compressed query c^Q (query_path with q_norm_w) is a
+# reading beyond the pages: none of them prints it.
 # ---------------------------------------------------------------------------
 def rms_norm(x, w, eps=1e-6):
     """Row-wise x / sqrt(mean(x^2) + eps) * w over the last axis."""
@@ -287,7 +293,9 @@ def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None, n
     sequence b sits at position t_b = T_b: its row is appended at that index,
     and the query uses the same position ([MLA-struct], worked example step 3:
     write at start_pos, visible length start_pos + 1).  With ``norms`` the
-    latent norms (rms_norm with W["q_norm_w"], W["kv_norm_w"]) are applied.
+    latent norm on c^KV (W["kv_norm_w"], printed on the pages) and the
+    query-side norm on c^Q (W["q_norm_w"], a reading beyond the pages) are
+    applied.
     Returns dict of per-sequence results keyed by b.
     """
     n_h, d_h, d_r = dims["n_h"], dims["d_h"], dims["d_r"]

@@ -469,8 +469,33 @@ def test_layer_step_consistent_and_shapes(golden_dir):
 
 
 # ---------------------------------------------------------------------------
-# A planted mistake must be caught (mutations applied to a copy of the oracle
-# on the CPU; the suite above must reject each of them).
+# The softmax scale against the values the workload statements write out.
+# ---------------------------------------------------------------------------
+def _scale_pinned(scale_fn, golden):
+    return all(abs(scale_fn(e["d_h"], e["d_r"]) - e["value"]) <= 1e-15 * e["value"]
+               for e in golden["entries"])
+
+
+def test_softmax_scale_matches_workload_statements(golden_dir, monkeypatch):
+    g = _golden(golden_dir, "softmax_scale.json")
+    assert _scale_pinned(O.scale_for, g)
+    # the explicit route applies it to the sum of the content and RoPE scores:
+    # one row, so lse is that scaled score exactly
+    rng = np.random.default_rng(26)
+    for e in g["entries"]:
+        k = rand_case(rng, n_h=2, d_c=12, d_r=e["d_r"], d_h=e["d_h"], d_v=5, T=1)
+        _, _, lse = O.decode_explicit(k["q_C"], k["q_R"], 1, k["c"], k["k"], k["W_UK"], k["W_UV"],
+                                      O.scale_for(e["d_h"], e["d_r"]))
+        raw = (np.einsum("hk,hkc,c->h", k["q_C"], k["W_UK"], k["c"][0])
+               + O.rope(k["q_R"], 1) @ k["k"][0])
+        assert rel_err(lse, raw * e["value"]) < RTOL
+    # planted mistakes: 1/sqrt(d_h) (content width only) and 1/(d_h + d_R)
+    monkeypatch.setattr(O.mla_oracle, "scale_for", lambda d_h, d_r: 1.0 / math.sqrt(d_h))
+    assert not _scale_pinned(O.mla_oracle.scale_for, g)
+    monkeypatch.setattr(O.mla_oracle, "scale_for", lambda d_h, d_r: 1.0 / (d_h + d_r))
+    assert not _scale_pinned(O.mla_oracle.scale_for, g)
+
+
 # ---------------------------------------------------------------------------
 # The latent norms (root-mean-square reading).
 def test_rms_norm_matches_torch_and_closed_forms():
@@ -563,6 +588,9 @@ def test_causal_first_token_of_fresh_sequence_sees_one_row():
         assert abs(lse[0, h] - s0) < 1e-12 * max(1.0, abs(s0))
 
 
+# ---------------------------------------------------------------------------
+# A planted mistake must be caught (mutations applied to a copy of the oracle
+# on the CPU; the pins above must reject each of them).
 # ---------------------------------------------------------------------------
 def test_planted_mistakes_are_caught(monkeypatch):
     rng = np.random.default_rng(18)
