@@ -29,7 +29,7 @@ EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_decode_attn_causal", "mla_decode_attn_causal_workspace",
            "mla_absorb_q_normed", "mla_append_cache_normed",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
-           "mla_status_string", "mla_abi_version")
+           "mla_status_string", "mla_abi_version", "mla_decode_attn_noalloc")
 
 
 class MLAError(RuntimeError):
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "mla_append_cache_workspace": ([D, i32, i32, i32], sz),
         "mla_decode_attn": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_workspace": ([D, i32, i64], sz),
+        "mla_decode_attn_noalloc": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp], i32),
         "mla_decode_attn_causal": ([D, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_causal_workspace": ([D, i32, i32, i64], sz),
         "mla_project_out": ([D, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -226,6 +227,28 @@ def decode_attn(dims: Dims, q_lat, q_pe, cache, offsets, lens, o_lat, lse=None,
                            _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse),
                            _ptr(err_flag), w, wn, _stream(stream))
     _check("mla_decode_attn", st)
+
+
+def decode_attn_noalloc(dims: Dims, q_lat, q_pe, cache, offsets, lens, o_lat, lse=None,
+                        total_rows_hint: Optional[int] = None, err_flag=None, stream=None):
+    """decode_attn with the library's fixed scratch instead of a workspace
+    (the call allocates nothing)."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(q_lat, q_pe, cache, offsets, lens, o_lat, lse, err_flag)
+    _need(q_lat, B * dims.n_h * dims.d_c, dt, "q_lat")
+    _need(q_pe, B * dims.n_h * dims.d_r, dt, "q_pe")
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(o_lat, B * dims.n_h * dims.d_c, torch.float32, "o_lat")
+    _need(lse, B * dims.n_h, torch.float32, "lse")
+    if cache.dtype != dt:
+        raise ValueError("cache dtype")
+    hint = int(total_rows_hint) if total_rows_hint is not None else max(1, cache.shape[0])
+    st = L.mla_decode_attn_noalloc(ctypes.byref(dims), B, _ptr(q_lat), _ptr(q_pe), _ptr(cache),
+                                   _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse),
+                                   _ptr(err_flag), _stream(stream))
+    _check("mla_decode_attn_noalloc", st)
 
 
 def project_out(dims: Dims, o_lat, W_UV, o=None, u=None, W_O=None, ws=None, stream=None):

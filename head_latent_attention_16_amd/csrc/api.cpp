@@ -160,6 +160,35 @@ mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const
                                         err_flag, (hipStream_t)stream));
 }
 
+// ---- fixed scratch for mla_decode_attn_noalloc -----------------------------
+// Device memory the library owns: one copy of this array on every device the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(52) << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on first use).
+hipError_t scratch_ptr_current(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 int num_cu_or_default() {
   DeviceInfo info;
   if (current_device_info(&info) == hipSuccess && info.num_cu > 0) return info.num_cu;
@@ -425,6 +454,27 @@ mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n
                                     int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   return decode_common(dims, B, n_q, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, ws_bytes, stream);
+}
+
+mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                                     const void* q_pe, const void* cache, const int32_t* offsets,
+                                     const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                                     float* lse, int32_t* err_flag, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (B < 0 || B > kMaxQueryTokens) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (total_rows_hint < 1) return MLA_ERR_SHAPE;
+  if (!q_lat || !q_pe || !cache || !offsets || !lens || !o_lat) return MLA_ERR_NULL;
+  DeviceInfo info;
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  const size_t need = decode_ws(s, B, 1, total_rows_hint, info.num_cu);
+  if (need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && scratch_ptr_current(&ws) != hipSuccess) return MLA_ERR_DEVICE;
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+                       err_flag, ws, need, stream);
 }
 
 size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {

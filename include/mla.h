@@ -187,6 +187,24 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_la
                              void* stream);
 size_t mla_decode_attn_workspace(const mla_dims_t* dims, int32_t B, int64_t total_rows_hint);
 
+/* mla_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, kernels and results as mla_decode_attn
+ * with the same arguments, but the scratch is a fixed array inside the
+ * library (52 MiB on each device it runs on, held until the process ends)
+ * instead of a caller workspace.  The call allocates and frees nothing.
+ * Limit: the scratch mla_decode_attn_workspace(dims, B, total_rows_hint)
+ * would ask for must fit in 52 MiB (at V3 dims on a 256-CU MI355X: up to
+ * 156 sequences; other dims need none); larger requests return
+ * MLA_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one device shares that device's
+ * scratch: calls that overlap on one device (different streams or threads)
+ * race and must be serialised by the caller. */
+mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                                     const void* q_pe, const void* cache, const int32_t* offsets,
+                                     const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                                     float* lse, int32_t* err_flag, void* stream);
+
 /* Several new tokens per sequence in one step ("MLA模型结构详解", worked
  * example step 4: with more than one new token the inference code masks the
  * scores causally before the softmax).  The step's n_q tokens are the last
