@@ -53,7 +53,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     # default: the largest single-GPU attention workload (ragged, 1.29 GB of cache per step)
-    p.add_argument("--workload", default="ragged", choices=["uniform", "ragged", "long", "layer", "causal"])
+    p.add_argument("--workload", default="ragged",
+                   choices=["uniform", "ragged", "long", "layer", "causal", "paged"])
+    p.add_argument("--block-rows", type=int, default=64, help="paged workload: rows per pool block")
     p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
     p.add_argument("--norms", action="store_true",
                    help="layer workload: root-mean-square latent norms on c^Q and c^KV")
@@ -177,7 +179,9 @@ def main():
     log(f"generating workload {name} ...")
     t0 = time.perf_counter()
     w = (I.layer(spare=spare) if name == "layer"
-         else I.causal(n_q=args.n_q) if name == "causal" else I.make(name))
+         else I.causal(n_q=args.n_q) if name == "causal"
+         else I.make("ragged") if name == "paged" else I.make(name))
+    paged = name == "paged"
     n_q = w.n_q
     log(f"  done in {time.perf_counter() - t0:.1f}s: B={w.B} total_rows={w.total_rows}")
     d = w.dims
@@ -190,7 +194,14 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    base = {"cache": dev(w.cache), "offsets": dev(w.offsets), "lens": dev(w.lens)}
+    if paged:
+        # the ragged batch's rows in a pool of block_rows-row blocks with shuffled ids
+        pp = I.paged_pool([w.cache], w.lens, w.lens, args.block_rows, seed=1)
+        base = {"cache": dev(pp.pool), "table": dev(pp.tables[0]), "offsets": dev(w.offsets),
+                "lens": dev(w.lens)}
+        del pp
+    else:
+        base = {"cache": dev(w.cache), "offsets": dev(w.offsets), "lens": dev(w.lens)}
     for k, v in w.W.items():
         base[k] = dev(v)
     if layer:
@@ -218,7 +229,10 @@ def main():
     ws_dec = torch.empty(L.decode_attn_causal_workspace(dims, B, n_q, hint), dtype=torch.uint8, device="cuda")
 
     def attend(s):
-        if n_q > 1:
+        if paged:
+            L.decode_attn_paged(dims, q_lat, q_pe, s["cache"], args.block_rows, s["table"], s["lens"], o_lat, lse,
+                                total_rows_hint=hint, ws=ws_dec)
+        elif n_q > 1:
             L.decode_attn_causal(dims, n_q, q_lat, q_pe, s["cache"], s["offsets"], s["lens"], o_lat, lse,
                                  total_rows_hint=hint, ws=ws_dec)
         else:
@@ -321,7 +335,9 @@ def main():
           "ragged": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows}",
           "long": f"long-context B={w.B} T={int(w.lens[0])}",
           "layer": f"full layer step B={w.B} prior T~U[512,8192] sum={w.total_rows}",
-          "causal": f"causal B={w.B} T={int(w.lens[0])} n_q={n_q} new tokens per sequence"}[name]
+          "causal": f"causal B={w.B} T={int(w.lens[0])} n_q={n_q} new tokens per sequence",
+          "paged": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows} in a paged pool of "
+                   f"{args.block_rows}-row blocks"}[name]
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -340,12 +356,14 @@ def main():
                    "step": ("absorb_q_normed+append_normed+decode_attn+project_out(o,u)" if args.norms
                             else "absorb_q+append+decode_attn+project_out(o,u)") if layer
                    else "absorb_q+decode_attn_causal+project_out(o)" if n_q > 1
+                   else "absorb_q+decode_attn_paged+project_out(o)" if paged
                    else "absorb_q+decode_attn+project_out(o)",
                    "input_copies_rotated": copies,
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
-                     "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn")
+                     "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn_paged" if paged
+                                else "mla_decode_attn")
                      + " (split attention with length scan + combine)",
                      "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
                      "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,

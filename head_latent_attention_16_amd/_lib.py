@@ -22,6 +22,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_LAUNCH", 6: "MLA_ERR_DEVICE"}
 DEVERR_LENS = 1
 DEVERR_OVERFLOW = 2
+DEVERR_TABLE = 4
 DT_BF16, DT_F32 = 0, 1
 
 EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
@@ -29,7 +30,8 @@ EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_decode_attn_causal", "mla_decode_attn_causal_workspace",
            "mla_absorb_q_normed", "mla_append_cache_normed",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
-           "mla_status_string", "mla_abi_version", "mla_decode_attn_noalloc")
+           "mla_status_string", "mla_abi_version", "mla_decode_attn_noalloc",
+           "mla_decode_attn_paged", "mla_append_cache_paged")
 
 
 class MLAError(RuntimeError):
@@ -80,6 +82,10 @@ def lib() -> ctypes.CDLL:
         "mla_decode_attn": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_workspace": ([D, i32, i64], sz),
         "mla_decode_attn_noalloc": ([D, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp], i32),
+        "mla_decode_attn_paged": ([D, i32, vp, vp, vp, i32, i32, vp, i32, vp, i64, vp, vp, vp, vp, sz, vp],
+                                  i32),
+        "mla_append_cache_paged": ([D, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp],
+                                   i32),
         "mla_decode_attn_causal": ([D, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_causal_workspace": ([D, i32, i32, i64], sz),
         "mla_project_out": ([D, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -249,6 +255,56 @@ def decode_attn_noalloc(dims: Dims, q_lat, q_pe, cache, offsets, lens, o_lat, ls
                                    _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse),
                                    _ptr(err_flag), _stream(stream))
     _check("mla_decode_attn_noalloc", st)
+
+
+def decode_attn_paged(dims: Dims, q_lat, q_pe, pool, block_rows: int, block_table, lens, o_lat, lse=None,
+                      total_rows_hint: Optional[int] = None, err_flag=None, ws=None, stream=None):
+    """decode_attn over a block pool: row t of sequence b is row
+    t % block_rows of block block_table[b, t // block_rows]."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(q_lat, q_pe, pool, block_table, lens, o_lat, lse, err_flag)
+    _need(q_lat, B * dims.n_h * dims.d_c, dt, "q_lat")
+    _need(q_pe, B * dims.n_h * dims.d_r, dt, "q_pe")
+    _need(o_lat, B * dims.n_h * dims.d_c, torch.float32, "o_lat")
+    _need(lse, B * dims.n_h, torch.float32, "lse")
+    if pool.dtype != dt or block_table.dtype != torch.int32 or block_table.dim() != 2 \
+            or block_table.shape[0] != B:
+        raise ValueError("pool dtype or block table shape")
+    nrows = pool.numel() // (dims.d_c + dims.d_r)
+    hint = int(total_rows_hint) if total_rows_hint is not None else max(1, nrows)
+    ws = _workspace(decode_attn_workspace(dims, B, hint), ws, pool.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_decode_attn_paged(ctypes.byref(dims), B, _ptr(q_lat), _ptr(q_pe), _ptr(pool),
+                                 nrows // block_rows, block_rows, _ptr(block_table), block_table.shape[1],
+                                 _ptr(lens), hint, _ptr(o_lat), _ptr(lse), _ptr(err_flag), w, wn,
+                                 _stream(stream))
+    _check("mla_decode_attn_paged", st)
+
+
+def append_cache_paged(dims: Dims, pool, block_rows: int, block_table, lens, n_new: int, kv_raw=None,
+                       h_t=None, W_DKV=None, W_KR=None, err_flag=None, ws=None, stream=None):
+    """append_cache into a block pool (row lens[b] + i of sequence b)."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(pool, block_table, lens, kv_raw, h_t, W_DKV, W_KR, err_flag)
+    _need(lens, B, torch.int32, "lens")
+    _need(kv_raw, B * n_new * (dims.d_c + dims.d_r), dt, "kv_raw")
+    _need(h_t, B * n_new * dims.d_model, dt, "h_t")
+    if pool.dtype != dt or block_table.dtype != torch.int32 or block_table.dim() != 2 \
+            or block_table.shape[0] != B:
+        raise ValueError("pool dtype or block table shape")
+    nrows = pool.numel() // (dims.d_c + dims.d_r)
+    nbytes = int(L.mla_append_cache_workspace(ctypes.byref(dims), B, n_new, int(h_t is not None)))
+    ws = _workspace(nbytes, ws, pool.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_append_cache_paged(ctypes.byref(dims), B, n_new, _ptr(h_t), _ptr(W_DKV), _ptr(W_KR),
+                                  _ptr(kv_raw), _ptr(pool), nrows // block_rows, block_rows,
+                                  _ptr(block_table), block_table.shape[1], _ptr(lens), _ptr(err_flag), w, wn,
+                                  _stream(stream))
+    _check("mla_append_cache_paged", st)
 
 
 def project_out(dims: Dims, o_lat, W_UV, o=None, u=None, W_O=None, ws=None, stream=None):

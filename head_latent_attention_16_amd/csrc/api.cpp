@@ -130,8 +130,34 @@ size_t decode_ws(const Shape& s, int B, int n_q, int64_t hint, int num_cu) {
   return 0;
 }
 
+RowMap contiguous_map(const int32_t* offsets) {
+  RowMap m;
+  m.offsets = offsets;
+  m.table = nullptr;
+  m.max_blocks = m.shift = m.num_blocks = 0;
+  return m;
+}
+
+// Host-side validation of a paged pool description (see mla_decode_attn_paged).
+mla_status_t paged_map(int32_t num_blocks, int32_t block_rows, const int32_t* block_table,
+                       int32_t max_blocks, RowMap* out) {
+  if (num_blocks < 1 || max_blocks < 1 || block_rows < 32 || block_rows > (1 << 20) ||
+      (block_rows & (block_rows - 1)) != 0)
+    return MLA_ERR_SHAPE;
+  // a sequence's capacity max_blocks * block_rows must be an int32 length
+  if ((int64_t)max_blocks * block_rows > INT32_MAX) return MLA_ERR_SHAPE;
+  int shift = 0;
+  while ((1 << shift) < block_rows) ++shift;
+  out->offsets = nullptr;
+  out->table = block_table;
+  out->max_blocks = max_blocks;
+  out->shift = shift;
+  out->num_blocks = num_blocks;
+  return MLA_OK;
+}
+
 mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
-                           const void* q_pe, const void* cache, const int32_t* offsets,
+                           const void* q_pe, const void* cache, const RowMap& map,
                            const int32_t* lens, int64_t total_rows_hint, float* o_lat, float* lse,
                            int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
@@ -140,7 +166,8 @@ mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const
   if (B < 0 || n_q < 1 || (int64_t)B * n_q > kMaxQueryTokens) return MLA_ERR_SHAPE;
   if (B == 0) return MLA_OK;
   if (total_rows_hint < 1) return MLA_ERR_SHAPE;
-  if (!q_lat || !q_pe || !cache || !offsets || !lens || !o_lat) return MLA_ERR_NULL;
+  if (!q_lat || !q_pe || !cache || !(map.paged() ? map.table : map.offsets) || !lens || !o_lat)
+    return MLA_ERR_NULL;
   total_rows_hint = clamp_hint(total_rows_hint);
   DeviceInfo info;
   const bool fast = !force_generic() && decode_v3_supported(s);
@@ -151,12 +178,12 @@ mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const
     if ((st = device_ready(&info)) != MLA_OK) return st;
     const size_t need = decode_v3_workspace(s, B, n_q, total_rows_hint, info.num_cu);
     if (ws_bytes < need) return MLA_ERR_WORKSPACE;
-    return launched(launch_decode_v3(s, B, n_q, q_lat, q_pe, cache, offsets, lens, total_rows_hint,
+    return launched(launch_decode_v3(s, B, n_q, q_lat, q_pe, cache, map, lens, total_rows_hint,
                                      o_lat, lse, err_flag, ws, ws_bytes, info.num_cu,
                                      (hipStream_t)stream));
   }
   if ((st = device_ready(&info)) != MLA_OK) return st;
-  return launched(launch_decode_generic(s, B, n_q, q_lat, q_pe, cache, offsets, lens, o_lat, lse,
+  return launched(launch_decode_generic(s, B, n_q, q_lat, q_pe, cache, map, lens, o_lat, lse,
                                         err_flag, (hipStream_t)stream));
 }
 
@@ -351,14 +378,14 @@ namespace {
 // (root-mean-square, eps) before they are written.
 mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
                            const void* W_DKV, const void* kv_norm_w, float eps, const void* W_KR,
-                           const void* kv_raw, void* cache, const int32_t* offsets, int32_t* lens,
+                           const void* kv_raw, void* cache, const RowMap& map, int32_t* lens,
                            int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
   if (B < 0 || n_new < 0) return MLA_ERR_SHAPE;
   if (B == 0 || n_new == 0) return MLA_OK;
-  if (!cache || !offsets || !lens) return MLA_ERR_NULL;
+  if (!cache || !(map.paged() ? map.table : map.offsets) || !lens) return MLA_ERR_NULL;
   const bool from_hidden = h_t != nullptr;
   if (from_hidden) {
     if (!W_DKV || !W_KR) return MLA_ERR_NULL;
@@ -383,7 +410,7 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
       if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, D, kv_norm_w, eps, hs) != hipSuccess)
         return MLA_ERR_LAUNCH;
-      return launched(launch_append_generic(s, B, n_new, kc, D, kc + s.d_c, D, true, cache, offsets,
+      return launched(launch_append_generic(s, B, n_new, kc, D, kc + s.d_c, D, true, cache, map,
                                             lens, err_flag, hs));
     }
     float* kr = kc + (size_t)M * s.d_c;
@@ -394,12 +421,12 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
     e = linear(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
     return launched(launch_append_generic(s, B, n_new, kc, (size_t)s.d_c, kr, (size_t)s.d_r, true,
-                                          cache, offsets, lens, err_flag, hs));
+                                          cache, map, lens, err_flag, hs));
   }
   const char* raw = (const char*)kv_raw;
   // kv_raw is in the storage type: fp32 rows are read as fp32, bf16 rows as bf16.
   return launched(launch_append_generic(s, B, n_new, raw, D, raw + (size_t)s.d_c * elem_bytes(s), D,
-                                        !s.bf16, cache, offsets, lens, err_flag, hs));
+                                        !s.bf16, cache, map, lens, err_flag, hs));
 }
 }  // namespace
 
@@ -409,7 +436,7 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
                               const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
                               const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
                               size_t ws_bytes, void* stream) {
-  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache, offsets, lens,
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache, contiguous_map(offsets), lens,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -423,7 +450,7 @@ mla_status_t mla_append_cache_normed(const mla_dims_t* dims, int32_t B, int32_t 
   if (st != MLA_OK) return st;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return MLA_ERR_SHAPE;
   if (B > 0 && n_new > 0 && (!h_t || !kv_norm_w)) return MLA_ERR_NULL;
-  return append_common(dims, B, n_new, h_t, W_DKV, kv_norm_w, eps, W_KR, nullptr, cache, offsets, lens,
+  return append_common(dims, B, n_new, h_t, W_DKV, kv_norm_w, eps, W_KR, nullptr, cache, contiguous_map(offsets), lens,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -436,7 +463,7 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_la
                              const int32_t* lens, int64_t total_rows_hint, float* o_lat,
                              float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
                              void* stream) {
-  return decode_common(dims, B, 1, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -452,7 +479,7 @@ mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n
                                     const int32_t* offsets, const int32_t* lens,
                                     int64_t total_rows_hint, float* o_lat, float* lse,
                                     int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
-  return decode_common(dims, B, n_q, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, n_q, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -473,8 +500,37 @@ mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t B, const vo
   if (need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
   void* ws = nullptr;
   if (need > 0 && scratch_ptr_current(&ws) != hipSuccess) return MLA_ERR_DEVICE;
-  return decode_common(dims, B, 1, q_lat, q_pe, cache, offsets, lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, need, stream);
+}
+
+mla_status_t mla_decode_attn_paged(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                                   const void* q_pe, const void* pool, int32_t num_blocks,
+                                   int32_t block_rows, const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                                   float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  RowMap map;
+  if ((st = paged_map(num_blocks, block_rows, block_table, max_blocks, &map)) != MLA_OK) return st;
+  return decode_common(dims, B, 1, q_lat, q_pe, pool, map, lens, total_rows_hint, o_lat, lse, err_flag,
+                       ws, ws_bytes, stream);
+}
+
+mla_status_t mla_append_cache_paged(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                                    const void* W_DKV, const void* W_KR, const void* kv_raw, void* pool,
+                                    int32_t num_blocks, int32_t block_rows, const int32_t* block_table,
+                                    int32_t max_blocks, int32_t* lens, int32_t* err_flag, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  RowMap map;
+  if ((st = paged_map(num_blocks, block_rows, block_table, max_blocks, &map)) != MLA_OK) return st;
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, pool, map, lens, err_flag,
+                       ws, ws_bytes, stream);
 }
 
 size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {

@@ -185,10 +185,10 @@ __device__ __forceinline__ int4 seq_info(int64_t vb, int64_t len, const Line& vl
 __device__ __forceinline__ int seq_of(int v, int n_q) { return n_q == 1 ? v : v / n_q; }
 
 // Rows seen by sequence v (>= 1), or 0 if its sequence is invalid.
-__device__ __forceinline__ int vseq_len(const int32_t* lens, const int32_t* offsets, int v, int n_q) {
+__device__ __forceinline__ int vseq_len(const int32_t* lens, const RowMap& map, int v, int n_q) {
   const int b = seq_of(v, n_q);
-  const int len = lens[b], cap = offsets[b + 1] - offsets[b];
-  return len >= n_q && len <= cap ? len - (n_q - 1 - (v - b * n_q)) : 0;
+  const int len = lens[b];
+  return len >= n_q && (int64_t)len <= map.capacity(b) ? len - (n_q - 1 - (v - b * n_q)) : 0;
 }
 
 constexpr int SCHED_THREADS = 1024;
@@ -230,7 +230,7 @@ __device__ __forceinline__ int64_t block_scan_1024(int64_t tsum, int64_t* wsum, 
 }
 
 __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int n_q, int G,
-                                                         const int32_t* __restrict__ offsets,
+                                                         RowMap map,
                                                          const int32_t* __restrict__ lens,
                                                          int64_t* __restrict__ prefix,
                                                          int32_t* __restrict__ cnt,
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int n_q, int G,
       const int b = base + SCHED_PER * tid + j;
       v[j] = 0;
       if (b < B) {
-        const int len = vseq_len(lens, offsets, b, n_q);
+        const int len = vseq_len(lens, map, b, n_q);
         if (len > 0)
           v[j] = len;
         else if (err_flag)
@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(SCHED_THREADS) k_sched(int B, int n_q, int G,
     r.seq_begin = pre(lo);
     r.seq_end = pre(lo + 1);
     r.b = lo;
-    r.off_b = offsets[seq_of(lo, n_q)];
+    r.off_b = map.paged() ? 0 : map.offsets[seq_of(lo, n_q)];
     r.pad[0] = r.pad[1] = 0;
     rec[g] = r;
   }
@@ -368,8 +368,8 @@ struct SplitArgs {
   float* lse;
   const __bf16* q_lat;
   const __bf16* q_pe;
-  const char* cache;
-  const int32_t* offsets;
+  const char* cache;     // the cache, or the block pool (paged)
+  RowMap map;
   const int64_t* prefix;
   _Float16* part_o;
   float* part_ml;
@@ -415,6 +415,18 @@ __device__ __forceinline__ void dma_16B(uint32_t lds_addr, uint32_t voff, const 
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(base))
                : "m0");
+}
+
+// One int32 of wave-uniform address through the scalar unit, waited for in
+// the same statement (vector loads would disturb the hand-counted vmcnt of
+// the tile DMAs).  Used only where no LDS read is in flight.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v)
+               : "s"(uniform_ptr((const char*)p))
+               : "memory");
+  return v;
 }
 
 template <int N>
@@ -479,7 +491,7 @@ __device__ __forceinline__ int swz(int r) {
 // One wave per SIMD holds Q (144 VGPRs) and O (256 accumulation registers);
 // latency is hidden inside the wave by loading LDS fragments several
 // steps ahead of the MFMA that consumes them.
-template <bool SCAN>
+template <bool SCAN, bool PAGED>
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
   // in-kernel scan (SCAN): prefix of the valid lengths and the offsets
@@ -513,8 +525,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     if (wave == 0) {
       const int l = lane_id;
       const bool in = l < B;
-      const int len = vseq_len(a.lens, a.offsets, min(l, B - 1), a.n_q);
-      const int o0 = a.offsets[seq_of(min(l, B - 1), a.n_q)];
+      const int len = vseq_len(a.lens, a.map, min(l, B - 1), a.n_q);
+      const int o0 = PAGED ? 0 : a.map.offsets[seq_of(min(l, B - 1), a.n_q)];
       const bool ok = len > 0;
       const int64_t v = in && ok ? len : 0;
       bad = in && !ok ? 1 : 0;
@@ -582,8 +594,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 #pragma unroll
     for (int j = 0; j < SPL_PER; ++j) {
       const int bb = min(tid * SPL_PER + j, B - 1);
-      lenj[j] = vseq_len(a.lens, a.offsets, bb, a.n_q);
-      offj[j] = a.offsets[seq_of(bb, a.n_q)];
+      lenj[j] = vseq_len(a.lens, a.map, bb, a.n_q);
+      offj[j] = PAGED ? 0 : a.map.offsets[seq_of(bb, a.n_q)];
     }
     int64_t v[SPL_PER];
     int64_t tsum = 0;
@@ -728,7 +740,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   };
   auto off_of = [&](int i) -> int {
     if constexpr (SCAN) return uniform_i32(s_off[i]);
-    else return uniform_i32(a.offsets[seq_of(i, a.n_q)]);
+    else if constexpr (PAGED) return 0;
+    else return uniform_i32(a.map.offsets[seq_of(i, a.n_q)]);
   };
 
   if (start >= end) {
@@ -838,6 +851,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int seg_len = (int)(seg_end - pos);
     const int ntiles = (seg_len + TILE - 1) / TILE;
     const char* rows = a.cache + ((size_t)off_b + (size_t)t0) * ROWB;
+    // paged: this sequence's row of the block table
+    const int32_t* tbl = PAGED ? a.map.table + (size_t)seq_of(b, a.n_q) * a.map.max_blocks : nullptr;
 
     if (!first_segment) barrier_all_lds();   // previous segment's tiles fully consumed
     first_segment = false;
@@ -879,23 +894,58 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     //    (just fetched, so served by L2) into the stage that tile t would
     //    use -- it is free, and no later tile of this piece uses it.
     // With a fixed count per tile the wait for tile `it` is always the same.
-    auto dma_src = [&](int t, const char*& tbase, uint32_t& bound) {
+    //
+    // Paged rows: the tile's (at most 32) rows lie in at most two pool blocks
+    // (a block holds >= 32 rows).  Lanes whose byte offset in the tile is
+    // below thr read from block 0 at a0 + offset, the others from block 1 at
+    // a1 + offset (a1 is block 1's address shifted back by the rows of block
+    // 0 in the tile), so one compare and select per DMA picks the source.
+    // An id outside [0, num_blocks) is replaced by block 0 (nothing outside
+    // the pool is read) and the piece is flagged; its sequence's result is
+    // then NaN with MLA_DEVERR_TABLE.
+    struct TileSrc {
+      const char* a0;
+      const char* a1;
+      uint32_t thr, bound;
+    };
+    bool bad_tbl = false;
+    auto dma_src = [&](int t) -> TileSrc {
       const int ts = t < ntiles ? t : ntiles - 1;
-      tbase = rows + (size_t)ts * TILEB;
       const int nv = seg_len - ts * TILE;
-      bound = nv >= TILE ? (uint32_t)TILEB - 16u : (uint32_t)(nv * ROWB - 16);
+      TileSrc r;
+      r.bound = nv >= TILE ? (uint32_t)TILEB - 16u : (uint32_t)(nv * ROWB - 16);
+      if constexpr (!PAGED) {
+        r.a0 = r.a1 = rows + (size_t)ts * TILEB;
+        r.thr = 0xffffffffu;
+      } else {
+        const int sh = a.map.shift;
+        const int brows = 1 << sh;
+        const int R0 = t0 + ts * TILE;   // the tile's first row in the sequence
+        const int rin = R0 & (brows - 1);
+        const int blk = R0 >> sh;
+        const int nrow = nv < TILE ? nv : TILE;
+        int id0 = sload_i32(tbl + blk);
+        int id1 = rin + nrow > brows ? sload_i32(tbl + blk + 1) : id0;
+        if ((unsigned)id0 >= (unsigned)a.map.num_blocks) { id0 = 0; bad_tbl = true; }
+        if ((unsigned)id1 >= (unsigned)a.map.num_blocks) { id1 = 0; bad_tbl = true; }
+        r.a0 = a.cache + (((int64_t)id0 << sh) + rin) * (int64_t)ROWB;
+        r.a1 = a.cache + (((int64_t)id1 << sh) + rin - brows) * (int64_t)ROWB;
+        r.thr = (uint32_t)((brows - rin) * ROWB);
+      }
+      return r;
+    };
+    auto dma = [&](uint32_t lds_addr, uint32_t off, const TileSrc& src) {
+      if constexpr (!PAGED) dma_16B(lds_addr, off, src.a0);
+      else dma_16B_at(lds_addr, (off < src.thr ? src.a0 : src.a1) + off);
     };
     auto issue_tile = [&](int t) {
-      const char* tbase;
-      uint32_t bound;
-      dma_src(t, tbase, bound);
+      const TileSrc src = dma_src(t);
       const uint32_t stage_lds = lds0 + (uint32_t)((t % NSTAGE) * TILEB);
       uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_off(k), bound);
+      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_off(k), src.bound);
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k)
-        dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], tbase);
+      for (int k = 0; k < DMA_PER_WAVE; ++k) dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], src);
     };
     // Wait for tile `it`: the tiles it+1 and it+2 were issued after it.
     auto wait_tile = [&]() { wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>(); };
@@ -1002,6 +1052,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     // ---- software pipeline: [QK(it+1) || softmax(it)], then PV(it) ----
     for (int it = 0; it < ntiles; ++it) {
       const int nvalid = seg_len - it * TILE;
+      // source of tile it+3, DMA'd during PV below (paged: its block ids are
+      // fetched here, where no LDS read is in flight)
+      const TileSrc nsrc = dma_src(it + NSTAGE - 1);
       const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
       bf16x8 P[2];
       floatx16 S_next;
@@ -1087,9 +1140,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       // clock, so issuing them back to back stalls the wave for ~600 cycles.
       {
         const int nt = it + NSTAGE - 1;
-        const char* tbase;
-        uint32_t bound;
-        dma_src(nt, tbase, bound);
         const uint32_t stage_lds = lds0 + (uint32_t)((nt % NSTAGE) * TILEB);
         // DMA k goes out after MFMA 3k+2 (its source offset is recomputed
         // there: a few VALU instructions in the MFMA gaps, no registers held).
@@ -1108,8 +1158,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
           }
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
           if (s % 3 == 2 && s / 3 < DMA_PER_WAVE)
-            dma_16B(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024),
-                    min(dma_off(s / 3), bound), tbase);
+            dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024), min(dma_off(s / 3), nsrc.bound),
+                nsrc);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
 #pragma unroll
@@ -1141,7 +1191,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       if (g32 == 0 && a.lse) a.lse[(size_t)b * NH + head] = (m_ref + log2f(l_tot)) * kLn2;
-      const int flag = __any(ovf_any) ? 1 : 0;
+      const int flag = (__any(ovf_any) ? 1 : 0) | (bad_tbl ? 2 : 0);
       if (lane == 0) a.flags[slot * WAVES + wave] = flag;
       pos = seg_end;
       continue;
@@ -1171,7 +1221,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // once would need as many VGPRs
         __builtin_amdgcn_sched_barrier(0);
       }
-    const int flag = __any(ovf_any || amax > PART_MAX) ? 1 : 0;
+    const int flag = (__any(ovf_any || amax > PART_MAX) ? 1 : 0) | (bad_tbl ? 2 : 0);
     if (lane == 0) a.flags[slot * WAVES + wave] = flag;
     if (g32 == 0) {
       float* pm = a.part_ml + (slot * NH + head) * 2;
@@ -1189,13 +1239,14 @@ struct CombineArgs {
   const __bf16* q_lat;
   const __bf16* q_pe;
   const __bf16* cache;
-  const int32_t* offsets;
+  RowMap map;
   const int4* seqinfo;
   const int32_t* flags;
   const _Float16* part_o;
   const float* part_ml;
   float* o_lat;
   float* lse;
+  int32_t* err_flag;
   int B;     // one per query token, as in the split kernel
   int n_q;
   int G;
@@ -1224,9 +1275,13 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
 #pragma unroll
   for (int k = 0; k < DC / 64; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const __bf16* rows = a.cache + (size_t)a.offsets[seq_of(b, a.n_q)] * DK;
+  const int seq = seq_of(b, a.n_q);
   for (int j = wave; j < len; j += CMB_WAVES) {
-    const __bf16* r = rows + (size_t)j * DK;
+    // (every block of a sequence that reaches this fallback was validated by
+    // the split kernel; the check only keeps a bad id from being followed)
+    const int64_t rj = a.map.row(seq, j);
+    if (rj < 0) continue;
+    const __bf16* r = a.cache + (size_t)rj * DK;
     float sdot = 0.f;
 #pragma unroll
     for (int k = 0; k < DK / 64; ++k) sdot += q[k] * (float)r[lane + 64 * k];
@@ -1417,7 +1472,8 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
   const int hb = blockIdx.x / ngrp, cb0 = (blockIdx.x % ngrp) * cpw, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int4 si = a.seqinfo[b];   // first range, ranges, valid length
-  if (si.z <= 0) {   // invalid length: NaN result (the error flag is set)
+  // this block's share of the result set to NaN
+  auto write_nan = [&]() {
     const float nan = __builtin_nanf("");
     const int h_r = tid >> 3, c_r = (tid & 7) * 4;
     for (int c = 0; c < cpw; ++c) {
@@ -1425,15 +1481,25 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
       *out = make_float4(nan, nan, nan, nan);
     }
     if (cb0 == 0 && tid < CMB_HB && a.lse) a.lse[(size_t)b * NH + hb * CMB_HB + tid] = nan;
+  };
+  if (si.z <= 0) {   // invalid length: NaN result (the error flag is set)
+    write_nan();
     return;
   }
   const int npiece = si.y;
   const size_t slot0 = (size_t)si.x + (size_t)b;   // piece i is slot slot0 + i
   int flag = 0;
   for (int k = tid; k < npiece * WAVES; k += CMB_THREADS) flag |= a.flags[slot0 * WAVES + k];
-  // a piece overflowed: the blocks of this head block share its heads out
-  // and recompute whole rows each
+  // A flagged piece (reached by every thread of the block together): a block
+  // id outside the pool (bit 2) makes the sequence's result NaN; otherwise a
+  // piece overflowed (bit 1) and the blocks of this head block share its
+  // heads out and recompute whole rows each.
   auto fallback = [&]() {
+    if (__syncthreads_or(flag & 2)) {
+      write_nan();
+      if (tid == 0 && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_TABLE);
+      return;
+    }
     for (int k = blockIdx.x % ngrp; k < CMB_HB; k += ngrp) recompute_head(a, b, hb * CMB_HB + k, si.z);
   };
   float M, L;
@@ -1481,7 +1547,7 @@ size_t decode_v3_workspace(const Shape&, int B, int n_q, int64_t total_rows_hint
 }
 
 hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_lat, const void* q_pe,
-                            const void* cache, const int32_t* offsets, const int32_t* lens,
+                            const void* cache, const RowMap& map, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t, int num_cu, hipStream_t st) {
   const int B = B_seq * n_q;
@@ -1503,7 +1569,7 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   a.q_lat = (const __bf16*)q_lat;
   a.q_pe = (const __bf16*)q_pe;
   a.cache = (const char*)cache;
-  a.offsets = offsets;
+  a.map = map;
   a.prefix = prefix;
   a.part_o = (_Float16*)(w + L.o_off);
   a.part_ml = (float*)(w + L.ml_off);
@@ -1512,13 +1578,15 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   a.G = G;
   a.scale_log2 = s.scale * kLog2e;
   if (B <= SPL_MAXB) {
-    k_split<true><<<G, THREADS, 0, st>>>(a);
+    if (map.paged()) k_split<true, true><<<G, THREADS, 0, st>>>(a);
+    else k_split<true, false><<<G, THREADS, 0, st>>>(a);
   } else {
-    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, n_q, G, offsets, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
+    k_sched<<<1, SCHED_THREADS, 0, st>>>(B, n_q, G, map, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
                                          err_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_split<false><<<G, THREADS, 0, st>>>(a);
+    if (map.paged()) k_split<false, true><<<G, THREADS, 0, st>>>(a);
+    else k_split<false, false><<<G, THREADS, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1526,7 +1594,8 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   c.q_lat = a.q_lat;
   c.q_pe = a.q_pe;
   c.cache = (const __bf16*)cache;
-  c.offsets = offsets;
+  c.map = map;
+  c.err_flag = err_flag;
   c.seqinfo = seqinfo;
   c.flags = flags;
   c.part_o = a.part_o;

@@ -76,23 +76,27 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_append(int n_new, int d_c, int d_r, double base,
                                                 const void* c_src, size_t c_stride,
                                                 const void* k_src, size_t k_stride, bool src_f32,
-                                                T* __restrict__ cache,
-                                                const int32_t* __restrict__ offsets,
+                                                T* __restrict__ cache, RowMap map,
                                                 int32_t* __restrict__ lens, int32_t* err_flag) {
   const int b = blockIdx.x;
   const int D = d_c + d_r;
   const int len = lens[b];
-  const int off = offsets[b];
-  const int cap = offsets[b + 1] - off;
-  if (len < 0 || (int64_t)len + n_new > (int64_t)cap) {
+  if (len < 0 || (int64_t)len + n_new > map.capacity(b)) {
     if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, MLA_DEVERR_OVERFLOW);
+    return;
+  }
+  // every destination row must map to a valid block before anything is written
+  bool bad = false;
+  for (int i = 0; i < n_new; ++i) bad |= map.row(b, (int64_t)len + i) < 0;
+  if (bad) {
+    if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, MLA_DEVERR_TABLE);
     return;
   }
   const int half = d_r / 2;
   for (int i = 0; i < n_new; ++i) {
     const size_t idx = (size_t)b * n_new + i;
     const size_t cs = idx * c_stride, ks = idx * k_stride;
-    T* dst = cache + (size_t)(off + len + i) * D;
+    T* dst = cache + (size_t)map.row(b, (int64_t)len + i) * D;
     for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
       if (src_f32)
         dst[c] = from_f32<T>(((const float*)c_src)[cs + c]);
@@ -118,8 +122,7 @@ __global__ void __launch_bounds__(256) k_append(int n_new, int d_c, int d_r, dou
 template <typename T>
 __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n_q, float scale_log2,
                                                 const T* __restrict__ q_lat, const T* __restrict__ q_pe,
-                                                const T* __restrict__ cache,
-                                                const int32_t* __restrict__ offsets,
+                                                const T* __restrict__ cache, RowMap map,
                                                 const int32_t* __restrict__ lens,
                                                 float* __restrict__ o_lat, float* __restrict__ lse,
                                                 int32_t* err_flag) {
@@ -132,18 +135,24 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n
   const int nw = blockDim.x >> 6;
   const int D = d_c + d_r;
   const int all = lens[b];
-  const int off = offsets[b];
-  const int cap = offsets[b + 1] - off;
   float* out = o_lat + ((size_t)v * n_h + h) * d_c;
-  if (all < n_q || all > cap) {
+  int bad = all < n_q || all > map.capacity(b) ? MLA_DEVERR_LENS : 0;
+  const int len = all - (n_q - 1 - tok);
+  // paged rows: every block the sequence uses must be a valid pool block
+  if (!bad && map.paged()) {
+    const int nblk = (int)(((int64_t)len + (int64_t(1) << map.shift) - 1) >> map.shift);
+    int any = 0;
+    for (int k = threadIdx.x; k < nblk; k += blockDim.x) any |= map.row(b, (int64_t)k << map.shift) < 0;
+    if (__syncthreads_or(any)) bad = MLA_DEVERR_TABLE;
+  }
+  if (bad) {
     for (int c = threadIdx.x; c < d_c; c += blockDim.x) out[c] = __builtin_nanf("");
     if (threadIdx.x == 0) {
       if (lse) lse[(size_t)v * n_h + h] = __builtin_nanf("");
-      if (err_flag) atomicOr(err_flag, MLA_DEVERR_LENS);
+      if (err_flag) atomicOr(err_flag, bad);
     }
     return;
   }
-  const int len = all - (n_q - 1 - tok);
   float q[kMaxRowPerLane];
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
@@ -158,7 +167,7 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n
   for (int k = 0; k < kMaxLatPerLane; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int j = wave; j < len; j += nw) {
-    const T* row = cache + (size_t)(off + j) * D;
+    const T* row = cache + (size_t)map.row(b, j) * D;
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxRowPerLane; ++k) {
@@ -245,19 +254,19 @@ hipError_t launch_absorb_generic(const Shape& s, int B, const void* q, bool q_f3
 
 hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c_src,
                                  size_t c_stride, const void* k_src, size_t k_stride, bool src_f32,
-                                 void* cache, const int32_t* offsets, int32_t* lens,
+                                 void* cache, const RowMap& map, int32_t* lens,
                                  int32_t* err_flag, hipStream_t st) {
   if (s.bf16)
     k_append<__bf16><<<B, 256, 0, st>>>(n_new, s.d_c, s.d_r, s.rope_base, c_src, c_stride, k_src,
-                                        k_stride, src_f32, (__bf16*)cache, offsets, lens, err_flag);
+                                        k_stride, src_f32, (__bf16*)cache, map, lens, err_flag);
   else
     k_append<float><<<B, 256, 0, st>>>(n_new, s.d_c, s.d_r, s.rope_base, c_src, c_stride, k_src,
-                                       k_stride, src_f32, (float*)cache, offsets, lens, err_flag);
+                                       k_stride, src_f32, (float*)cache, map, lens, err_flag);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                                 const void* cache, const int32_t* offsets, const int32_t* lens,
+                                 const void* cache, const RowMap& map, const int32_t* lens,
                                  float* o_lat, float* lse, int32_t* err_flag, hipStream_t st) {
   const int threads = 256, nw = threads / 64;
   size_t smem = sizeof(float) * (2 * nw + (size_t)nw * s.d_c);
@@ -265,11 +274,11 @@ hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_l
   float sl2 = s.scale * kLog2e;
   if (s.bf16)
     k_decode<__bf16><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const __bf16*)q_lat,
-                                                  (const __bf16*)q_pe, (const __bf16*)cache, offsets,
+                                                  (const __bf16*)q_pe, (const __bf16*)cache, map,
                                                   lens, o_lat, lse, err_flag);
   else
     k_decode<float><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const float*)q_lat,
-                                                 (const float*)q_pe, (const float*)cache, offsets,
+                                                 (const float*)q_pe, (const float*)cache, map,
                                                  lens, o_lat, lse, err_flag);
   return hipGetLastError();
 }

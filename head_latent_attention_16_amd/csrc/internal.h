@@ -17,6 +17,34 @@ struct Shape {
   bool bf16;
 };
 
+// Where the cached rows of a sequence live.
+//  * contiguous (table == nullptr): sequence b owns rows offsets[b] ..
+//    offsets[b+1]-1 of the cache, row t of the sequence is cache row
+//    offsets[b] + t;
+//  * paged: the cache is a pool of num_blocks blocks of 2^shift rows; row t of
+//    sequence b is row t & (2^shift - 1) of block table[b max_blocks + (t >> shift)],
+//    i.e. pool row (block << shift) + (t & (2^shift - 1)).
+// A block id outside [0, num_blocks) is reported as row -1 (the kernels then
+// read nothing through it and flag MLA_DEVERR_TABLE).
+struct RowMap {
+  const int32_t* offsets;
+  const int32_t* table;
+  int32_t max_blocks;
+  int32_t shift;
+  int32_t num_blocks;
+
+  __host__ __device__ bool paged() const { return table != nullptr; }
+  __device__ int64_t capacity(int b) const {
+    return table ? ((int64_t)max_blocks << shift) : (int64_t)(offsets[b + 1] - offsets[b]);
+  }
+  __device__ int64_t row(int b, int64_t t) const {
+    if (!table) return (int64_t)offsets[b] + t;
+    const int id = table[(size_t)b * max_blocks + (size_t)(t >> shift)];
+    if (id < 0 || id >= num_blocks) return -1;
+    return ((int64_t)id << shift) + (t & ((int64_t(1) << shift) - 1));
+  }
+};
+
 // ---- generic kernels: any dims, fp32 or bf16 storage, fp32 math -------------
 // Y[M,N] (fp32) = X[M,K] . W[N,K]^T ; X is fp32 or storage type, W storage type.
 hipError_t launch_linear_generic(const Shape& s, int M, int N, int K, const void* X, bool x_f32,
@@ -28,13 +56,13 @@ hipError_t launch_absorb_generic(const Shape& s, int B, const void* q, bool q_f3
 // k from k_src (stride k_stride); both fp32 or both the storage type.
 hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c_src,
                                  size_t c_stride, const void* k_src, size_t k_stride, bool src_f32,
-                                 void* cache, const int32_t* offsets, int32_t* lens,
+                                 void* cache, const RowMap& map, int32_t* lens,
                                  int32_t* err_flag, hipStream_t st);
 // B sequences with n_q query tokens each (n_q = 1: one decode query; n_q > 1:
 // the last n_q cached rows are the step's tokens, token i sees rows up to
 // lens[b] - n_q + i).  q_lat, q_pe, o_lat, lse are [B, n_q, n_h, ...].
 hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                                 const void* cache, const int32_t* offsets, const int32_t* lens,
+                                 const void* cache, const RowMap& map, const int32_t* lens,
                                  float* o_lat, float* lse, int32_t* err_flag, hipStream_t st);
 // In place on fp32 rows (stride ld): x[:cols] / sqrt(mean(x[:cols]^2) + eps) * w.
 hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
@@ -47,7 +75,7 @@ hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const vo
 bool decode_v3_supported(const Shape& s);
 size_t decode_v3_workspace(const Shape& s, int B, int n_q, int64_t total_rows_hint, int num_cu);
 hipError_t launch_decode_v3(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                            const void* cache, const int32_t* offsets, const int32_t* lens,
+                            const void* cache, const RowMap& map, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t ws_bytes, int num_cu, hipStream_t st);
 

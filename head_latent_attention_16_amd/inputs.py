@@ -227,6 +227,66 @@ def layer(seed: int = 0, B: int = 128, lo: int = 512, hi: int = 8192, spare: int
     return Workload("layer", "bf16", d, B, lens, offsets, cache, W=W, h_t=h_t, seed=seed)
 
 
+@dataclasses.dataclass
+class PagedPool:
+    """A block pool holding the rows of several layers' caches.
+
+    ``pool`` is [num_blocks * block_rows, d_c + d_R] (same storage as the
+    workload's cache); layer l's block table is ``tables[l]`` [B, max_blocks]
+    (int32; unused entries -1).  Row t of sequence b in layer l is pool row
+    tables[l][b, t // block_rows] * block_rows + t % block_rows.
+    """
+
+    pool: np.ndarray
+    tables: np.ndarray           # int32 [layers, B, max_blocks]
+    block_rows: int
+    num_blocks: int
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.tables.shape[2])
+
+
+def paged_pool(caches, lens, caps, block_rows: int = 64, seed: int = 0, spare_blocks: int = 0) -> PagedPool:
+    """Lay the rows of one or more layers' caches out in a shared block pool.
+
+    ``caches[l]`` is layer l's contiguous cache with sequence b in rows
+    offsets[b] .. offsets[b] + lens[b] - 1 (offsets = cumulative ``caps``);
+    each (layer, sequence) gets ceil(caps[b] / block_rows) blocks, and block
+    ids are a seeded random permutation over all layers (so neighbouring rows
+    of a sequence are not neighbours in the pool).  Unused rows of the pool
+    hold bf16/fp32 NaN so that a wrong row shows.  Layout only: no arithmetic.
+    """
+    caps = np.asarray(caps, np.int64)
+    lens = np.asarray(lens, np.int64)
+    L = len(caches)
+    B = len(lens)
+    nblk = (caps + block_rows - 1) // block_rows
+    max_blocks = int(max(1, nblk.max()))
+    total = int(nblk.sum()) * L + spare_blocks
+    perm = np.random.default_rng(seed + 7919).permutation(total).astype(np.int64)
+    D = caches[0].shape[1]
+    dt = caches[0].dtype
+    pool = np.empty((total * block_rows, D), dtype=dt)
+    pool[...] = np.uint16(0x7FC0) if dt == np.uint16 else np.float32("nan")
+    tables = np.full((L, B, max_blocks), -1, dtype=np.int32)
+    offsets = np.zeros(B + 1, np.int64)
+    offsets[1:] = np.cumsum(caps)
+    k = 0
+    for l in range(L):
+        for b in range(B):
+            for j in range(int(nblk[b])):
+                blk = int(perm[k])
+                k += 1
+                tables[l, b, j] = blk
+                lo = j * block_rows
+                n = int(min(block_rows, lens[b] - lo))
+                if n > 0:
+                    src = int(offsets[b]) + lo
+                    pool[blk * block_rows: blk * block_rows + n] = caches[l][src:src + n]
+    return PagedPool(pool=pool, tables=tables, block_rows=block_rows, num_blocks=total)
+
+
 WORKLOADS = {
     "tiny": tiny,
     "uniform": uniform,

@@ -57,8 +57,10 @@ extern "C" {
 #endif
 
 /* 2: adds mla_decode_attn_causal, mla_absorb_q_normed, mla_append_cache_normed;
- * the decode entry points reject more than 65535 query tokens up front. */
-#define MLA_ABI_VERSION 2
+ * the decode entry points reject more than 65535 query tokens up front.
+ * 3: adds mla_decode_attn_noalloc, the paged pool (mla_decode_attn_paged,
+ * mla_append_cache_paged) and MLA_DEVERR_TABLE. */
+#define MLA_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -75,6 +77,7 @@ typedef enum { MLA_DT_BF16 = 0, MLA_DT_F32 = 1 } mla_dtype_t;
 /* Device-side error bits OR-ed into *err_flag. */
 #define MLA_DEVERR_LENS 1       /* lens[b] < 1 or lens[b] > offsets[b+1]-offsets[b]   */
 #define MLA_DEVERR_OVERFLOW 2   /* an appended row would not fit in its region        */
+#define MLA_DEVERR_TABLE 4      /* a paged block id is outside [0, num_blocks)        */
 
 /* Model dimensions ("MLA模型结构详解", section "结合 DeepSeek 推理代码看 MLA":
  * n_heads, kv_lora_rank = d_c, qk_nope_head_dim = d_h, qk_rope_head_dim = d_R,
@@ -230,6 +233,44 @@ mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n
                                     int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
 size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q,
                                         int64_t total_rows_hint);
+
+/* Paged latent cache pool, shared by the layers of a model.
+ *
+ * The pages give the per-token cache of a whole model as layers x (d_c + d_R)
+ * numbers ("MLA latent attention / KV cache", section "MLA 的思路：把 KV 压缩成一个
+ * 小向量": 61 x 576 x 2 B, about 68 KB per token for DeepSeek-V3) and name
+ * PagedAttention-style memory management as the system-level companion of
+ * MLA ("给 KV Cache 瘦身：MQA · GQA · MLA", section "易错点与常见追问") without
+ * describing it.  Reading: the cache rows of every layer and sequence live in
+ * one pool of fixed-size blocks, pool [num_blocks, block_rows, d_c + d_R] in
+ * dims->dtype; each (layer, sequence) owns a list of blocks, and a layer's
+ * call gets that layer's block table, block_table [B, max_blocks] int32
+ * (device): row t of sequence b is row t % block_rows of block
+ * block_table[b * max_blocks + t / block_rows].  block_rows is a power of two
+ * >= 32 (at most 2^20) and max_blocks * block_rows <= 2^31 - 1; else
+ * MLA_ERR_SHAPE.  Only the entries of the blocks a call touches are read;
+ * an id outside [0, num_blocks) is never followed (MLA_DEVERR_TABLE; the
+ * sequence's outputs are NaN, or nothing is appended for it).
+ *
+ * mla_decode_attn_paged: mla_decode_attn over the pool (lens[b] <=
+ * max_blocks * block_rows, else MLA_DEVERR_LENS).  Same results as
+ * mla_decode_attn over a contiguous cache holding the same rows, with the
+ * same total_rows_hint (the split points depend on lens only); ws: at least
+ * mla_decode_attn_workspace(dims, B, total_rows_hint) bytes.
+ * mla_append_cache_paged: mla_append_cache into the pool (row lens[b] + i of
+ * sequence b; capacity max_blocks * block_rows); ws: at least
+ * mla_append_cache_workspace(dims, B, n_new, h_t != NULL) bytes. */
+mla_status_t mla_decode_attn_paged(const mla_dims_t* dims, int32_t B, const void* q_lat,
+                                   const void* q_pe, const void* pool, int32_t num_blocks,
+                                   int32_t block_rows, const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* lens, int64_t total_rows_hint, float* o_lat,
+                                   float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
+                                   void* stream);
+mla_status_t mla_append_cache_paged(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                                    const void* W_DKV, const void* W_KR, const void* kv_raw, void* pool,
+                                    int32_t num_blocks, int32_t block_rows, const int32_t* block_table,
+                                    int32_t max_blocks, int32_t* lens, int32_t* err_flag, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Output side ("MLA模型结构详解", worked example step 5: multiply by the value
  * part of wkv_b per head, flatten heads, output projection).

@@ -80,6 +80,8 @@ __all__ = [
     "layer_step",
     "cache_elems_per_token_layer",
     "cache_bytes_per_token",
+    "paged_rows",
+    "pool_bytes_per_token",
 ]
 
 
@@ -316,6 +318,30 @@ def layer_step(h_t, W, prior_c, prior_k, dims, scale, base=10000.0, seqs=None, n
         out[b] = dict(o=o, o_lat=o_lat, lse=lse, u=u[0], c_new=c_new[0], k_new=k_new[0],
                       q_C=q_C[0], q_R=q_R[0])
     return out
+
+
+# ---------------------------------------------------------------------------
+# A paged pool shared by the layers of a model.  [KV-2026], section "MLA 的思路：
+# 把 KV 压缩成一个小向量": the model-wide cache per token is layers x (d_c + d_R)
+# numbers; [KV-slim], section "易错点与常见追问", names PagedAttention-style memory
+# management without describing it.  Reading: fixed-size blocks of
+# block_rows rows, a block table per (layer, sequence); row t of a sequence is
+# row t % block_rows of block table[t // block_rows].
+# ---------------------------------------------------------------------------
+def paged_rows(pool, table_row, n, block_rows):
+    """Rows 0 .. n-1 of one sequence of a paged pool, in order: row t is pool
+    row table_row[t // block_rows] * block_rows + t % block_rows."""
+    pool = np.asarray(pool)
+    t = np.arange(n, dtype=np.int64)
+    blocks = np.asarray(table_row, dtype=np.int64)[t // block_rows]
+    if n and (blocks.min() < 0 or blocks.max() * block_rows >= len(pool)):
+        raise IndexError("block id outside the pool")
+    return pool[blocks * block_rows + t % block_rows]
+
+
+def pool_bytes_per_token(layers: int, d_c: int, d_r: int, bytes_per_elem: int) -> int:
+    """Bytes one token occupies across the layers of a pooled latent cache."""
+    return layers * (d_c + d_r) * bytes_per_elem
 
 
 # ---------------------------------------------------------------------------

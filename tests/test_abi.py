@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
     for st in range(7):
         s = lib.mla_status_string(st)
         assert isinstance(s, bytes) and len(s) > 0
@@ -172,3 +172,18 @@ def test_normed_validation(lib):
     assert ap(eps=float("inf")) == 2
     assert ap(n_new=0) == 0
     assert ap() == 6
+
+
+def test_paged_validation(lib):
+    d = v3()
+    one = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+    args = lambda nb, br, tab, mb: (ctypes.byref(d), 1, one, one, one, nb, br, tab, mb, one, 100, one, None,
+                                    None, one, 1 << 30, None)
+    for nb, br, mb in ((0, 64, 4), (8, 48, 4), (8, 16, 4), (8, 64, 0), (8, 1 << 21, 4), (8, 1 << 20, 4096)):
+        assert lib.mla_decode_attn_paged(*args(nb, br, one, mb)) == 2, (nb, br, mb)
+    assert lib.mla_decode_attn_paged(*args(8, 64, None, 4)) == 1
+    # append: same pool checks
+    app = lambda nb, br, tab: lib.mla_append_cache_paged(ctypes.byref(d), 1, 1, None, None, None, one, one, nb,
+                                                          br, tab, 4, one, None, None, 0, None)
+    assert app(8, 100, one) == 2
+    assert app(8, 64, None) == 1

@@ -627,3 +627,51 @@ def test_planted_mistakes_are_caught(monkeypatch):
     th = np.array([10000.0 ** (-(2.0 * i) / 8) for i in range(4)])
     zr = z * np.exp(1j * 9 * th)
     assert rel_err(bad_rope(x, 9), np.concatenate([zr.real, zr.imag], 1)) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# The paged pool reading: rows gathered through a block table.
+# ---------------------------------------------------------------------------
+def _scatter_by_hand(rows_per_seq, block_rows, rng):
+    """An independent pure-Python scatter into a pool with shuffled blocks."""
+    nblk = [(len(r) + block_rows - 1) // block_rows for r in rows_per_seq]
+    ids = list(rng.permutation(sum(nblk) + 3))
+    pool = [[float("nan")] * 3 for _ in range((sum(nblk) + 3) * block_rows)]
+    tables = []
+    for rows in rows_per_seq:
+        tab = [int(ids.pop()) for _ in range((len(rows) + block_rows - 1) // block_rows)]
+        for t, row in enumerate(rows):
+            pool[tab[t // block_rows] * block_rows + t % block_rows] = list(row)
+        tables.append(tab)
+    return np.array(pool), tables
+
+
+def test_paged_rows_round_trip_and_brute_force():
+    rng = np.random.default_rng(30)
+    for block_rows in (1, 4, 32):
+        seqs = [rng.standard_normal((n, 3)) for n in (1, 5, block_rows, block_rows + 1, 3 * block_rows + 2)]
+        pool, tables = _scatter_by_hand(seqs, block_rows, rng)
+        for rows, tab in zip(seqs, tables):
+            got = O.paged_rows(pool, tab, len(rows), block_rows)
+            assert np.array_equal(got, rows)
+            # a prefix is the prefix of the rows
+            assert np.array_equal(O.paged_rows(pool, tab, 1, block_rows), rows[:1])
+    # a mistaken reading (block-major within the table, t % n_blocks) does not round-trip
+    seqs = [rng.standard_normal((9, 3))]
+    pool, tables = _scatter_by_hand(seqs, 4, rng)
+    tab = np.asarray(tables[0])
+    t = np.arange(9)
+    wrong = pool[tab[t % len(tab)] * 4 + t // len(tab)]
+    assert not np.array_equal(wrong, seqs[0])
+    with pytest.raises(IndexError):
+        O.paged_rows(pool, [len(pool)], 1, 4)
+
+
+def test_pool_bytes_per_token_matches_pages(golden_dir):
+    # a pool shared by DeepSeek-V3's 61 layers: 61 x 576 bf16 per token, the
+    # pages' ~68 KB (exactly 70,272 B); 32K tokens of one sequence ~ 2.1 GB
+    g = _golden(golden_dir, "cache_sizes.json")
+    e = {x["id"]: x for x in g["entries"]}
+    per_tok = O.pool_bytes_per_token(61, 512, 64, 2)
+    assert per_tok == e["v3_mla_per_token"]["exact_bytes"] == 70272
+    assert abs(per_tok * 32768 / 2 ** 30 - 2.1) / 2.1 < 0.03
