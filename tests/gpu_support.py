@@ -66,12 +66,32 @@ def run_attention(u: Uploaded, hint=None, pos=None):
     o_lat = torch.empty(B, n_h, d.d_c, dtype=torch.float32, device="cuda")
     lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hint = hint if hint is not None else w.total_rows
+    ws, check_canary = canaried_workspace(L.decode_attn_workspace(d, B, hint))
     L.decode_attn(d, q_lat, q_pe, u.cache, u.offsets, u.lens, o_lat, lse,
-                  total_rows_hint=hint if hint is not None else w.total_rows, err_flag=err)
+                  total_rows_hint=hint, err_flag=err, ws=ws)
     o = torch.empty(B, n_h, d.d_v, dtype=torch.float32, device="cuda")
     L.project_out(d, o_lat, u.W["W_UV"], o=o)
     torch.cuda.synchronize()
+    check_canary()
     return dict(q_lat=q_lat, q_pe=q_pe, o_lat=o_lat, lse=lse, o=o, err=int(err.item()))
+
+
+CANARY_BYTES = 4096
+
+
+def canaried_workspace(nbytes: int):
+    """A workspace of exactly nbytes (as the library asked for) followed, in
+    the same allocation, by canary bytes; the returned check asserts that no
+    kernel wrote past the end of the workspace."""
+    buf = torch.empty(nbytes + CANARY_BYTES, dtype=torch.uint8, device="cuda")
+    buf[nbytes:].fill_(0xA5)
+
+    def check():
+        tail = buf[nbytes:].cpu()
+        assert bool((tail == 0xA5).all()), "a kernel wrote past the end of its workspace"
+
+    return buf[:nbytes], check
 
 
 def oracle_seq(w: I.Workload, b: int, heads=None, pos=None):

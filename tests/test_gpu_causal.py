@@ -83,11 +83,12 @@ def test_causal_single_token_is_the_plain_decode():
     assert np.array_equal(glse[:, 0], host_f64(lse))
 
 
-@pytest.mark.parametrize("B,n_q", [(16, 4), (13, 5), (40, 4), (300, 4)])
+@pytest.mark.parametrize("B,n_q", [(16, 4), (13, 5), (40, 4), (300, 4), (1024, 5)])
 def test_causal_many_tokens(B, n_q):
     """B n_q = 64 token-sequences is the largest count the split kernel scans
     in one wave, 65 and 160 go through its block scan, 1200 through the
-    separate scan kernel; sampled sequences are checked."""
+    separate scan kernel, 5120 past what the scan kernel holds in LDS;
+    sampled sequences (and the last) are checked."""
     rng = np.random.default_rng(B * 7 + n_q)
     lens = rng.integers(n_q, 90, size=B).astype(np.int32)
     w, q_lat, q_pe = _case(lens, n_q, seed=B + n_q)

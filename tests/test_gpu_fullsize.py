@@ -21,10 +21,10 @@ pytestmark = pytest.mark.gpu
 def _samples(name, w):
     lens = w.lens
     if name == "uniform":
-        return {0: [0, 77], 7: [31], 15: [64, 127]}
+        return {0: [0, 40, 77], 7: [31, 63], 15: [64, 127]}
     if name == "ragged":
-        return {0: [5], int(np.argmax(lens)): [100], int(np.argmin(lens)): [0, 127], w.B - 1: [64]}
-    return {0: [3], w.B - 1: [64, 127]}
+        return {0: [5, 33], int(np.argmax(lens)): [100, 50], int(np.argmin(lens)): [0, 127], w.B - 1: [64]}
+    return {0: [3, 45], w.B - 1: [64, 127]}
 
 
 @pytest.mark.parametrize("name", ["uniform", "ragged", "long"])
@@ -42,6 +42,18 @@ def test_full_size_attention(name):
         compare(o_lat[b][heads], ro_lat, f"{tag} o_lat")
         compare(o[b][heads], ro, f"{tag} o")
         compare(lse[b][heads], rlse, f"{tag} lse", max_abs=2e-2, mean_abs=2e-3, norm_max=1e-2, norm_mean=2e-3)
+    # every head (all four 32-head groups of the split kernel) of two
+    # sequences: the latent definition evaluated by the oracle on the
+    # kernel's own q_lat / q_pe (that definition is pinned to the explicit
+    # route on the CPU)
+    ql, qp = host_f64(r["q_lat"]), host_f64(r["q_pe"])
+    two = [int(np.argmin(w.lens)), int(np.argmax(w.lens))] if name == "ragged" else [0, w.B - 1]
+    for b in two:
+        rows = w.f64(w.seq_rows(b))
+        ref, rl = O.latent_attention(ql[b], qp[b], rows[:, :512], rows[:, 512:], O.scale_for(128, 64))
+        compare(o_lat[b], ref, f"{name} b={b} all heads o_lat")
+        compare(lse[b], rl, f"{name} b={b} all heads lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2,
+                norm_mean=1e-3)
 
 
 @pytest.mark.parametrize("norms", [False, True])

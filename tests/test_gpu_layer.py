@@ -70,3 +70,39 @@ def test_layer_step_v3(B, lo, hi, check):
         compare(host_f64(o[b]), r["o"], f"o[{b}]")
         compare(host_f64(lse[b]), r["lse"], f"lse[{b}]")
         compare(host_f64(u[b]), r["u"], f"u[{b}]")
+
+
+def test_append_selection_matrix_bit_exact():
+    """h_t through the fused W_DKV | W_KR MFMA GEMM with 0/1 selection
+    weights: every product is exact and the fp32 sums add zeros, so the
+    cached c^KV is exactly the selected features of h_t; at position 0 the
+    rotation is the identity, so k^R is exact too.  At later positions k^R is
+    within one bf16 rounding of the fp64 rotation of the selected features."""
+    B, D, dm = 128, 576, 7168
+    rng = np.random.default_rng(77)
+    d = L.Dims.make(128, 512, 64, 128, 128, d_model=dm, d_q=1536, dtype="bf16")
+    h = I.bf16_bits(rng.standard_normal((B, dm), dtype=np.float32))
+    pick = rng.permutation(dm)[:D]
+    W = np.zeros((D, dm), np.float32)
+    W[np.arange(D), pick] = 1.0
+    Wb = I.bf16_bits(W)
+    pos = rng.integers(0, 5000, size=B).astype(np.int32)
+    pos[:64] = 0
+    caps = pos.astype(np.int64) + 1
+    offsets = np.concatenate([[0], np.cumsum(caps)]).astype(np.int32)
+    cache = torch.zeros(int(offsets[-1]), D, dtype=torch.bfloat16, device="cuda")
+    lens = dev(pos.copy())
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.append_cache(d, cache, dev(offsets), lens, 1, h_t=dev(h), W_DKV=dev(Wb[:512]), W_KR=dev(Wb[512:]),
+                   err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and np.array_equal(lens.cpu().numpy(), pos + 1)
+    got = cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    rows = got[offsets[:-1] + pos]
+    sel = h[:, pick]
+    assert np.array_equal(rows[:, :512], sel[:, :512])                   # c^KV bit-exact
+    assert np.array_equal(rows[:64, 512:], sel[:64, 512:])               # k^R at position 0
+    kr = O.rope(I.bf16_to_f32(sel[64:, 512:]).astype(np.float64), pos[64:].astype(np.float64))
+    gk = I.bf16_to_f32(rows[64:, 512:]).astype(np.float64)
+    ulp = np.maximum(np.abs(kr), 1e-30) * 2.0 ** -8
+    assert np.all(np.abs(gk - kr) <= ulp + 1e-12), float(np.max(np.abs(gk - kr) / ulp))

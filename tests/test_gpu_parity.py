@@ -161,11 +161,13 @@ def test_decode_more_workgroups_than_rows():
         compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
 
 
-@pytest.mark.parametrize("B", [1024, 1100])
+@pytest.mark.parametrize("B", [1024, 1100, 5000])
 def test_decode_large_batch(B):
     """Many short sequences: B = 1024 is the largest batch whose lengths the
     split kernel scans itself, B = 1100 goes through the separate scan
-    kernel.  Every 37th sequence and the last ones are checked."""
+    kernel, and B = 5000 exceeds what the scan kernel keeps in LDS (its
+    prefix and charge counts are then read back from memory).  Every 37th
+    sequence and the last ones are checked."""
     rng = np.random.default_rng(B)
     lens = rng.integers(1, 41, size=B).astype(np.int32)
     w = small_v3(lens, seed=B)
