@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIB_PATH selects another build of the same library (the host-sanitized
+# one used by the CPU ABI checks); by default the in-tree libmla.so.
+LIB_PATH = os.environ.get("MLA_LIB_PATH") or os.path.join(_HERE, "libmla.so")
 
 MLA_OK = 0
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",

@@ -252,7 +252,7 @@ extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 
-const char* mla_status_string(mla_status_t st) {
+const char* mla_status_string(int32_t st) {
   switch (st) {
     case MLA_OK: return "ok";
     case MLA_ERR_NULL: return "a required pointer is NULL";

@@ -293,8 +293,9 @@ size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with
  * 0 if dims is NULL or invalid. */
 size_t mla_cache_row_bytes(const mla_dims_t* dims);
 
-/* Static, NUL-terminated description of a status code. */
-const char* mla_status_string(mla_status_t status);
+/* Static, NUL-terminated description of a status code (any int32 value;
+ * values that are not an mla_status_t give "unknown status"). */
+const char* mla_status_string(int32_t status);
 
 /* MLA_ABI_VERSION of the built library. */
 int32_t mla_abi_version(void);
