@@ -82,6 +82,11 @@ __all__ = [
     "cache_bytes_per_token",
     "paged_rows",
     "pool_bytes_per_token",
+    "e4m3_value",
+    "e4m3_encode",
+    "e4m3_decode",
+    "quantize_rows",
+    "dequantize_rows",
 ]
 
 
@@ -342,6 +347,77 @@ def paged_rows(pool, table_row, n, block_rows):
 def pool_bytes_per_token(layers: int, d_c: int, d_r: int, bytes_per_elem: int) -> int:
     """Bytes one token occupies across the layers of a pooled latent cache."""
     return layers * (d_c + d_r) * bytes_per_elem
+
+
+# ---------------------------------------------------------------------------
+# A low-precision latent cache.  [KV-slim], section "易错点与常见追问", names KV
+# quantisation (INT8/INT4) as a companion of MLA; [MLA-struct], worked example
+# step 3 notes that precision and quantisation change the real memory
+# footprint.  Neither page fixes a format or a scale.  Reading: each cached row
+# [c^KV | k^R] (d_c + d_R numbers) is stored as 8-bit floats in the OCP E4M3
+# format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+# finite 448, smallest subnormal 2^-9, codes 0x7F / 0xFF are NaN) with one
+# fp32 scale per row: s = amax / 448 and code = E4M3(clamp(x * (448 / amax),
+# -448, 448)) rounded to nearest, ties to even; amax = max |x| over the row
+# (s = 1 and all codes 0 for an all-zero row).  The products and quotients are
+# float32 operations, as a GPU kernel takes them.  A row dequantises to
+# value(code) * s.
+# ---------------------------------------------------------------------------
+def e4m3_value(code: int) -> float:
+    """The number an E4M3 code stands for (the format's definition)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_POS = np.array([e4m3_value(c) for c in range(0x7F)])   # codes 0x00 .. 0x7E, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float32 values to E4M3 codes: nearest, ties to the even code,
+    |x| >= 448 saturating to +-448 (NaN maps to 0x7F)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    neg = np.signbit(x)
+    i = np.searchsorted(_E4M3_POS, np.minimum(a, 448.0))       # first code >= a
+    i = np.minimum(i, 0x7E)
+    lo = np.maximum(i - 1, 0)
+    exact = _E4M3_POS[i] == a
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[i] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (i % 2 == 0))
+    code = np.where(exact | pick_hi, i, lo)
+    code = np.where(a >= 448.0, 0x7E, code).astype(np.uint8)
+    code = np.where(neg, code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    table = np.array([e4m3_value(c) for c in range(256)])
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def quantize_rows(x):
+    """Per-row E4M3 quantisation of float32 rows: (codes uint8 [n, D], scales float32 [n])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1), safe / np.float32(448.0)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(448.0) / safe).astype(np.float32)
+    v = (x * inv[..., None]).astype(np.float32)
+    v = np.clip(v, np.float32(-448.0), np.float32(448.0))
+    return e4m3_encode(v), scale
+
+
+def dequantize_rows(codes, scales):
+    """value(code) * scale, in float64."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
 # ---------------------------------------------------------------------------

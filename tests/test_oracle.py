@@ -675,3 +675,79 @@ def test_pool_bytes_per_token_matches_pages(golden_dir):
     per_tok = O.pool_bytes_per_token(61, 512, 64, 2)
     assert per_tok == e["v3_mla_per_token"]["exact_bytes"] == 70272
     assert abs(per_tok * 32768 / 2 ** 30 - 2.1) / 2.1 < 0.03
+
+
+# ---------------------------------------------------------------------------
+# The low-precision cache reading: E4M3 codes with one scale per row.
+# ---------------------------------------------------------------------------
+def _e4m3_by_hand(v):
+    """Pure-Python nearest E4M3 code by search over every code of v's sign:
+    clamp to [-448, 448], nearest value, ties to the even code (whose last
+    bit, the mantissa's, is 0)."""
+    if math.isnan(v):
+        return 0x7F
+    sign = 0x80 if math.copysign(1.0, v) < 0 else 0x00
+    t = max(-448.0, min(448.0, v))
+    best = None
+    for m in range(0x7F):
+        c = sign | m
+        d = abs(O.e4m3_value(c) - t)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_e4m3_format_points():
+    # values fixed by the format's definition
+    assert O.e4m3_value(0x7E) == 448.0 and math.isnan(O.e4m3_value(0x7F)) and math.isnan(O.e4m3_value(0xFF))
+    assert O.e4m3_value(0x01) == 2.0 ** -9 and O.e4m3_value(0x08) == 2.0 ** -6 and O.e4m3_value(0x38) == 1.0
+    assert O.e4m3_value(0x80) == 0.0 and O.e4m3_value(0xBE) == -1.75
+    vals = [O.e4m3_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))                     # increasing, no duplicates
+    # every finite code round-trips
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes).astype(np.float32)), codes)
+
+
+def test_e4m3_rounding_ties_and_saturation():
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 17.0: 0x58, 19.0: 0x5A, 464.0: 0x7E, 500.0: 0x7E, 1e9: 0x7E,
+             2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, -448.0: 0xFE, -1e9: 0xFE}
+    for v, code in cases.items():
+        assert int(O.e4m3_encode(np.float32(v))) == code, (v, hex(int(O.e4m3_encode(np.float32(v)))), hex(code))
+    rng = np.random.default_rng(31)
+    xs = np.concatenate([rng.standard_normal(300) * 50, rng.uniform(-470, 470, 300),
+                         rng.standard_normal(100) * 2.0 ** -7]).astype(np.float32)
+    got = O.e4m3_encode(xs)
+    for x, c in zip(xs, got):
+        assert int(c) == _e4m3_by_hand(float(x)), (float(x), hex(int(c)))
+
+
+def test_quantize_rows_bounds_and_special_rows():
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((50, 576)) * rng.uniform(0.01, 100, (50, 1))).astype(np.float32)
+    codes, scales = O.quantize_rows(x)
+    deq = O.dequantize_rows(codes, scales)
+    amax = np.max(np.abs(x), axis=1)
+    # the row maximum maps to +-448 (code 0x7E / 0xFE), so it is kept to a float32 rounding
+    i = np.argmax(np.abs(x), axis=1)
+    assert np.all((codes[np.arange(50), i] & 0x7F) == 0x7E)
+    assert np.allclose(np.abs(deq[np.arange(50), i]), amax, rtol=2e-7)
+    # every element within half an E4M3 step (relative 2^-4 of its binade) plus
+    # the subnormal floor 2^-10 * scale
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None] * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    # an all-zero row: scale 1, zero codes; a constant row: every code -448,
+    # the value back to a float32 rounding of the scale
+    c0, s0 = O.quantize_rows(np.zeros((1, 8), np.float32))
+    assert s0[0] == 1.0 and not c0.any()
+    c1, s1 = O.quantize_rows(np.full((1, 8), -3.25, np.float32))
+    assert np.all(c1 == 0xFE)
+    assert np.allclose(O.dequantize_rows(c1, s1), -3.25, rtol=2e-7, atol=0)
+    # a planted mistake: rounding toward zero instead of to nearest breaks the
+    # half-step bound
+    v = np.clip(x * (np.float32(448) / amax.astype(np.float32))[:, None], -448, 448)
+    mags = np.array([O.e4m3_value(c) for c in range(0x7F)])
+    toward0 = np.sign(v) * mags[np.searchsorted(mags, np.abs(v), side="right") - 1]
+    bad = np.abs(toward0 * scales[:, None] - x)
+    assert np.any(bad > bound)
