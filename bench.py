@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     # default: the largest single-GPU attention workload (ragged, 1.29 GB of cache per step)
     p.add_argument("--workload", default="ragged",
-                   choices=["uniform", "ragged", "long", "layer", "causal", "paged"])
+                   choices=["uniform", "ragged", "long", "layer", "causal", "paged", "fp8"])
     p.add_argument("--block-rows", type=int, default=64, help="paged workload: rows per pool block")
     p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
     p.add_argument("--norms", action="store_true",
@@ -69,13 +69,15 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic(w):
+def algorithmic(w, row_bytes=None):
     """Bytes and FLOPs of one attention call: the cache read once, q in, o_lat
-    out; with n_q tokens per sequence token i scores T - n_q + i + 1 rows."""
+    out; with n_q tokens per sequence token i scores T - n_q + i + 1 rows.
+    row_bytes: bytes of one cached row (default bf16: 2 (d_c + d_r))."""
     n_h, d_c, d_r, n_q = w.dims["n_h"], w.dims["d_c"], w.dims["d_r"], w.n_q
     tokens = int(w.total_rows)
     nq_tok = w.B * n_q
-    byts = tokens * (d_c + d_r) * 2 + nq_tok * n_h * (d_c + d_r) * 2 + nq_tok * n_h * d_c * 4
+    rb = row_bytes if row_bytes is not None else (d_c + d_r) * 2
+    byts = tokens * rb + nq_tok * n_h * (d_c + d_r) * 2 + nq_tok * n_h * d_c * 4
     scored = n_q * tokens - w.B * (n_q * (n_q - 1) // 2)     # rows seen, summed over tokens
     flops = scored * 2 * n_h * ((d_c + d_r) + d_c)
     return tokens, byts, flops
@@ -180,8 +182,9 @@ def main():
     t0 = time.perf_counter()
     w = (I.layer(spare=spare) if name == "layer"
          else I.causal(n_q=args.n_q) if name == "causal"
-         else I.make("ragged") if name == "paged" else I.make(name))
+         else I.make("ragged") if name in ("paged", "fp8") else I.make(name))
     paged = name == "paged"
+    fp8 = name == "fp8"
     n_q = w.n_q
     log(f"  done in {time.perf_counter() - t0:.1f}s: B={w.B} total_rows={w.total_rows}")
     d = w.dims
@@ -194,7 +197,15 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    if paged:
+    if fp8:
+        # the ragged batch's rows as E4M3 codes with one fp32 scale per row
+        # (quantised on the host here; mla_append_cache_fp8 writes the same
+        # codes on the device)
+        import oracle as O
+        codes, scales = O.quantize_rows(I.bf16_to_f32(w.cache))
+        base = {"cache": dev(codes), "scales": dev(scales), "offsets": dev(w.offsets), "lens": dev(w.lens)}
+        del codes, scales
+    elif paged:
         # the ragged batch's rows in a pool of block_rows-row blocks with shuffled ids
         pp = I.paged_pool([w.cache], w.lens, w.lens, args.block_rows, seed=1)
         base = {"cache": dev(pp.pool), "table": dev(pp.tables[0]), "offsets": dev(w.offsets),
@@ -229,7 +240,10 @@ def main():
     ws_dec = torch.empty(L.decode_attn_causal_workspace(dims, B, n_q, hint), dtype=torch.uint8, device="cuda")
 
     def attend(s):
-        if paged:
+        if fp8:
+            L.decode_attn_fp8(dims, q_lat, q_pe, s["cache"], s["scales"], s["offsets"], s["lens"], o_lat, lse,
+                              total_rows_hint=hint, ws=ws_dec)
+        elif paged:
             L.decode_attn_paged(dims, q_lat, q_pe, s["cache"], args.block_rows, s["table"], s["lens"], o_lat, lse,
                                 total_rows_hint=hint, ws=ws_dec)
         elif n_q > 1:
@@ -313,7 +327,8 @@ def main():
         ev.append((a, b))
     torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    tokens, byts, flops = algorithmic(w)
+    # 8-bit rows: d_c + d_r codes and a 4-byte scale
+    tokens, byts, flops = algorithmic(w, row_bytes=(d["d_c"] + d["d_r"] + 4) if fp8 else None)
     if layer:
         # Every step appends one row per sequence to the copy it uses: step j
         # (j = warmup + i) on copy j % copies attends over the prior rows plus
@@ -337,7 +352,9 @@ def main():
           "layer": f"full layer step B={w.B} prior T~U[512,8192] sum={w.total_rows}",
           "causal": f"causal B={w.B} T={int(w.lens[0])} n_q={n_q} new tokens per sequence",
           "paged": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows} in a paged pool of "
-                   f"{args.block_rows}-row blocks"}[name]
+                   f"{args.block_rows}-row blocks",
+          "fp8": f"ragged B={w.B} T~U[1024,32768] sum={w.total_rows}, 8-bit E4M3 cache rows with a "
+                 f"per-row scale"}[name]
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -357,19 +374,27 @@ def main():
                             else "absorb_q+append+decode_attn+project_out(o,u)") if layer
                    else "absorb_q+decode_attn_causal+project_out(o)" if n_q > 1
                    else "absorb_q+decode_attn_paged+project_out(o)" if paged
+                   else "absorb_q+decode_attn_fp8+project_out(o)" if fp8
                    else "absorb_q+decode_attn+project_out(o)",
                    "input_copies_rotated": copies,
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                      "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn_paged" if paged
-                                else "mla_decode_attn")
+                                else "mla_decode_attn_fp8" if fp8 else "mla_decode_attn")
                      + " (split attention with length scan + combine)",
                      "decode_us": dec_ms * 1e3, "algorithmic_bytes": byts,
                      "mfma_tflops": flops / (dec_ms * 1e-3) / 1e12,
                      "mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
+    # the binding roof: the one whose time at peak is longer (8-bit rows carry
+    # 480 FLOP per byte, past the bf16 ridge, so the matrix cores bind there)
+    mfma_tflops = flops / (dec_ms * 1e-3) / 1e12
+    if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9):
+        out["roofline"].update({"bound": "mfma", "achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
+                                "hbm_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS})
     if not args.no_cpu_baseline and n_q == 1:
         log(f"oracle baseline on the host ({args.cpu_seconds:.0f} s budget) ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

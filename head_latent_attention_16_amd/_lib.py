@@ -33,7 +33,8 @@ EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_absorb_q_normed", "mla_append_cache_normed",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
            "mla_status_string", "mla_abi_version", "mla_decode_attn_noalloc",
-           "mla_decode_attn_paged", "mla_append_cache_paged")
+           "mla_decode_attn_paged", "mla_append_cache_paged", "mla_append_cache_fp8",
+           "mla_decode_attn_fp8")
 
 
 class MLAError(RuntimeError):
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                   i32),
         "mla_append_cache_paged": ([D, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp],
                                    i32),
+        "mla_append_cache_fp8": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "mla_decode_attn_fp8": ([D, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_causal": ([D, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_causal_workspace": ([D, i32, i32, i64], sz),
         "mla_project_out": ([D, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -307,6 +310,56 @@ def append_cache_paged(dims: Dims, pool, block_rows: int, block_table, lens, n_n
                                   _ptr(block_table), block_table.shape[1], _ptr(lens), _ptr(err_flag), w, wn,
                                   _stream(stream))
     _check("mla_append_cache_paged", st)
+
+
+def append_cache_fp8(dims: Dims, cache8, scales, offsets, lens, n_new: int, kv_raw=None, h_t=None,
+                     W_DKV=None, W_KR=None, err_flag=None, ws=None, stream=None):
+    """append_cache into an 8-bit cache: E4M3 codes cache8 [rows, d_c + d_r]
+    (uint8) and one fp32 scale per row in scales [rows]."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(cache8, scales, offsets, lens, kv_raw, h_t, W_DKV, W_KR, err_flag)
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(lens, B, torch.int32, "lens")
+    _need(kv_raw, B * n_new * (dims.d_c + dims.d_r), dt, "kv_raw")
+    _need(h_t, B * n_new * dims.d_model, dt, "h_t")
+    rows = cache8.numel() // (dims.d_c + dims.d_r)
+    _need(scales, rows, torch.float32, "scales")
+    if cache8.dtype != torch.uint8:
+        raise ValueError("cache8 must be uint8")
+    nbytes = int(L.mla_append_cache_workspace(ctypes.byref(dims), B, n_new, int(h_t is not None)))
+    ws = _workspace(nbytes, ws, cache8.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_append_cache_fp8(ctypes.byref(dims), B, n_new, _ptr(h_t), _ptr(W_DKV), _ptr(W_KR), _ptr(kv_raw),
+                                _ptr(cache8), _ptr(scales), _ptr(offsets), _ptr(lens), _ptr(err_flag), w, wn,
+                                _stream(stream))
+    _check("mla_append_cache_fp8", st)
+
+
+def decode_attn_fp8(dims: Dims, q_lat, q_pe, cache8, scales, offsets, lens, o_lat, lse=None,
+                    total_rows_hint: Optional[int] = None, err_flag=None, ws=None, stream=None):
+    """decode_attn over an 8-bit cache (codes x row scale)."""
+    L = lib()
+    B = lens.shape[0]
+    dt = dims.torch_dtype
+    _dev(q_lat, q_pe, cache8, scales, offsets, lens, o_lat, lse, err_flag)
+    _need(q_lat, B * dims.n_h * dims.d_c, dt, "q_lat")
+    _need(q_pe, B * dims.n_h * dims.d_r, dt, "q_pe")
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(o_lat, B * dims.n_h * dims.d_c, torch.float32, "o_lat")
+    _need(lse, B * dims.n_h, torch.float32, "lse")
+    rows = cache8.numel() // (dims.d_c + dims.d_r)
+    _need(scales, rows, torch.float32, "scales")
+    if cache8.dtype != torch.uint8:
+        raise ValueError("cache8 must be uint8")
+    hint = int(total_rows_hint) if total_rows_hint is not None else max(1, rows)
+    ws = _workspace(decode_attn_workspace(dims, B, hint), ws, cache8.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_decode_attn_fp8(ctypes.byref(dims), B, _ptr(q_lat), _ptr(q_pe), _ptr(cache8), _ptr(scales),
+                               _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse), _ptr(err_flag), w, wn,
+                               _stream(stream))
+    _check("mla_decode_attn_fp8", st)
 
 
 def project_out(dims: Dims, o_lat, W_UV, o=None, u=None, W_O=None, ws=None, stream=None):

@@ -156,8 +156,9 @@ mla_status_t paged_map(int32_t num_blocks, int32_t block_rows, const int32_t* bl
   return MLA_OK;
 }
 
+// scales != NULL: `cache` holds E4M3 codes with one fp32 scale per row.
 mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
-                           const void* q_pe, const void* cache, const RowMap& map,
+                           const void* q_pe, const void* cache, const float* scales, const RowMap& map,
                            const int32_t* lens, int64_t total_rows_hint, float* o_lat, float* lse,
                            int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
@@ -178,12 +179,12 @@ mla_status_t decode_common(const mla_dims_t* dims, int32_t B, int32_t n_q, const
     if ((st = device_ready(&info)) != MLA_OK) return st;
     const size_t need = decode_v3_workspace(s, B, n_q, total_rows_hint, info.num_cu);
     if (ws_bytes < need) return MLA_ERR_WORKSPACE;
-    return launched(launch_decode_v3(s, B, n_q, q_lat, q_pe, cache, map, lens, total_rows_hint,
+    return launched(launch_decode_v3(s, B, n_q, q_lat, q_pe, cache, scales, map, lens, total_rows_hint,
                                      o_lat, lse, err_flag, ws, ws_bytes, info.num_cu,
                                      (hipStream_t)stream));
   }
   if ((st = device_ready(&info)) != MLA_OK) return st;
-  return launched(launch_decode_generic(s, B, n_q, q_lat, q_pe, cache, map, lens, o_lat, lse,
+  return launched(launch_decode_generic(s, B, n_q, q_lat, q_pe, cache, scales, map, lens, o_lat, lse,
                                         err_flag, (hipStream_t)stream));
 }
 
@@ -376,10 +377,11 @@ size_t mla_append_cache_workspace(const mla_dims_t* dims, int32_t B, int32_t n_n
 namespace {
 // kv_norm_w != NULL: the new latents c^KV are normalised in place
 // (root-mean-square, eps) before they are written.
+// scales != NULL: `cache` receives E4M3 codes with one fp32 scale per row.
 mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
                            const void* W_DKV, const void* kv_norm_w, float eps, const void* W_KR,
-                           const void* kv_raw, void* cache, const RowMap& map, int32_t* lens,
-                           int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+                           const void* kv_raw, void* cache, float* scales, const RowMap& map,
+                           int32_t* lens, int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
@@ -399,6 +401,13 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
   if ((st = device_ready(&info)) != MLA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   const size_t D = (size_t)(s.d_c + s.d_r);
+  // the row writer: the storage type, or 8-bit codes with a row scale
+  auto write_rows = [&](const void* c_src, size_t c_stride, const void* k_src, size_t k_stride, bool src_f32) {
+    return scales ? launch_append_fp8(s, B, n_new, c_src, c_stride, k_src, k_stride, src_f32, cache, scales, map,
+                                      lens, err_flag, hs)
+                  : launch_append_generic(s, B, n_new, c_src, c_stride, k_src, k_stride, src_f32, cache, map,
+                                          lens, err_flag, hs);
+  };
   if (from_hidden) {
     // c = x W_DKV^T and k = x W_KR^T into fp32 scratch, then rotate + write.
     const int M = B * n_new;
@@ -410,8 +419,7 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
       if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, D, kv_norm_w, eps, hs) != hipSuccess)
         return MLA_ERR_LAUNCH;
-      return launched(launch_append_generic(s, B, n_new, kc, D, kc + s.d_c, D, true, cache, map,
-                                            lens, err_flag, hs));
+      return launched(write_rows(kc, D, kc + s.d_c, D, true));
     }
     float* kr = kc + (size_t)M * s.d_c;
     hipError_t e = linear(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, part, hs);
@@ -420,13 +428,11 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
       return MLA_ERR_LAUNCH;
     e = linear(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
-    return launched(launch_append_generic(s, B, n_new, kc, (size_t)s.d_c, kr, (size_t)s.d_r, true,
-                                          cache, map, lens, err_flag, hs));
+    return launched(write_rows(kc, (size_t)s.d_c, kr, (size_t)s.d_r, true));
   }
   const char* raw = (const char*)kv_raw;
   // kv_raw is in the storage type: fp32 rows are read as fp32, bf16 rows as bf16.
-  return launched(launch_append_generic(s, B, n_new, raw, D, raw + (size_t)s.d_c * elem_bytes(s), D,
-                                        !s.bf16, cache, map, lens, err_flag, hs));
+  return launched(write_rows(raw, D, raw + (size_t)s.d_c * elem_bytes(s), D, !s.bf16));
 }
 }  // namespace
 
@@ -436,7 +442,7 @@ mla_status_t mla_append_cache(const mla_dims_t* dims, int32_t B, int32_t n_new, 
                               const void* W_DKV, const void* W_KR, const void* kv_raw, void* cache,
                               const int32_t* offsets, int32_t* lens, int32_t* err_flag, void* ws,
                               size_t ws_bytes, void* stream) {
-  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache, contiguous_map(offsets), lens,
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache, nullptr, contiguous_map(offsets), lens,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -450,7 +456,7 @@ mla_status_t mla_append_cache_normed(const mla_dims_t* dims, int32_t B, int32_t 
   if (st != MLA_OK) return st;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return MLA_ERR_SHAPE;
   if (B > 0 && n_new > 0 && (!h_t || !kv_norm_w)) return MLA_ERR_NULL;
-  return append_common(dims, B, n_new, h_t, W_DKV, kv_norm_w, eps, W_KR, nullptr, cache, contiguous_map(offsets), lens,
+  return append_common(dims, B, n_new, h_t, W_DKV, kv_norm_w, eps, W_KR, nullptr, cache, nullptr, contiguous_map(offsets), lens,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -463,7 +469,7 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t B, const void* q_la
                              const int32_t* lens, int64_t total_rows_hint, float* o_lat,
                              float* lse, int32_t* err_flag, void* ws, size_t ws_bytes,
                              void* stream) {
-  return decode_common(dims, B, 1, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, nullptr, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -479,7 +485,7 @@ mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n
                                     const int32_t* offsets, const int32_t* lens,
                                     int64_t total_rows_hint, float* o_lat, float* lse,
                                     int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
-  return decode_common(dims, B, n_q, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, n_q, q_lat, q_pe, cache, nullptr, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, ws_bytes, stream);
 }
 
@@ -500,7 +506,7 @@ mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t B, const vo
   if (need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
   void* ws = nullptr;
   if (need > 0 && scratch_ptr_current(&ws) != hipSuccess) return MLA_ERR_DEVICE;
-  return decode_common(dims, B, 1, q_lat, q_pe, cache, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
+  return decode_common(dims, B, 1, q_lat, q_pe, cache, nullptr, contiguous_map(offsets), lens, total_rows_hint, o_lat, lse,
                        err_flag, ws, need, stream);
 }
 
@@ -515,7 +521,7 @@ mla_status_t mla_decode_attn_paged(const mla_dims_t* dims, int32_t B, const void
   if (st != MLA_OK) return st;
   RowMap map;
   if ((st = paged_map(num_blocks, block_rows, block_table, max_blocks, &map)) != MLA_OK) return st;
-  return decode_common(dims, B, 1, q_lat, q_pe, pool, map, lens, total_rows_hint, o_lat, lse, err_flag,
+  return decode_common(dims, B, 1, q_lat, q_pe, pool, nullptr, map, lens, total_rows_hint, o_lat, lse, err_flag,
                        ws, ws_bytes, stream);
 }
 
@@ -529,8 +535,26 @@ mla_status_t mla_append_cache_paged(const mla_dims_t* dims, int32_t B, int32_t n
   if (st != MLA_OK) return st;
   RowMap map;
   if ((st = paged_map(num_blocks, block_rows, block_table, max_blocks, &map)) != MLA_OK) return st;
-  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, pool, map, lens, err_flag,
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, pool, nullptr, map, lens, err_flag,
                        ws, ws_bytes, stream);
+}
+
+mla_status_t mla_decode_attn_fp8(const mla_dims_t* dims, int32_t B, const void* q_lat, const void* q_pe,
+                                 const uint8_t* cache8, const float* scales, const int32_t* offsets,
+                                 const int32_t* lens, int64_t total_rows_hint, float* o_lat, float* lse,
+                                 int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+  if (dims && B > 0 && !scales) return MLA_ERR_NULL;
+  return decode_common(dims, B, 1, q_lat, q_pe, cache8, scales, contiguous_map(offsets), lens, total_rows_hint,
+                       o_lat, lse, err_flag, ws, ws_bytes, stream);
+}
+
+mla_status_t mla_append_cache_fp8(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                                  const void* W_DKV, const void* W_KR, const void* kv_raw, uint8_t* cache8,
+                                  float* scales, const int32_t* offsets, int32_t* lens, int32_t* err_flag,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (dims && B > 0 && n_new > 0 && !scales) return MLA_ERR_NULL;
+  return append_common(dims, B, n_new, h_t, W_DKV, nullptr, 0.f, W_KR, kv_raw, cache8, scales,
+                       contiguous_map(offsets), lens, err_flag, ws, ws_bytes, stream);
 }
 
 size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {

@@ -73,10 +73,28 @@ constexpr int SPL_PER = SPL_MAXB / THREADS;           // sequences per lane
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // Largest |O / l| a partial may carry in fp16 (max finite 65504); a piece
 // above it is flagged and its sequence recomputed by the fallback.
 constexpr float PART_MAX = 65000.0f;
 
+
+// 8-bit cache rows (E4M3 codes, one power-of-two scale per row, stored as
+// fp32): a 32-row tile is
+// 18 KiB of codes plus 128 bytes of scales.  Each wave issues five DMAs per
+// tile: waves 0-2 five 1 KiB code chunks each, wave 3 the last three
+// chunks, the scales (one dword per lane) and a repeat of the last chunk, so
+// that every wave waits for the same count.  Four 8-bit stages are followed
+// in LDS by two bf16 tiles in the layout of the 16-bit path: after a tile
+// lands, the workgroup converts it (code value x scale, exact in bf16) into
+// one of them, and the QK / PV code of the 16-bit path runs unchanged.
+constexpr int F8_ROWB = DK;                       // 576 bytes per row
+constexpr int F8_TILEB = TILE * F8_ROWB;          // 18432
+constexpr int F8_STAGE = F8_TILEB + 256;          // codes + scale area
+constexpr int F8_DPW = 5;
+constexpr int F8_BF16_OFF = NSTAGE * F8_STAGE;    // 74752: first bf16 tile
+constexpr int F8_LDS = F8_BF16_OFF + 2 * TILEB;   // 148480
+static_assert(F8_TILEB / 1024 == 18 && F8_BF16_OFF % 1024 == 0, "8-bit tile layout");
 
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
 static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
@@ -368,7 +386,8 @@ struct SplitArgs {
   float* lse;
   const __bf16* q_lat;
   const __bf16* q_pe;
-  const char* cache;     // the cache, or the block pool (paged)
+  const char* cache;     // the cache, or the block pool (paged), or 8-bit codes
+  const float* scales;   // 8-bit cache: one scale per row
   RowMap map;
   const int64_t* prefix;
   _Float16* part_o;
@@ -427,6 +446,14 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
                : "s"(uniform_ptr((const char*)p))
                : "memory");
   return v;
+}
+
+// Direct global -> LDS of one dword per lane (lane i's 4 bytes land at M0 + 4 i).
+__device__ __forceinline__ void dma_4B_at(uint32_t lds_addr, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "m0");
 }
 
 template <int N>
@@ -491,9 +518,13 @@ __device__ __forceinline__ int swz(int r) {
 // One wave per SIMD holds Q (144 VGPRs) and O (256 accumulation registers);
 // latency is hidden inside the wave by loading LDS fragments several
 // steps ahead of the MFMA that consumes them.
-template <bool SCAN, bool PAGED>
+// MODE: 0 contiguous bf16 cache, 1 paged bf16 pool, 2 contiguous 8-bit cache.
+template <bool SCAN, int MODE>
 __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
+  constexpr bool PAGED = MODE == 1;
+  constexpr bool FP8 = MODE == 2;
+  constexpr int DPW = FP8 ? F8_DPW : DMA_PER_WAVE;   // DMAs per wave and tile
+  __shared__ __attribute__((aligned(1024))) char lds[FP8 ? F8_LDS : NSTAGE * TILEB];
   // in-kernel scan (SCAN): prefix of the valid lengths and the offsets
   __shared__ int64_t s_pre[SCAN ? SPL_MAXB + 1 : 1];
   __shared__ int32_t s_off[SCAN ? SPL_MAXB : 1];
@@ -850,7 +881,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     const int t0 = (int)(pos - seq_begin);
     const int seg_len = (int)(seg_end - pos);
     const int ntiles = (seg_len + TILE - 1) / TILE;
-    const char* rows = a.cache + ((size_t)off_b + (size_t)t0) * ROWB;
+    const char* rows = a.cache + ((size_t)off_b + (size_t)t0) * (FP8 ? F8_ROWB : ROWB);
     // paged: this sequence's row of the block table
     const int32_t* tbl = PAGED ? a.map.table + (size_t)seq_of(b, a.n_q) * a.map.max_blocks : nullptr;
 
@@ -907,6 +938,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       const char* a0;
       const char* a1;
       uint32_t thr, bound;
+      const char* scl;   // 8-bit cache: the tile's first scale
+      int nv;            // 8-bit cache: valid rows in the tile (clamped to TILE)
     };
     bool bad_tbl = false;
     auto dma_src = [&](int t) -> TileSrc {
@@ -914,7 +947,15 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       const int nv = seg_len - ts * TILE;
       TileSrc r;
       r.bound = nv >= TILE ? (uint32_t)TILEB - 16u : (uint32_t)(nv * ROWB - 16);
-      if constexpr (!PAGED) {
+      r.scl = nullptr;
+      r.nv = 0;
+      if constexpr (FP8) {
+        r.bound = nv >= TILE ? (uint32_t)F8_TILEB - 16u : (uint32_t)(nv * F8_ROWB - 16);
+        r.a0 = r.a1 = rows + (size_t)ts * F8_TILEB;
+        r.thr = 0xffffffffu;
+        r.scl = (const char*)(a.scales + (size_t)off_b + (size_t)t0 + (size_t)ts * TILE);
+        r.nv = nv < TILE ? nv : TILE;
+      } else if constexpr (!PAGED) {
         r.a0 = r.a1 = rows + (size_t)ts * TILEB;
         r.thr = 0xffffffffu;
       } else {
@@ -938,17 +979,72 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       if constexpr (!PAGED) dma_16B(lds_addr, off, src.a0);
       else dma_16B_at(lds_addr, (off < src.thr ? src.a0 : src.a1) + off);
     };
+    // LDS stage (DMA target) of tile t
+    auto stage_of = [&](int t) -> uint32_t {
+      return lds0 + (uint32_t)((t % NSTAGE) * (FP8 ? F8_STAGE : TILEB));
+    };
+    // 8-bit cache: the DMA slot k of this wave -> code chunk (0..17), or -1
+    // for the scales (wave 3, slot 3); wave 3's slot 4 repeats chunk 17.
+    auto f8_chunk = [&](int k) -> int {
+      if (wave < 3) return 5 * wave + k;
+      return k < 3 ? 15 + k : (k == 3 ? -1 : 17);
+    };
+    // the k-th DMA of this wave for a tile
+    auto dma_slot = [&](int k, uint32_t stage_lds, const TileSrc& src) {
+      if constexpr (FP8) {
+        const int j = f8_chunk(k);
+        if (j < 0) {
+          dma_4B_at(stage_lds + F8_TILEB, src.scl + 4 * (lane_id < src.nv ? lane_id : src.nv - 1));
+        } else {
+          dma_16B(stage_lds + (uint32_t)(j * 1024), min((uint32_t)((64 * j + lane_id) * 16), src.bound), src.a0);
+        }
+      } else {
+        dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), min(dma_off(k), src.bound), src);
+      }
+    };
     auto issue_tile = [&](int t) {
       const TileSrc src = dma_src(t);
-      const uint32_t stage_lds = lds0 + (uint32_t)((t % NSTAGE) * TILEB);
-      uint32_t off[DMA_PER_WAVE];
+      const uint32_t stage_lds = stage_of(t);
 #pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) off[k] = min(dma_off(k), src.bound);
-#pragma unroll
-      for (int k = 0; k < DMA_PER_WAVE; ++k) dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), off[k], src);
+      for (int k = 0; k < DPW; ++k) dma_slot(k, stage_lds, src);
+    };
+    // bf16 tile read by QK / PV for tile t
+    auto ctile = [&](int t) -> const MLA_LDS char* {
+      if constexpr (FP8) return (const MLA_LDS char*)lds + F8_BF16_OFF + (t & 1) * TILEB;
+      else return (const MLA_LDS char*)lds + (t % NSTAGE) * TILEB;
+    };
+    // 8-bit cache: convert the landed tile t into its bf16 tile (the whole
+    // workgroup; 2304 chunks of 8 codes, nine per thread): code value x row
+    // scale (exact in bf16: a power-of-two scale), stored at the swizzled chunk position.
+    auto convert_tile = [&](int t) {
+      if constexpr (FP8) {
+        const MLA_LDS char* src = (const MLA_LDS char*)lds + (t % NSTAGE) * F8_STAGE;
+        const MLA_LDS float* sc = (const MLA_LDS float*)(src + F8_TILEB);
+        MLA_LDS char* dst = (MLA_LDS char*)lds + F8_BF16_OFF + (t & 1) * TILEB;
+#pragma unroll 3
+        for (int k = 0; k < (TILE * CHUNKS) / THREADS; ++k) {
+          const int q = (int)threadIdx.x + THREADS * k;
+          const int r = q / CHUNKS, c = q - r * CHUNKS;
+          const u32x2 raw = *(const MLA_LDS u32x2*)(src + r * F8_ROWB + c * 8);
+          const float sr = sc[r];
+          bf16x8 o;
+          const floatx2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[0], false);
+          const floatx2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[0], true);
+          const floatx2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[1], false);
+          const floatx2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[1], true);
+          o[0] = (__bf16)(f0[0] * sr);
+          o[1] = (__bf16)(f0[1] * sr);
+          o[2] = (__bf16)(f1[0] * sr);
+          o[3] = (__bf16)(f1[1] * sr);
+          o[4] = (__bf16)(f2[0] * sr);
+          o[5] = (__bf16)(f2[1] * sr);
+          o[6] = (__bf16)(f3[0] * sr);
+          o[7] = (__bf16)(f3[1] * sr);
+          *(MLA_LDS bf16x8*)(dst + r * ROWB + ((c ^ swz(r)) << 4)) = o;
+        }
+      }
     };
     // Wait for tile `it`: the tiles it+1 and it+2 were issued after it.
-    auto wait_tile = [&]() { wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>(); };
 
     // Three tiles ahead: tile it+3 goes into the stage of tile it-1.
     for (int t = 0; t < NSTAGE - 1; ++t) issue_tile(t);
@@ -965,7 +1061,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
     // ---- S^T = K . Q^T of tile t, fragments loaded QK_PF steps ahead ----
     auto qk = [&](int t, floatx16& S) {
-      const MLA_LDS char* T = (const MLA_LDS char*)lds + (t % NSTAGE) * TILEB;
+      const MLA_LDS char* T = ctile(t);
       uint32_t qk_off[4];
       make_qk_off(qk_off);
       bf16x8 kf[QK_PF];
@@ -1035,7 +1131,11 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 
     // ---- prologue: QK of tile 0 and the reference max ----
     floatx16 S_cur;
-    wait_vm_then_barrier<(NSTAGE - 2) * DMA_PER_WAVE>();   // tile 0 landed
+    wait_vm_then_barrier<(NSTAGE - 2) * DPW>();   // tile 0 landed
+    if constexpr (FP8) {
+      convert_tile(0);
+      barrier_all_lds();
+    }
     qk(0, S_cur);
     qk_schedule();
     {
@@ -1055,7 +1155,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       // source of tile it+3, DMA'd during PV below (paged: its block ids are
       // fetched here, where no LDS read is in flight)
       const TileSrc nsrc = dma_src(it + NSTAGE - 1);
-      const MLA_LDS char* T = (const MLA_LDS char*)lds + (it % NSTAGE) * TILEB;
+      const MLA_LDS char* T = ctile(it);
       bf16x8 P[2];
       floatx16 S_next;
       // PV A-fragments of tile it, PV_PF pairs ahead of their MFMAs.  The
@@ -1079,14 +1179,20 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         // refilled below.
         uint32_t qk_off[4];
         make_qk_off(qk_off);   // lane arithmetic only: ahead of the wait
-        wait_vm_then_barrier<(NSTAGE - 3) * DMA_PER_WAVE>();
+        wait_vm_then_barrier<(NSTAGE - 3) * DPW>();
+        if constexpr (FP8) {
+          // tile it+1 landed for every wave; its bf16 tile held tile it-1,
+          // whose PV every wave has finished
+          convert_tile(it + 1);
+          barrier_all_lds();
+        }
         floatx16 Sc = S_cur;
         asm volatile("" : "+v"(Sc));
         // QK of tile it+1 with the softmax of tile it in its MFMA gaps: one
         // pair of weights after each odd MFMA, their row sums later; the
         // scheduling barriers keep every step where it is written, so the
         // fragment prefetch and the VALU placement stay as planned.
-        const MLA_LDS char* Tn = (const MLA_LDS char*)lds + ((it + 1) % NSTAGE) * TILEB;
+        const MLA_LDS char* Tn = ctile(it + 1);
         bf16x8 kf[QK_PF];
 #pragma unroll
         for (int j = 0; j < QK_PF; ++j)
@@ -1140,7 +1246,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       // clock, so issuing them back to back stalls the wave for ~600 cycles.
       {
         const int nt = it + NSTAGE - 1;
-        const uint32_t stage_lds = lds0 + (uint32_t)((nt % NSTAGE) * TILEB);
+        const uint32_t stage_lds = stage_of(nt);
         // DMA k goes out after MFMA 3k+2 (its source offset is recomputed
         // there: a few VALU instructions in the MFMA gaps, no registers held).
 #pragma unroll
@@ -1157,9 +1263,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
             pa[s % PV_PF][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
           }
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, P[kk2], O[cb], 0, 0, 0);
-          if (s % 3 == 2 && s / 3 < DMA_PER_WAVE)
-            dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + s / 3) * 1024), min(dma_off(s / 3), nsrc.bound),
-                nsrc);
+          if (s % 3 == 2 && s / 3 < DPW) dma_slot(s / 3, stage_lds, nsrc);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 1);
 #pragma unroll
@@ -1239,6 +1343,8 @@ struct CombineArgs {
   const __bf16* q_lat;
   const __bf16* q_pe;
   const __bf16* cache;
+  const uint8_t* cache8;   // 8-bit cache (codes) or NULL
+  const float* scales;     // its row scales
   RowMap map;
   const int4* seqinfo;
   const int32_t* flags;
@@ -1281,17 +1387,28 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
     // the split kernel; the check only keeps a bad id from being followed)
     const int64_t rj = a.map.row(seq, j);
     if (rj < 0) continue;
-    const __bf16* r = a.cache + (size_t)rj * DK;
+    // the row's values: bf16, or 8-bit code value x row scale
+    float rv[DK / 64];
+    if (a.cache8) {
+      const uint8_t* r8 = a.cache8 + (size_t)rj * DK;
+      const float sc = a.scales[rj];
+#pragma unroll
+      for (int k = 0; k < DK / 64; ++k) rv[k] = __builtin_amdgcn_cvt_f32_fp8((int)r8[lane + 64 * k], 0) * sc;
+    } else {
+      const __bf16* r = a.cache + (size_t)rj * DK;
+#pragma unroll
+      for (int k = 0; k < DK / 64; ++k) rv[k] = (float)r[lane + 64 * k];
+    }
     float sdot = 0.f;
 #pragma unroll
-    for (int k = 0; k < DK / 64; ++k) sdot += q[k] * (float)r[lane + 64 * k];
+    for (int k = 0; k < DK / 64; ++k) sdot += q[k] * rv[k];
     const float x = wave_sum(sdot) * a.scale_log2;
     const float mn = fmaxf(m, x);
     const float al = exp2f(m - mn);
     const float p = exp2f(x - mn);
     l = l * al + p;
 #pragma unroll
-    for (int k = 0; k < DC / 64; ++k) acc[k] = acc[k] * al + p * (float)r[lane + 64 * k];
+    for (int k = 0; k < DC / 64; ++k) acc[k] = acc[k] * al + p * rv[k];
     m = mn;
   }
   if (lane == 0) { st_m[wave] = m; st_l[wave] = l; }
@@ -1547,7 +1664,7 @@ size_t decode_v3_workspace(const Shape&, int B, int n_q, int64_t total_rows_hint
 }
 
 hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_lat, const void* q_pe,
-                            const void* cache, const RowMap& map, const int32_t* lens,
+                            const void* cache, const float* scales, const RowMap& map, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t, int num_cu, hipStream_t st) {
   const int B = B_seq * n_q;
@@ -1569,6 +1686,7 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   a.q_lat = (const __bf16*)q_lat;
   a.q_pe = (const __bf16*)q_pe;
   a.cache = (const char*)cache;
+  a.scales = scales;
   a.map = map;
   a.prefix = prefix;
   a.part_o = (_Float16*)(w + L.o_off);
@@ -1577,16 +1695,20 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   a.n_q = n_q;
   a.G = G;
   a.scale_log2 = s.scale * kLog2e;
+  // 8-bit cache (scales given), paged pool, or contiguous bf16 cache
+  const int mode = scales ? 2 : map.paged() ? 1 : 0;
   if (B <= SPL_MAXB) {
-    if (map.paged()) k_split<true, true><<<G, THREADS, 0, st>>>(a);
-    else k_split<true, false><<<G, THREADS, 0, st>>>(a);
+    if (mode == 2) k_split<true, 2><<<G, THREADS, 0, st>>>(a);
+    else if (mode == 1) k_split<true, 1><<<G, THREADS, 0, st>>>(a);
+    else k_split<true, 0><<<G, THREADS, 0, st>>>(a);
   } else {
     k_sched<<<1, SCHED_THREADS, 0, st>>>(B, n_q, G, map, lens, prefix, (int32_t*)(w + L.cnt_off), rec, seqinfo,
                                          err_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (map.paged()) k_split<false, true><<<G, THREADS, 0, st>>>(a);
-    else k_split<false, false><<<G, THREADS, 0, st>>>(a);
+    if (mode == 2) k_split<false, 2><<<G, THREADS, 0, st>>>(a);
+    else if (mode == 1) k_split<false, 1><<<G, THREADS, 0, st>>>(a);
+    else k_split<false, 0><<<G, THREADS, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1594,6 +1716,8 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   c.q_lat = a.q_lat;
   c.q_pe = a.q_pe;
   c.cache = (const __bf16*)cache;
+  c.cache8 = scales ? (const uint8_t*)cache : nullptr;
+  c.scales = scales;
   c.map = map;
   c.err_flag = err_flag;
   c.seqinfo = seqinfo;

@@ -116,13 +116,84 @@ __global__ void __launch_bounds__(256) k_append(int n_new, int d_c, int d_r, dou
   if (threadIdx.x == 0) lens[b] = len + n_new;
 }
 
+// 8-bit cache rows: one block per sequence.  For each new row its d_c + d_r
+// values in fp32 (c copied, k rotated as in k_append) are staged in LDS, the
+// row's largest magnitude amax comes from a block reduction, and the row is
+// stored as E4M3 codes of x / 2^e (round to nearest even) with scale 2^e,
+// e the smallest integer with amax <= 448 2^e (clamped to [-120, 120]; an
+// all-zero row: codes 0, scale 1).  Dividing by a power of two is exact, so
+// the codes depend only on the row's fp32 values.
+__global__ void __launch_bounds__(256) k_append_fp8(int n_new, int d_c, int d_r, double base,
+                                                    const void* c_src, size_t c_stride,
+                                                    const void* k_src, size_t k_stride, bool src_f32,
+                                                    uint8_t* __restrict__ cache, float* __restrict__ scales,
+                                                    RowMap map, int32_t* __restrict__ lens, int32_t* err_flag) {
+  extern __shared__ float row[];   // d_c + d_r
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int D = d_c + d_r;
+  const int len = lens[b];
+  if (len < 0 || (int64_t)len + n_new > map.capacity(b)) {
+    if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, MLA_DEVERR_OVERFLOW);
+    return;
+  }
+  bool bad = false;
+  for (int i = 0; i < n_new; ++i) bad |= map.row(b, (int64_t)len + i) < 0;
+  if (bad) {
+    if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, MLA_DEVERR_TABLE);
+    return;
+  }
+  const int half = d_r / 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = 0; i < n_new; ++i) {
+    const size_t idx = (size_t)b * n_new + i;
+    const size_t cs = idx * c_stride, ks = idx * k_stride;
+    for (int c = threadIdx.x; c < d_c; c += blockDim.x) row[c] = ld_any(c_src, src_f32, cs + c);
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+      float cn, sn;
+      rope_cos_sin((int64_t)len + i, j, d_r, base, &cn, &sn);
+      const float lo = ld_any(k_src, src_f32, ks + j);
+      const float hi = ld_any(k_src, src_f32, ks + half + j);
+      row[d_c + j] = lo * cn - hi * sn;
+      row[d_c + half + j] = hi * cn + lo * sn;
+    }
+    __syncthreads();
+    float m = 0.f;
+    for (int f = threadIdx.x; f < D; f += blockDim.x) m = fmaxf(m, fabsf(row[f]));
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int E = 0;
+    const float mant = frexpf(amax, &E);          // amax = mant 2^E, 0.5 <= mant < 1
+    int e = amax == 0.f ? 0 : (mant <= 0.875f ? E - 9 : E - 8);   // 448 = 0.875 2^9
+    e = e < -120 ? -120 : (e > 120 ? 120 : e);
+    const float inv = ldexpf(1.f, -e);
+    const int64_t r = map.row(b, (int64_t)len + i);
+    uint8_t* dst = cache + (size_t)r * D;
+    for (int pr = threadIdx.x; 2 * pr < D; pr += blockDim.x) {
+      const int f = 2 * pr;
+      const float v0 = fminf(fmaxf(row[f] * inv, -448.f), 448.f);
+      const float v1 = f + 1 < D ? fminf(fmaxf(row[f + 1] * inv, -448.f), 448.f) : 0.f;
+      const int code = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+      dst[f] = (uint8_t)(code & 0xff);
+      if (f + 1 < D) dst[f + 1] = (uint8_t)((code >> 8) & 0xff);
+    }
+    if (threadIdx.x == 0) scales[r] = ldexpf(1.f, e);
+    __syncthreads();   // row[] and red[] are reused by the next row
+  }
+  if (threadIdx.x == 0) lens[b] = len + n_new;
+}
+
 // One block (4 waves) per (head, sequence).  Each wave streams every 4th row,
 // keeps an online softmax (running max m, sum l, accumulator), and the four
 // partial states are merged through LDS at the end.
-template <typename T>
+// F8: the cache holds E4M3 codes with one fp32 scale per row (scales).
+template <typename T, bool F8>
 __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n_q, float scale_log2,
                                                 const T* __restrict__ q_lat, const T* __restrict__ q_pe,
-                                                const T* __restrict__ cache, RowMap map,
+                                                const void* __restrict__ cache, const float* __restrict__ scales,
+                                                RowMap map,
                                                 const int32_t* __restrict__ lens,
                                                 float* __restrict__ o_lat, float* __restrict__ lse,
                                                 int32_t* err_flag) {
@@ -167,12 +238,18 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n
   for (int k = 0; k < kMaxLatPerLane; ++k) acc[k] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int j = wave; j < len; j += nw) {
-    const T* row = cache + (size_t)map.row(b, j) * D;
+    const int64_t rj = map.row(b, j);
+    // element f of row rj: the stored value, or code value x row scale
+    const float rs = F8 ? scales[rj] : 1.f;
+    auto elem = [&](int f) -> float {
+      if constexpr (F8) return __builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t*)cache)[(size_t)rj * D + f], 0) * rs;
+      else return ld((const T*)cache + (size_t)rj * D, f);
+    };
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxRowPerLane; ++k) {
       int f = lane + 64 * k;
-      if (f < D) s += q[k] * ld(row, f);
+      if (f < D) s += q[k] * elem(f);
     }
     s = wave_sum(s) * scale_log2;
     float mn = fmaxf(m, s);
@@ -182,7 +259,7 @@ __global__ void __launch_bounds__(256) k_decode(int n_h, int d_c, int d_r, int n
 #pragma unroll
     for (int k = 0; k < kMaxLatPerLane; ++k) {
       int f = lane + 64 * k;
-      if (f < d_c) acc[k] = acc[k] * a + p * ld(row, f);
+      if (f < d_c) acc[k] = acc[k] * a + p * elem(f);
     }
     m = mn;
   }
@@ -265,21 +342,39 @@ hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c
   return hipGetLastError();
 }
 
+hipError_t launch_append_fp8(const Shape& s, int B, int n_new, const void* c_src, size_t c_stride,
+                             const void* k_src, size_t k_stride, bool src_f32, void* cache, float* scales,
+                             const RowMap& map, int32_t* lens, int32_t* err_flag, hipStream_t st) {
+  k_append_fp8<<<B, 256, sizeof(float) * (size_t)(s.d_c + s.d_r), st>>>(
+      n_new, s.d_c, s.d_r, s.rope_base, c_src, c_stride, k_src, k_stride, src_f32, (uint8_t*)cache, scales, map,
+      lens, err_flag);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                                 const void* cache, const RowMap& map, const int32_t* lens,
-                                 float* o_lat, float* lse, int32_t* err_flag, hipStream_t st) {
+                                 const void* cache, const float* scales, const RowMap& map,
+                                 const int32_t* lens, float* o_lat, float* lse, int32_t* err_flag,
+                                 hipStream_t st) {
   const int threads = 256, nw = threads / 64;
   size_t smem = sizeof(float) * (2 * nw + (size_t)nw * s.d_c);
   dim3 grid(s.n_h, B * n_q);
   float sl2 = s.scale * kLog2e;
-  if (s.bf16)
-    k_decode<__bf16><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const __bf16*)q_lat,
-                                                  (const __bf16*)q_pe, (const __bf16*)cache, map,
-                                                  lens, o_lat, lse, err_flag);
+  if (s.bf16 && scales)
+    k_decode<__bf16, true><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const __bf16*)q_lat,
+                                                        (const __bf16*)q_pe, cache, scales, map,
+                                                        lens, o_lat, lse, err_flag);
+  else if (s.bf16)
+    k_decode<__bf16, false><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const __bf16*)q_lat,
+                                                         (const __bf16*)q_pe, cache, nullptr, map,
+                                                         lens, o_lat, lse, err_flag);
+  else if (scales)
+    k_decode<float, true><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const float*)q_lat,
+                                                       (const float*)q_pe, cache, scales, map,
+                                                       lens, o_lat, lse, err_flag);
   else
-    k_decode<float><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const float*)q_lat,
-                                                 (const float*)q_pe, (const float*)cache, map,
-                                                 lens, o_lat, lse, err_flag);
+    k_decode<float, false><<<grid, threads, smem, st>>>(s.n_h, s.d_c, s.d_r, n_q, sl2, (const float*)q_lat,
+                                                        (const float*)q_pe, cache, nullptr, map,
+                                                        lens, o_lat, lse, err_flag);
   return hipGetLastError();
 }
 

@@ -61,9 +61,16 @@ hipError_t launch_append_generic(const Shape& s, int B, int n_new, const void* c
 // B sequences with n_q query tokens each (n_q = 1: one decode query; n_q > 1:
 // the last n_q cached rows are the step's tokens, token i sees rows up to
 // lens[b] - n_q + i).  q_lat, q_pe, o_lat, lse are [B, n_q, n_h, ...].
+// scales != NULL: the cache holds E4M3 codes with one fp32 scale per row.
 hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                                 const void* cache, const RowMap& map, const int32_t* lens,
-                                 float* o_lat, float* lse, int32_t* err_flag, hipStream_t st);
+                                 const void* cache, const float* scales, const RowMap& map,
+                                 const int32_t* lens, float* o_lat, float* lse, int32_t* err_flag,
+                                 hipStream_t st);
+// New rows -> 8-bit cache rows (E4M3 codes [rows, d_c + d_r], scales [rows]);
+// sources as launch_append_generic.
+hipError_t launch_append_fp8(const Shape& s, int B, int n_new, const void* c_src, size_t c_stride,
+                             const void* k_src, size_t k_stride, bool src_f32, void* cache, float* scales,
+                             const RowMap& map, int32_t* lens, int32_t* err_flag, hipStream_t st);
 // In place on fp32 rows (stride ld): x[:cols] / sqrt(mean(x[:cols]^2) + eps) * w.
 hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
                           float eps, hipStream_t st);
@@ -74,8 +81,10 @@ hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const vo
 // ---- V3 fast path (bf16, d_c = 512, d_r = 64, n_h = 128) --------------------
 bool decode_v3_supported(const Shape& s);
 size_t decode_v3_workspace(const Shape& s, int B, int n_q, int64_t total_rows_hint, int num_cu);
+// scales != NULL: the cache holds 8-bit E4M3 codes [rows, d_c + d_r] with one
+// fp32 scale per row (contiguous map only).
 hipError_t launch_decode_v3(const Shape& s, int B, int n_q, const void* q_lat, const void* q_pe,
-                            const void* cache, const RowMap& map, const int32_t* lens,
+                            const void* cache, const float* scales, const RowMap& map, const int32_t* lens,
                             int64_t total_rows_hint, float* o_lat, float* lse, int32_t* err_flag,
                             void* ws, size_t ws_bytes, int num_cu, hipStream_t st);
 

@@ -59,7 +59,8 @@ extern "C" {
 /* 2: adds mla_decode_attn_causal, mla_absorb_q_normed, mla_append_cache_normed;
  * the decode entry points reject more than 65535 query tokens up front.
  * 3: adds mla_decode_attn_noalloc, the paged pool (mla_decode_attn_paged,
- * mla_append_cache_paged) and MLA_DEVERR_TABLE. */
+ * mla_append_cache_paged), MLA_DEVERR_TABLE and the 8-bit cache
+ * (mla_append_cache_fp8, mla_decode_attn_fp8). */
 #define MLA_ABI_VERSION 3
 
 typedef enum {
@@ -271,6 +272,35 @@ mla_status_t mla_append_cache_paged(const mla_dims_t* dims, int32_t B, int32_t n
                                     int32_t num_blocks, int32_t block_rows, const int32_t* block_table,
                                     int32_t max_blocks, int32_t* lens, int32_t* err_flag, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* Low-precision latent cache.  "给 KV Cache 瘦身：MQA · GQA · MLA" (section
+ * "易错点与常见追问") names KV quantisation as the companion of MLA, and
+ * "MLA模型结构详解" (worked example step 3) notes that precision changes the
+ * real footprint; neither fixes a format.  Reading: each row [c^KV | k^R] is
+ * stored as d_c + d_R OCP E4M3 codes (1 byte each; largest finite 448) with
+ * one power-of-two scale per row (stored as fp32): scale = 2^e with e the
+ * smallest integer for which amax <= 448 2^e (clamped to [-120, 120]), amax
+ * = max |x| over the row's d_c + d_R values (k^R after its rotation), and
+ * code = E4M3(x / scale) rounded to nearest even; an all-zero row gets codes
+ * 0 and scale 1.  A row then holds (d_c + d_R) + 4 bytes: 580 at V3 dims,
+ * about half of the 1152-byte bf16 row.  The row's value is value(code) x
+ * scale, exactly representable in bf16, which is what the decode feeds to the
+ * matrix cores.
+ *
+ * mla_append_cache_fp8: mla_append_cache writing codes into cache8 [rows,
+ * d_c + d_r] (uint8) and the row's scale into scales [rows] (fp32); h_t,
+ * the weights and kv_raw are in dims->dtype.
+ * mla_decode_attn_fp8: mla_decode_attn over such a cache (q_lat, q_pe in
+ * dims->dtype); ws: at least mla_decode_attn_workspace(dims, B, hint) bytes.
+ * Inputs must be finite. */
+mla_status_t mla_append_cache_fp8(const mla_dims_t* dims, int32_t B, int32_t n_new, const void* h_t,
+                                  const void* W_DKV, const void* W_KR, const void* kv_raw, uint8_t* cache8,
+                                  float* scales, const int32_t* offsets, int32_t* lens, int32_t* err_flag,
+                                  void* ws, size_t ws_bytes, void* stream);
+mla_status_t mla_decode_attn_fp8(const mla_dims_t* dims, int32_t B, const void* q_lat, const void* q_pe,
+                                 const uint8_t* cache8, const float* scales, const int32_t* offsets,
+                                 const int32_t* lens, int64_t total_rows_hint, float* o_lat, float* lse,
+                                 int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
 
 /* Output side ("MLA模型结构详解", worked example step 5: multiply by the value
  * part of wkv_b per head, flatten heads, output projection).

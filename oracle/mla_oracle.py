@@ -85,6 +85,7 @@ __all__ = [
     "e4m3_value",
     "e4m3_encode",
     "e4m3_decode",
+    "row_scale_exponent",
     "quantize_rows",
     "dequantize_rows",
 ]
@@ -357,10 +358,12 @@ def pool_bytes_per_token(layers: int, d_c: int, d_r: int, bytes_per_elem: int) -
 # [c^KV | k^R] (d_c + d_R numbers) is stored as 8-bit floats in the OCP E4M3
 # format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
 # finite 448, smallest subnormal 2^-9, codes 0x7F / 0xFF are NaN) with one
-# fp32 scale per row: s = amax / 448 and code = E4M3(clamp(x * (448 / amax),
-# -448, 448)) rounded to nearest, ties to even; amax = max |x| over the row
-# (s = 1 and all codes 0 for an all-zero row).  The products and quotients are
-# float32 operations, as a GPU kernel takes them.  A row dequantises to
+# power-of-two scale per row, s = 2^e with e the smallest integer for which
+# amax <= 448 * 2^e (amax = max |x| over the row; e clamped to [-120, 120]; an
+# all-zero row has s = 1), and code = E4M3(x / s) rounded to nearest, ties to
+# even.  A power-of-two scale keeps x / s exact and makes value(code) * s
+# exactly representable in bf16, so a kernel may feed the dequantised row to
+# bf16 matrix cores without a further rounding.  A row dequantises to
 # value(code) * s.
 # ---------------------------------------------------------------------------
 def e4m3_value(code: int) -> float:
@@ -402,17 +405,22 @@ def e4m3_decode(codes) -> np.ndarray:
     return table[np.asarray(codes, dtype=np.uint8)]
 
 
+def row_scale_exponent(amax: float) -> int:
+    """Smallest e with amax <= 448 * 2^e (amax > 0), clamped to [-120, 120]."""
+    m, E = math.frexp(float(amax))            # amax = m 2^E, 0.5 <= m < 1
+    e = E - 9 if m <= 0.875 else E - 8        # 448 = 0.875 * 2^9
+    return max(-120, min(120, e))
+
+
 def quantize_rows(x):
-    """Per-row E4M3 quantisation of float32 rows: (codes uint8 [n, D], scales float32 [n])."""
+    """Per-row E4M3 quantisation of float32 rows with a power-of-two scale:
+    (codes uint8 [n, D], scales float32 [n])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x), axis=-1)
-    zero = amax == 0
-    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
-    scale = np.where(zero, np.float32(1), safe / np.float32(448.0)).astype(np.float32)
-    inv = np.where(zero, np.float32(1), np.float32(448.0) / safe).astype(np.float32)
-    v = (x * inv[..., None]).astype(np.float32)
-    v = np.clip(v, np.float32(-448.0), np.float32(448.0))
-    return e4m3_encode(v), scale
+    e = np.array([row_scale_exponent(a) if a > 0 else 0 for a in amax.reshape(-1)], np.int64).reshape(amax.shape)
+    scale = np.ldexp(np.float32(1), e).astype(np.float32)
+    v = np.ldexp(x.astype(np.float64), -e[..., None])          # exact: a power-of-two rescale
+    return e4m3_encode(np.clip(v, -448.0, 448.0).astype(np.float32)), scale
 
 
 def dequantize_rows(codes, scales):

@@ -187,3 +187,17 @@ def test_paged_validation(lib):
                                                           br, tab, 4, one, None, None, 0, None)
     assert app(8, 100, one) == 2
     assert app(8, 64, None) == 1
+
+
+def test_fp8_validation(lib):
+    d = v3()
+    one = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+    # missing scales
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d), 1, one, one, one, None, one, one, 100, one, None, None,
+                                   one, 1 << 30, None) == 1
+    assert lib.mla_append_cache_fp8(ctypes.byref(d), 1, 1, None, None, None, one, one, None, one, one, None,
+                                    None, 0, None) == 1
+    # bad dims before anything else
+    bad = v3(d_r=3)
+    assert lib.mla_decode_attn_fp8(ctypes.byref(bad), 1, one, one, one, one, one, one, 100, one, None, None,
+                                   one, 1 << 30, None) == 2

@@ -1,0 +1,203 @@
+"""The 8-bit latent cache: rows stored as E4M3 codes with one power-of-two
+scale per row.  The append must produce the oracle's codes and scales bit for
+bit (where both sides see the same fp32 row values); the decode must match
+the oracle over the dequantised rows and, since code x scale is exact in bf16,
+give exactly the bits of the 16-bit decode over a bf16 cache holding the
+dequantised values."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from head_latent_attention_16_amd import _lib as L
+from head_latent_attention_16_amd import inputs as I
+
+from gpu_support import Uploaded, compare, dev, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+V3 = L.Dims.make(128, 512, 64, 128, 128, d_model=7168, d_q=1536, dtype="bf16")
+SCALE = O.scale_for(128, 64)
+
+
+def _quantized(w):
+    """Codes and scales of the workload's cache rows (the oracle's quantiser),
+    and the bf16 cache of the dequantised values (exact in bf16)."""
+    x = I.bf16_to_f32(w.cache)
+    codes, scales = O.quantize_rows(x)
+    vals = O.dequantize_rows(codes, scales).astype(np.float32)
+    bits = I.bf16_bits(vals)
+    assert np.array_equal(I.bf16_to_f32(bits), vals)
+    return codes, scales, bits
+
+
+def _decode_pair(u, codes, scales, bf16_cache, hint):
+    d, w = u.dims, u.w
+    q_lat = torch.empty(w.B, 128, 512, dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty(w.B, 128, 64, dtype=torch.bfloat16, device="cuda")
+    L.absorb_q(d, q_lat, q_pe, u.W["W_UK"], u.lens.clone(), q=u.q)
+    out = []
+    for which in ("fp8", "bf16"):
+        o_lat = torch.full((w.B, 128, 512), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((w.B, 128), float("nan"), dtype=torch.float32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if which == "fp8":
+            L.decode_attn_fp8(d, q_lat, q_pe, codes, scales, u.offsets, u.lens, o_lat, lse, total_rows_hint=hint,
+                              err_flag=err)
+        else:
+            L.decode_attn(d, q_lat, q_pe, bf16_cache, u.offsets, u.lens, o_lat, lse, total_rows_hint=hint,
+                          err_flag=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        out.append((o_lat, lse))
+    return out, host_f64(q_lat), host_f64(q_pe)
+
+
+def _check_oracle(w, codes_np, scales_np, o_lat, lse, ql, qp, b, heads, tag):
+    o = int(w.offsets[b])
+    rows = O.dequantize_rows(codes_np[o:o + int(w.lens[b])], scales_np[o:o + int(w.lens[b])])
+    ref, rl = O.latent_attention(ql[b][heads], qp[b][heads], rows[:, :512], rows[:, 512:], SCALE)
+    compare(host_f64(o_lat[b])[heads], ref, f"{tag} b={b} o_lat")
+    compare(host_f64(lse[b])[heads], rl, f"{tag} b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2,
+            norm_mean=1e-3)
+
+
+def test_fp8_append_codes_bit_exact():
+    """kv_raw rows appended at position 0 (the rotation is the identity), 300
+    sequences: codes and scales equal the oracle's bit for bit; then two more
+    rows per sequence at positions 1, 2: the rotated values within one E4M3
+    step of the oracle's rotation, the c^KV codes exact whenever the row's
+    largest magnitude lies in c^KV."""
+    B, D = 300, 576
+    rng = np.random.default_rng(80)
+    raw = I.bf16_bits((rng.standard_normal((B, 3, D)) * rng.uniform(0.01, 50, (B, 3, 1))).astype(np.float32))
+    raw[0, 0] = 0                                    # an all-zero row
+    caps = np.full(B, 4, np.int64)
+    offsets = np.arange(B + 1, dtype=np.int32) * 4
+    cache8 = torch.zeros(B * 4, D, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(B * 4, dtype=torch.float32, device="cuda")
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.append_cache_fp8(V3, cache8, scales, dev(offsets), lens, 1, kv_raw=dev(np.ascontiguousarray(raw[:, :1])),
+                       err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and lens.cpu().tolist() == [1] * B
+    got_c = cache8.cpu().numpy()[offsets[:-1]]
+    got_s = scales.cpu().numpy()[offsets[:-1]]
+    want_c, want_s = O.quantize_rows(I.bf16_to_f32(raw[:, 0]))
+    assert np.array_equal(got_c, want_c), int(np.sum(got_c != want_c))
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+    # positions 1 and 2
+    L.append_cache_fp8(V3, cache8, scales, dev(offsets), lens, 2, kv_raw=dev(np.ascontiguousarray(raw[:, 1:])),
+                       err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and lens.cpu().tolist() == [3] * B
+    c8, sc = cache8.cpu().numpy(), scales.cpu().numpy()
+    x = I.bf16_to_f32(raw[:, 1:]).astype(np.float64)                   # [B, 2, D]
+    x[..., 512:] = O.rope(x[..., 512:], np.array([1.0, 2.0])[None, :])
+    for i in range(2):
+        rows = offsets[:-1] + 1 + i
+        deq = O.dequantize_rows(c8[rows], sc[rows])
+        ref = x[:, i]
+        amax = np.max(np.abs(ref), axis=1, keepdims=True)
+        # within one E4M3 step of the reference (relative 2^-3 of the binade),
+        # or the subnormal step 2^-9 of a scale (at most amax / 224)
+        bound = np.maximum(np.abs(ref) * 2.0 ** -3, amax / 224 * 2.0 ** -9) * 1.001
+        assert np.all(np.abs(deq - ref) <= bound)
+        in_c = np.argmax(np.abs(ref), axis=1) < 512
+        want_c, _ = O.quantize_rows(ref.astype(np.float32))
+        assert np.array_equal(c8[rows][in_c, :512], want_c[in_c, :512])
+
+
+@pytest.mark.parametrize("lens", [[1, 31, 32, 33, 100, 1000, 4097], [5000]])
+def test_fp8_decode_small(lens):
+    rng = np.random.default_rng(len(lens))
+    w = I.attention_only("fp8", len(lens), np.asarray(lens, np.int32), rng, 0)
+    say(f"fp8 decode: lens={lens}")
+    u = Uploaded(w)
+    codes, scales, bf = _quantized(w)
+    pair, ql, qp = _decode_pair(u, dev(codes), dev(scales), dev(bf), w.total_rows)
+    (a, la), (b, lb) = pair
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    for s in range(w.B):
+        _check_oracle(w, codes, scales, a, la, ql, qp, s, list(range(128)), "fp8")
+
+
+def test_fp8_full_size_ragged():
+    """The ragged workload (B=64, 1.1M rows) quantised to 8 bits: identical
+    bits to the 16-bit decode over the rounded values, and the oracle over
+    the dequantised rows on every head of the shortest and longest sequence."""
+    w = I.make("ragged")
+    say(f"fp8 full size ragged: rows={w.total_rows}")
+    u = Uploaded(w)
+    codes, scales, bf = _quantized(w)
+    del u.cache
+    pair, ql, qp = _decode_pair(u, dev(codes), dev(scales), dev(bf), w.total_rows)
+    (a, la), (b, lb) = pair
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    for s in (int(np.argmin(w.lens)), int(np.argmax(w.lens))):
+        _check_oracle(w, codes, scales, a, la, ql, qp, s, list(range(128)), "fp8 ragged")
+
+
+def test_fp8_dominant_row_fallback():
+    """A row whose score jumps by ~2^200 flags its sequence; the recompute
+    reads the 8-bit rows too."""
+    w = I.attention_only("fp8", 2, np.array([700, 300], np.int32), np.random.default_rng(11), 0)
+    o0 = int(w.offsets[0])
+    kr = w.cache[o0 + 600, 512:].copy()
+    kr[0] = I.bf16_bits(np.array([2000.0], np.float32))[0]
+    w.cache[o0 + 600, 512:] = kr
+    u = Uploaded(w)
+    codes, scales, bf = _quantized(w)
+    rng = np.random.default_rng(12)
+    q_lat = dev(I.bf16_bits(rng.standard_normal((2, 128, 512)).astype(np.float32) * 0.02))
+    qp = np.zeros((2, 128, 64), np.float32)
+    qp[:, :, 0] = 1.0
+    q_pe = dev(I.bf16_bits(qp))
+    o_lat = torch.empty(2, 128, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(2, 128, dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.decode_attn_fp8(V3, q_lat, q_pe, dev(codes), dev(scales), u.offsets, u.lens, o_lat, lse,
+                      total_rows_hint=w.total_rows, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ql, qpe = host_f64(q_lat), host_f64(q_pe)
+    for b in range(2):
+        _check_oracle(w, codes, scales, o_lat, lse, ql, qpe, b, list(range(0, 128, 5)), "fp8 fallback")
+    row = O.dequantize_rows(codes[o0 + 600:o0 + 601], scales[o0 + 600:o0 + 601])[0, :512]
+    assert np.allclose(host_f64(o_lat[0]), row[None], atol=1e-5)
+
+
+def test_fp8_generic_tiny():
+    """Other dims (fp32 queries, n_h=4, d_c=32, d_R=8) through the generic
+    kernels: rows appended raw (rotated at 0..63) into an 8-bit cache, then
+    decoded; the oracle runs on the codes and scales the GPU wrote."""
+    w = I.tiny()
+    u = Uploaded(w)
+    d = u.dims
+    T, D = 64, 40
+    cache8 = torch.zeros(T, D, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(T, dtype=torch.float32, device="cuda")
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.append_cache_fp8(d, cache8, scales, u.offsets, lens, T, kv_raw=dev(w.kv_raw), err_flag=err)
+    q_lat = torch.empty(1, 4, 32, dtype=torch.float32, device="cuda")
+    q_pe = torch.empty(1, 4, 8, dtype=torch.float32, device="cuda")
+    L.absorb_q(d, q_lat, q_pe, u.W["W_UK"], torch.full((1,), T, dtype=torch.int32, device="cuda"), q=u.q)
+    o_lat = torch.empty(1, 4, 32, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, 4, dtype=torch.float32, device="cuda")
+    L.decode_attn_fp8(d, q_lat, q_pe, cache8, scales, u.offsets, lens, o_lat, lse, total_rows_hint=T, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and int(lens.item()) == T
+    rows = O.dequantize_rows(cache8.cpu().numpy(), scales.cpu().numpy())
+    ref_rows = w.kv_raw[0].astype(np.float64)
+    ref_rows[:, 32:] = O.rope(ref_rows[:, 32:], np.arange(T))
+    assert np.all(np.abs(rows - ref_rows) <= np.maximum(np.abs(ref_rows) * 2.0 ** -3,
+                                                         np.max(np.abs(ref_rows), 1, keepdims=True) / 224 * 2.0 ** -9) * 1.001)
+    ref, rl = O.latent_attention(host_f64(q_lat)[0], host_f64(q_pe)[0], rows[:, :32], rows[:, 32:],
+                                 O.scale_for(16, 8))
+    compare(host_f64(o_lat)[0], ref, "fp8 tiny o_lat", max_abs=1e-5, mean_abs=1e-6)
+    compare(host_f64(lse)[0], rl, "fp8 tiny lse", max_abs=1e-5, mean_abs=1e-6)

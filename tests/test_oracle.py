@@ -728,25 +728,30 @@ def test_quantize_rows_bounds_and_special_rows():
     codes, scales = O.quantize_rows(x)
     deq = O.dequantize_rows(codes, scales)
     amax = np.max(np.abs(x), axis=1)
-    # the row maximum maps to +-448 (code 0x7E / 0xFE), so it is kept to a float32 rounding
-    i = np.argmax(np.abs(x), axis=1)
-    assert np.all((codes[np.arange(50), i] & 0x7F) == 0x7E)
-    assert np.allclose(np.abs(deq[np.arange(50), i]), amax, rtol=2e-7)
-    # every element within half an E4M3 step (relative 2^-4 of its binade) plus
-    # the subnormal floor 2^-10 * scale
+    # the scale is the smallest power of two that brings amax within 448
+    e = np.log2(scales.astype(np.float64))
+    assert np.all(e == np.round(e))
+    assert np.all(amax <= 448 * scales) and np.all(amax > 224 * scales)
+    # every element within half an E4M3 step (relative 2^-4 of its binade),
+    # or half the subnormal step 2^-10 * scale
     err = np.abs(deq - x)
-    bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None] * 2.0 ** -10) * (1 + 1e-6)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None] * 2.0 ** -10) * (1 + 1e-12)
     assert np.all(err <= bound)
-    # an all-zero row: scale 1, zero codes; a constant row: every code -448,
-    # the value back to a float32 rounding of the scale
+    # the dequantised values are exactly representable in bf16
+    assert np.array_equal(I.bf16_to_f32(I.bf16_bits(deq.astype(np.float32))).astype(np.float64), deq)
+    # an all-zero row: scale 1, zero codes; a row of powers of two: exact
     c0, s0 = O.quantize_rows(np.zeros((1, 8), np.float32))
     assert s0[0] == 1.0 and not c0.any()
-    c1, s1 = O.quantize_rows(np.full((1, 8), -3.25, np.float32))
-    assert np.all(c1 == 0xFE)
-    assert np.allclose(O.dequantize_rows(c1, s1), -3.25, rtol=2e-7, atol=0)
+    p2 = np.array([[-3.25, 1.0, 0.5, 448.0 * 4, -2.0 ** -3]], np.float32)
+    c1, s1 = O.quantize_rows(p2)
+    assert s1[0] == 4.0 and np.array_equal(O.dequantize_rows(c1, s1), p2.astype(np.float64))
+    # the exponent rule at its boundaries: amax = 448 2^e -> e; just above -> e + 1
+    assert O.row_scale_exponent(448.0) == 0 and O.row_scale_exponent(448.0 * 2 ** -5) == -5
+    assert O.row_scale_exponent(np.nextafter(np.float32(448.0), np.float32(1e9))) == 1
+    assert O.row_scale_exponent(224.0) == -1 and O.row_scale_exponent(225.0) == 0
     # a planted mistake: rounding toward zero instead of to nearest breaks the
     # half-step bound
-    v = np.clip(x * (np.float32(448) / amax.astype(np.float32))[:, None], -448, 448)
+    v = x / scales[:, None]
     mags = np.array([O.e4m3_value(c) for c in range(0x7F)])
     toward0 = np.sign(v) * mags[np.searchsorted(mags, np.abs(v), side="right") - 1]
     bad = np.abs(toward0 * scales[:, None] - x)
