@@ -73,6 +73,7 @@ __all__ = [
     "absorb_query",
     "latent_attention",
     "latent_attention_causal",
+    "prefill_explicit",
     "append_rows",
     "rms_norm",
     "query_path",
@@ -223,6 +224,43 @@ def latent_attention_causal(q_lat, q_pe, c, k_rot, scale):
     s = np.where((row <= tok)[:, None, :], s, -np.inf)                # causal mask
     p, lse = softmax_two_pass(s)
     return p @ c, lse
+
+
+# ---------------------------------------------------------------------------
+# The un-absorbed ("naive") branch for many new tokens.  [MLA-struct], section
+# "结合 DeepSeek 推理代码看 MLA", the `naive` branch: the full keys and values
+# are recovered from the latent (k^C = W^UK c, v = W^UV c), the key gets the
+# shared RoPE key concatenated, scores are [q^C; q^R] . [k^C; k^R], and the
+# output is the weighted sum of the explicit values; worked example step 4:
+# the scores are causally masked.  Reading: the n_q new tokens are the last n_q
+# of the T cached rows (appended first, as in the absorbed branch), token i
+# sits at row T - n_q + i and sees rows 0 .. T - n_q + i; q^R is rotated at
+# the token's position.
+# ---------------------------------------------------------------------------
+def prefill_explicit(q_C, q_R, c, k_rot, W_UK, W_UV, scale, base=10000.0):
+    """o [n_q, n_h, d_v] and lse [n_q, n_h] of n_q new tokens of one sequence.
+
+    q_C [n_q, n_h, d_h], q_R [n_q, n_h, d_R] (not rotated), c [T, d_c],
+    k_rot [T, d_R] (rotated, as cached), W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c].
+    """
+    q_C = np.asarray(q_C, np.float64)
+    q_R = np.asarray(q_R, np.float64)
+    c = np.asarray(c, np.float64)
+    k_rot = np.asarray(k_rot, np.float64)
+    n_q, n_h = q_C.shape[0], q_C.shape[1]
+    T = c.shape[0]
+    pos = T - n_q + np.arange(n_q)                                   # token positions = rows
+    q_R_rot = rope(q_R, pos[:, None], base)                          # [n_q, n_h, d_R]
+    o = np.empty((n_q, n_h, np.asarray(W_UV).shape[1]))
+    lse = np.empty((n_q, n_h))
+    visible = np.arange(T)[None, :] <= pos[:, None]                 # causal mask [n_q, T]
+    for h in range(n_h):
+        keys, values = explicit_kv(c, k_rot, np.asarray(W_UK[h], np.float64), np.asarray(W_UV[h], np.float64))
+        q = np.concatenate([q_C[:, h], q_R_rot[:, h]], axis=1)       # [n_q, d_h + d_R]
+        s = np.where(visible, (q @ keys.T) * scale, -np.inf)
+        p, lse[:, h] = softmax_two_pass(s)
+        o[:, h] = p @ values
+    return o, lse
 
 
 # ---------------------------------------------------------------------------

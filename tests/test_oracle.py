@@ -756,3 +756,50 @@ def test_quantize_rows_bounds_and_special_rows():
     toward0 = np.sign(v) * mags[np.searchsorted(mags, np.abs(v), side="right") - 1]
     bad = np.abs(toward0 * scales[:, None] - x)
     assert np.any(bad > bound)
+
+
+# ---------------------------------------------------------------------------
+# The un-absorbed branch for many new tokens (prefill).
+# ---------------------------------------------------------------------------
+def _prefill_case(rng, T, n_q, n_h=3, d_c=12, d_r=6, d_h=5, d_v=7):
+    return (rng.standard_normal((n_q, n_h, d_h)), rng.standard_normal((n_q, n_h, d_r)),
+            rng.standard_normal((T, d_c)), rng.standard_normal((T, d_r)),
+            rng.standard_normal((n_h, d_h, d_c)) / math.sqrt(d_c), rng.standard_normal((n_h, d_v, d_c)) / math.sqrt(d_c),
+            1.0 / math.sqrt(d_h + d_r))
+
+
+def test_prefill_token_equals_decode_over_prefix():
+    # token i is a single-query explicit decode over rows 0 .. T - n_q + i at
+    # its own position; an off-by-one mask is a different result
+    rng = np.random.default_rng(40)
+    for T, n_q in ((1, 1), (9, 9), (20, 6)):
+        qc, qr, c, kr, Wk, Wv, sc = _prefill_case(rng, T, n_q)
+        o, lse = O.prefill_explicit(qc, qr, c, kr, Wk, Wv, sc)
+        for i in range(n_q):
+            n = T - n_q + i + 1
+            oi, _, li = O.decode_explicit(qc[i], qr[i], n - 1, c[:n], kr[:n], Wk, Wv, sc)
+            assert rel_err(o[i], oi) < RTOL and rel_err(lse[i], li) < RTOL
+        if n_q > 1 and T > n_q:
+            n = T - n_q + 1
+            wrong, _, _ = O.decode_explicit(qc[1], qr[1], n, c[:n], kr[:n], Wk, Wv, sc)
+            assert rel_err(o[1], wrong) > 1e-3
+
+
+def test_prefill_matches_torch_causal_sdpa_and_absorbed_route():
+    rng = np.random.default_rng(41)
+    T, n_q = 30, 30
+    qc, qr, c, kr, Wk, Wv, sc = _prefill_case(rng, T, n_q)
+    o, lse = O.prefill_explicit(qc, qr, c, kr, Wk, Wv, sc)
+    # torch's attention with is_causal over explicit K, V (a fresh prompt: n_q = T)
+    qrot = O.rope(qr, np.arange(T)[:, None])
+    q = torch.from_numpy(np.concatenate([qc, qrot], 2)).transpose(0, 1).contiguous()          # [n_h, T, D]
+    K = torch.from_numpy(np.concatenate([np.einsum("tc,hkc->htk", c, Wk),
+                                         np.broadcast_to(kr, (3, T, kr.shape[1]))], 2)).contiguous()
+    V = torch.from_numpy(np.einsum("tc,hvc->htv", c, Wv)).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, is_causal=True, scale=sc)
+    assert rel_err(o, ref.transpose(0, 1).numpy()) < 1e-12
+    # the absorbed route: latent causal attention, then W_UV per head
+    q_lat = np.einsum("thk,hkc->thc", qc, Wk)
+    z, lse2 = O.latent_attention_causal(q_lat, qrot, c, kr, sc)
+    assert rel_err(np.einsum("hvc,thc->thv", Wv, z), o) < 1e-12
+    assert rel_err(lse2, lse) < 1e-12
