@@ -34,7 +34,7 @@ EXPORTS = ("mla_absorb_q", "mla_absorb_q_workspace", "mla_append_cache",
            "mla_project_out", "mla_project_out_workspace", "mla_cache_row_bytes",
            "mla_status_string", "mla_abi_version", "mla_decode_attn_noalloc",
            "mla_decode_attn_paged", "mla_append_cache_paged", "mla_append_cache_fp8",
-           "mla_decode_attn_fp8")
+           "mla_decode_attn_fp8", "mla_prefill_attn", "mla_prefill_attn_workspace")
 
 
 class MLAError(RuntimeError):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
                                    i32),
         "mla_append_cache_fp8": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_fp8": ([D, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
+        "mla_prefill_attn": ([D, i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "mla_prefill_attn_workspace": ([D, i32, i32, i64], sz),
         "mla_decode_attn_causal": ([D, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp], i32),
         "mla_decode_attn_causal_workspace": ([D, i32, i32, i64], sz),
         "mla_project_out": ([D, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -360,6 +362,35 @@ def decode_attn_fp8(dims: Dims, q_lat, q_pe, cache8, scales, offsets, lens, o_la
                                _ptr(offsets), _ptr(lens), hint, _ptr(o_lat), _ptr(lse), _ptr(err_flag), w, wn,
                                _stream(stream))
     _check("mla_decode_attn_fp8", st)
+
+
+def prefill_attn_workspace(dims: Dims, B: int, n_q: int, cache_rows: int) -> int:
+    return int(lib().mla_prefill_attn_workspace(ctypes.byref(dims), B, n_q, int(cache_rows)))
+
+
+def prefill_attn(dims: Dims, q, cache, offsets, lens, W_UK, W_UV, o, lse=None, err_flag=None, ws=None,
+                 stream=None):
+    """Un-absorbed causal attention of the last n_q cached tokens of each
+    sequence; q [B, n_q, n_h, d_h + d_r] (q^R not rotated), o [B, n_q, n_h, d_v]."""
+    L = lib()
+    B, n_q = q.shape[0], q.shape[1]
+    dt = dims.torch_dtype
+    _dev(q, cache, offsets, lens, W_UK, W_UV, o, lse, err_flag)
+    _need(q, B * n_q * dims.n_h * (dims.d_h + dims.d_r), dt, "q")
+    _need(offsets, B + 1, torch.int32, "offsets")
+    _need(lens, B, torch.int32, "lens")
+    _need(W_UK, dims.n_h * dims.d_h * dims.d_c, dt, "W_UK")
+    _need(W_UV, dims.n_h * dims.d_v * dims.d_c, dt, "W_UV")
+    _need(o, B * n_q * dims.n_h * dims.d_v, torch.float32, "o")
+    _need(lse, B * n_q * dims.n_h, torch.float32, "lse")
+    if cache.dtype != dt:
+        raise ValueError("cache dtype")
+    rows = cache.numel() // (dims.d_c + dims.d_r)
+    ws = _workspace(prefill_attn_workspace(dims, B, n_q, rows), ws, cache.device)
+    w, wn = _ws_args(ws)
+    st = L.mla_prefill_attn(ctypes.byref(dims), B, n_q, _ptr(q), _ptr(cache), rows, _ptr(offsets), _ptr(lens),
+                            _ptr(W_UK), _ptr(W_UV), _ptr(o), _ptr(lse), _ptr(err_flag), w, wn, _stream(stream))
+    _check("mla_prefill_attn", st)
 
 
 def project_out(dims: Dims, o_lat, W_UV, o=None, u=None, W_O=None, ws=None, stream=None):

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "generic.hip", "decode_v3.hip", "proj_v3.hip", "gemm_v3.hip"]
+SOURCES = ["api.cpp", "generic.hip", "decode_v3.hip", "proj_v3.hip", "gemm_v3.hip", "prefill.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 COMMON = [

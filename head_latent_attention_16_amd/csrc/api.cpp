@@ -557,6 +557,32 @@ mla_status_t mla_append_cache_fp8(const mla_dims_t* dims, int32_t B, int32_t n_n
                        contiguous_map(offsets), lens, err_flag, ws, ws_bytes, stream);
 }
 
+size_t mla_prefill_attn_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q, int64_t cache_rows) {
+  Shape s;
+  if (check_dims(dims, &s) != MLA_OK || !prefill_v3_supported(s) || B < 0 || B > 65535 || n_q < 1 ||
+      cache_rows < 1)
+    return 0;
+  return prefill_v3_workspace(B, n_q, cache_rows);
+}
+
+mla_status_t mla_prefill_attn(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q, const void* cache,
+                              int64_t cache_rows, const int32_t* offsets, const int32_t* lens, const void* W_UK,
+                              const void* W_UV, float* o, float* lse, int32_t* err_flag, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Shape s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (!prefill_v3_supported(s)) return MLA_ERR_SHAPE;
+  if (B < 0 || B > 65535 || n_q < 1 || cache_rows < 1 || cache_rows > INT32_MAX) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !cache || !offsets || !lens || !W_UK || !W_UV || !o) return MLA_ERR_NULL;
+  if (!ws || ws_bytes < prefill_v3_workspace(B, n_q, cache_rows)) return MLA_ERR_WORKSPACE;
+  DeviceInfo info;
+  if ((st = device_ready(&info)) != MLA_OK) return st;
+  return launched(launch_prefill_v3(s, B, n_q, q, cache, cache_rows, offsets, lens, W_UK, W_UV, o, lse, err_flag,
+                                    ws, (hipStream_t)stream));
+}
+
 size_t mla_project_out_workspace(const mla_dims_t* dims, int32_t B, int32_t with_u) {
   Shape s;
   if (check_dims(dims, &s) != MLA_OK || B < 0) return 0;

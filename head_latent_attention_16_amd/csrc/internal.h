@@ -106,6 +106,14 @@ hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32
 hipError_t launch_uv_v3(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
                         hipStream_t st);
 
+// Un-absorbed prefill at V3 dims (bf16): q [B, n_q, n_h, d_h + d_r] un-rotated,
+// cache rows [rows, d_c + d_r]; o [B, n_q, n_h, d_v] fp32, lse [B, n_q, n_h].
+bool prefill_v3_supported(const Shape& s);
+size_t prefill_v3_workspace(int B, int n_q, int64_t rows);
+hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, const void* cache, int64_t rows,
+                             const int32_t* offsets, const int32_t* lens, const void* W_UK, const void* W_UV,
+                             float* o, float* lse, int32_t* err_flag, void* ws, hipStream_t st);
+
 // Device properties of the current device (cached per device, thread-safe).
 struct DeviceInfo {
   int device;

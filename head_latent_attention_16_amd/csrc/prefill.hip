@@ -1,0 +1,488 @@
+// The un-absorbed ("naive") branch of MLA for many new tokens (prefill).
+//
+// What is computed ("MLA模型结构详解：从公式到推理代码", section "结合 DeepSeek 推理代码看
+// MLA", the naive branch; worked example step 4 for the causal mask): the full
+// per-head keys and values are recovered from the latent cache,
+//   k_j = [W^UK[h] c_j | kR_j],   v_j = W^UV[h] c_j,
+// and each new token i (at row p_i = lens[b] - n_q + i of its sequence)
+// attends causally to rows 0 .. p_i:
+//   o[b,i,h] = sum_{j <= p_i} softmax_j(scale [q^C; RoPE(q^R, p_i)] . k_j) v_j.
+// Per (query, key) pair this costs 2 n_h (d_h + d_R + d_v) flops instead of
+// the absorbed route's 2 n_h (2 d_c + d_R): the up-projection is paid once
+// per key row and amortised over the new tokens.
+//
+// The explicit keys and values live in an fp16 workspace (11 significant
+// bits: rounding them to bf16 would add an error comparable to the whole
+// tolerance when a token sees few keys), so the attention runs on fp16 MFMA;
+// the explicit keys, values and queries must lie within the fp16 range.
+//
+// Kernels (gfx950, wave64, MFMA with fp32 accumulation):
+// * k_q_rope: q^R rotated at each token's position (fp64 angle), q -> fp16.
+// * k_upproj: KV[r, h] = [W^UK[h] c_r | W^UV[h] c_r] (fp16) for every cache
+//   row r, a bf16 [rows x 512] . [512 x n_h 256] GEMM; a workgroup owns one head's 256
+//   output columns for 128 rows, the 512-deep reduction in 64-wide chunks
+//   double-buffered in LDS through direct global -> LDS loads.
+// * k_prefill: flash attention per (sequence, head, 128 new tokens): four
+//   waves of 32 tokens; 64-key blocks of [K^C | k^R] (384 B per row) and V
+//   (256 B per row) are DMA'd into LDS one block ahead; S^T = K Q^T and
+//   O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T fragments by transpose
+//   reads), an online softmax in base 2 with the running max, the causal mask
+//   on the diagonal blocks.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int PN_H = 128, PD_C = 512, PD_R = 64, PD_H = 128, PD_V = 128;
+constexpr int PQK = PD_H + PD_R;          // 192 query/key width
+constexpr int KVW = PD_H + PD_V;          // 256 up-projected columns per head
+constexpr int CROWB = (PD_C + PD_R) * 2;  // 1152 cache row bytes
+
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx4v __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ const char* uni_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global -> LDS, 16 bytes per lane (lane i's bytes land at M0 + 16 i);
+// completion is counted by hand (s_waitcnt vmcnt) before the barrier that
+// publishes the stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// q^R rotation: q_rot[t, h] = [q^C | RoPE(q^R, pos_t)] in fp16, pos_t the
+// token's row.  One thread per (token, head, rotation pair); the content part
+// is copied by the same threads.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_q_rope(int B, int n_q, double base, const __bf16* __restrict__ q,
+                                                const int32_t* __restrict__ lens, _Float16* __restrict__ q_rot) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_tok = (int64_t)PN_H * (PQK / 2);
+  if (idx >= (int64_t)B * n_q * per_tok) return;
+  const int64_t t = idx / per_tok;
+  const int rem = (int)(idx - t * per_tok);
+  const int h = rem / (PQK / 2), k = rem - h * (PQK / 2);   // k < 96
+  const int b = (int)(t / n_q), i = (int)(t - (int64_t)b * n_q);
+  const __bf16* src = q + (t * PN_H + h) * PQK;
+  _Float16* dst = q_rot + (t * PN_H + h) * PQK;
+  if (k < PD_H / 2) {   // content: two values per thread
+    dst[2 * k] = (_Float16)(float)src[2 * k];
+    dst[2 * k + 1] = (_Float16)(float)src[2 * k + 1];
+  } else {              // rope pair j = k - 64 of 32
+    const int j = k - PD_H / 2;
+    const int64_t pos = (int64_t)lens[b] - n_q + i;
+    float cs, sn;
+    rope_cos_sin(pos < 0 ? 0 : pos, j, PD_R, base, &cs, &sn);
+    const float lo = (float)src[PD_H + j], hi = (float)src[PD_H + PD_R / 2 + j];
+    dst[PD_H + j] = (_Float16)(lo * cs - hi * sn);
+    dst[PD_H + PD_R / 2 + j] = (_Float16)(hi * cs + lo * sn);
+  }
+}
+
+// k^R in fp16: kr[r] = cache[r, d_c ..] (one thread per value).
+__global__ void __launch_bounds__(256) k_kr_f16(int64_t rows, const __bf16* __restrict__ cache,
+                                                _Float16* __restrict__ kr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * PD_R) return;
+  const int64_t r = i / PD_R;
+  const int c = (int)(i - r * PD_R);
+  kr[i] = (_Float16)(float)cache[r * (PD_C + PD_R) + PD_C + c];
+}
+
+// ---------------------------------------------------------------------------
+// Up-projection GEMM.  KV^T tile of one head: rows of the output are the 256
+// weight rows (W^UK[h] then W^UV[h]), columns 128 cache rows.  Wave w:
+// weight rows 64 w .. +64 (two 32-row blocks) for all 128 cache rows (four
+// blocks): 8 accumulators.  Per 64-wide k chunk the
+// stage holds W [256 x 64] (32 KiB) and X [128 x 64] (16 KiB), rows of 128 B
+// with the 16-byte chunk c of row r at c ^ ((r >> 1) & 7).
+// ---------------------------------------------------------------------------
+constexpr int U_ROWS = 128;                      // cache rows per workgroup
+constexpr int U_KC = 64;                         // k per chunk
+constexpr int U_WB = KVW * U_KC * 2;             // 32768
+constexpr int U_XB = U_ROWS * U_KC * 2;          // 16384
+constexpr int U_STAGE = U_WB + U_XB;             // 49152
+constexpr int U_DPW = U_STAGE / 1024 / 4;        // 12 DMAs per wave per chunk
+static_assert(U_DPW * 4 * 1024 == U_STAGE, "whole DMA instructions per wave");
+
+__device__ __forceinline__ int usw(int r) { return (r >> 1) & 7; }
+
+__global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __restrict__ cache,
+                                                   const __bf16* __restrict__ W_UK,
+                                                   const __bf16* __restrict__ W_UV, _Float16* __restrict__ kv) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * U_STAGE];
+  const int h = blockIdx.x;
+  const int r0 = blockIdx.y * U_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
+  const char* wuk = (const char*)(W_UK + (size_t)h * PD_H * PD_C);
+  const char* wuv = (const char*)(W_UV + (size_t)h * PD_V * PD_C);
+  const char* crow = (const char*)cache;
+
+  // DMA k of this wave for chunk kc: LDS chunk p = 64 (12 wave + k) + lane of
+  // the stage; p < 2048: W row p / 8, else X row (p - 2048) / 8; physical
+  // 16-byte position p % 8 holds logical chunk (p % 8) ^ usw(row).
+  auto dma_chunk = [&](int kc, int stage) {
+#pragma unroll
+    for (int k = 0; k < U_DPW; ++k) {
+      const int p = 64 * (U_DPW * wave + k) + lane;
+      const char* src;
+      if (p < U_WB / 16) {
+        const int wr = p >> 3, c = (p & 7) ^ usw(wr);
+        src = (wr < PD_H ? wuk + (size_t)wr * PD_C * 2 : wuv + (size_t)(wr - PD_H) * PD_C * 2) + kc * U_KC * 2 + c * 16;
+      } else {
+        const int xr = (p - U_WB / 16) >> 3, c = (p & 7) ^ usw(xr);
+        const int r = min(r0 + xr, rows - 1);   // rows past the end repeat the last one
+        src = crow + (size_t)r * CROWB + kc * U_KC * 2 + c * 16;
+      }
+      dma16(lds0 + (uint32_t)(stage * U_STAGE + (U_DPW * wave + k) * 1024), src);
+    }
+  };
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  constexpr int NCH = PD_C / U_KC;   // 8 chunks
+  dma_chunk(0, 0);
+  const int n32 = lane & 31, g = lane >> 5;
+  for (int kc = 0; kc < NCH; ++kc) {
+    if (kc + 1 < NCH) {
+      dma_chunk(kc + 1, (kc + 1) & 1);
+      vm_wait_barrier<U_DPW>();   // chunk kc landed (only kc + 1 is in flight)
+    } else {
+      vm_wait_barrier<0>();
+    }
+    const MLA_LDS char* Ws = (const MLA_LDS char*)lds + (kc & 1) * U_STAGE;
+    const MLA_LDS char* Xs = Ws + U_WB;
+#pragma unroll
+    for (int ks = 0; ks < U_KC / 16; ++ks) {
+      const int c = 2 * ks + g;   // logical 16-byte chunk of this lane's 8 k values
+      bf16x8 A[2], Bx[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int wr = 64 * wave + 32 * i + n32;
+        A[i] = *(const MLA_LDS bf16x8*)(Ws + wr * 128 + ((c ^ usw(wr)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int xr = 32 * j + n32;
+        Bx[j] = *(const MLA_LDS bf16x8*)(Xs + xr * 128 + ((c ^ usw(xr)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], Bx[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_barrier" ::: "memory");   // the stage is refilled next
+  }
+  // acc[i][j]: weight rows 64 wave + 32 i + {8 (e / 4) + 4 g + e % 4}, cache
+  // row 32 j + n32; four consecutive weight rows -> 8 contiguous bytes.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = r0 + 32 * j + n32;
+    if (r >= rows) continue;
+    _Float16* out = kv + ((size_t)r * PN_H + h) * KVW;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        halfx4v v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (_Float16)acc[i][j][4 * q4 + e];
+        *(halfx4v*)(out + 64 * wave + 32 * i + 8 * q4 + 4 * g) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Causal flash attention over the explicit keys and values.
+// Key block stage: K [64 x 192] (rows of 384 B, 24 chunks; chunk c of row r at
+// c ^ ((r >> 1) & 7)) then V [64 x 128] (rows of 256 B, 16 chunks; chunk c of
+// row r at c ^ (4 (r & 3))).  40 KiB = 10 DMAs per wave; two stages.
+// ---------------------------------------------------------------------------
+constexpr int F_TQ = 128;                 // new tokens per workgroup
+constexpr int F_KB = 64;                  // keys per block
+constexpr int F_KROWB = PQK * 2;          // 384
+constexpr int F_VROWB = PD_V * 2;         // 256
+constexpr int F_KB_BYTES = F_KB * F_KROWB;   // 24576
+constexpr int F_STAGE = F_KB_BYTES + F_KB * F_VROWB;   // 40960
+constexpr int F_DPW = F_STAGE / 1024 / 4;    // 10
+static_assert(F_DPW * 4 * 1024 == F_STAGE, "whole DMA instructions per wave");
+
+__device__ __forceinline__ int ksw(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int vsw(int r) { return 4 * (r & 3); }
+
+struct PrefillArgs {
+  const _Float16* q_rot;   // [B, n_q, n_h, 192]
+  const _Float16* kr;      // [rows, 64]
+  const _Float16* kv;      // [rows, n_h, 256]
+  const int32_t* offsets;
+  const int32_t* lens;
+  float* o;                // [B, n_q, n_h, 128]
+  float* lse;              // [B, n_q, n_h] or NULL
+  int32_t* err_flag;
+  int B, n_q, rows;
+  float scale_log2;
+};
+
+__global__ void __launch_bounds__(256, 1) k_prefill(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * F_STAGE];
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31, g = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
+
+  const int len = a.lens[b];
+  const int off = a.offsets[b];
+  const int cap = a.offsets[b + 1] - off;
+  const int i0 = qb * F_TQ;                       // first token of the workgroup
+  const int nq_wg = min(F_TQ, a.n_q - i0);        // tokens of the workgroup
+  const bool valid = len >= a.n_q && len <= cap && (int64_t)off + len <= a.rows && off >= 0;
+  const int tok = i0 + 32 * wave + n32;           // this lane's token (column of S^T)
+  const bool tok_ok = 32 * wave + n32 < nq_wg;
+  float* orow = a.o + (((size_t)b * a.n_q + min(tok, a.n_q - 1)) * PN_H + h) * PD_V;
+  if (!valid) {
+    if (tok_ok) {
+      for (int c = g; c < PD_V; c += 2) orow[c] = __builtin_nanf("");
+      if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok) * PN_H + h] = __builtin_nanf("");
+    }
+    if (tid == 0 && qb == 0 && h == 0 && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_LENS);
+    return;
+  }
+  const int p_first = len - a.n_q + i0;           // position of the workgroup's first token
+  const int p_last = p_first + nq_wg - 1;
+  const int pos = len - a.n_q + min(tok, a.n_q - 1);   // this lane's token position
+  const int nblk = (p_last + 1 + F_KB - 1) / F_KB;     // key blocks any token sees
+
+  // Q^T fragments (B operand): token n32 of this wave, features 16 kk + 8 g.
+  halfx8 q[PQK / 16];
+  {
+    const _Float16* qr = a.q_rot + (((size_t)b * a.n_q + min(tok, a.n_q - 1)) * PN_H + h) * PQK;
+#pragma unroll
+    for (int kk = 0; kk < PQK / 16; ++kk) q[kk] = *(const halfx8*)(qr + 16 * kk + 8 * g);
+  }
+
+  const char* kvb = (const char*)(a.kv + (size_t)h * KVW);     // row r at kvb + r * n_h * 512
+  const size_t kv_row = (size_t)PN_H * KVW * 2;
+  // DMA k of this wave for key block kb: stage chunk p = 64 (10 wave + k) + lane;
+  // p < 1536: K row p / 24, physical chunk p % 24 holding logical chunk
+  // (p % 24) ^ ksw(row) (logical < 16: K^C from kv, else k^R);
+  // else V row (p - 1536) / 16, logical chunk ((p - 1536) % 16) ^ vsw(row).
+  auto dma_block = [&](int kb, int stage) {
+#pragma unroll
+    for (int k = 0; k < F_DPW; ++k) {
+      const int p = 64 * (F_DPW * wave + k) + lane;
+      const char* src;
+      if (p < F_KB_BYTES / 16) {
+        const int kr = p / 24, pc = p - kr * 24, c = pc ^ ksw(kr);
+        const int j = min(kb * F_KB + kr, len - 1);
+        const size_t row = (size_t)off + j;
+        src = c < 16 ? kvb + row * kv_row + c * 16 : (const char*)(a.kr + row * PD_R) + (c - 16) * 16;
+      } else {
+        const int pv = p - F_KB_BYTES / 16;
+        const int vr = pv >> 4, c = (pv & 15) ^ vsw(vr);
+        const int j = min(kb * F_KB + vr, len - 1);
+        src = kvb + ((size_t)off + j) * kv_row + PD_H * 2 + c * 16;
+      }
+      dma16(lds0 + (uint32_t)(stage * F_STAGE + (F_DPW * wave + k) * 1024), src);
+    }
+  };
+
+  floatx16 O[PD_V / 32];
+#pragma unroll
+  for (int cb = 0; cb < PD_V / 32; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O[cb][e] = 0.f;
+  float m_run = -INFINITY;   // running max of this lane's token (log2 units)
+  float l_run = 0.f;         // this lane's share of the weight sum
+
+  // transpose-read bases for V^T fragments: group G = lane / 16, i = lane % 16
+  // reads 8 bytes of key row 16 kk2 + 8 rd + rr (rr = 4 g + i / 4) at value
+  // columns 32 cb + 16 (G & 1) + 4 (i & 3).
+  const int Gq = lane >> 4, i16 = lane & 15;
+  const int rr = 4 * g + (i16 >> 2);
+
+  dma_block(0, 0);
+  for (int kb = 0; kb < nblk; ++kb) {
+    if (kb + 1 < nblk) {
+      dma_block(kb + 1, (kb + 1) & 1);
+      vm_wait_barrier<F_DPW>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    const MLA_LDS char* Ks = (const MLA_LDS char*)lds + (kb & 1) * F_STAGE;
+    const MLA_LDS char* Vs = Ks + F_KB_BYTES;
+    // S^T[keys x tokens] for the two 32-key halves
+    floatx16 S[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < PQK / 16; ++kk) {
+        const int kr = 32 * t + n32, c = 2 * kk + g;
+        const halfx8 kf = *(const MLA_LDS halfx8*)(Ks + kr * F_KROWB + ((c ^ ksw(kr)) << 4));
+        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[kk], S[t], 0, 0, 0);
+      }
+    }
+    // scores -> log2 units with the causal mask; key of S[t][e] is
+    // 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4
+    float x[2][16];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb * F_KB + 32 * t + 8 * (e >> 2) + 4 * g + (e & 3);
+        const bool ok = key <= pos && key < len;
+        x[t][e] = ok ? S[t][e] * a.scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, x[t][e]);
+      }
+    // the token's max over both lane halves
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
+    }
+    const float m_new = fmaxf(m_run, bmax);
+    // rescale what was accumulated when the max moved (no lane's token can
+    // have m_new = -inf here: every token sees key 0 in block 0)
+    if (__any(m_new > m_run)) {
+      const float al = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      l_run *= al;
+#pragma unroll
+      for (int cb = 0; cb < PD_V / 32; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[cb][e] *= al;
+    }
+    m_run = m_new;
+    // weights as the PV operand: P[t][kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3}
+    halfx8 P[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(x[t][e] - m_new);
+        const _Float16 ph = (_Float16)p;
+        P[t][e >> 3][e & 7] = ph;
+        l_run += (float)ph;
+      }
+    // O^T[value cols x tokens] += V^T . P^T, four 32-column blocks
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+        for (int cb = 0; cb < PD_V / 32; ++cb) {
+          halfx4v part[2];
+#pragma unroll
+          for (int rd = 0; rd < 2; ++rd) {
+            const int vr = 32 * t + 16 * kk2 + 8 * rd + rr;
+            const int c = 2 * (2 * cb + (Gq & 1)) + ((i16 & 3) >> 1);     // logical 16-byte chunk
+            const MLA_LDS char* pa = Vs + vr * F_VROWB + ((c ^ vsw(vr)) << 4) + 8 * (i16 & 1);
+            part[rd] = __builtin_bit_cast(halfx4v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)pa));
+          }
+          const halfx8 vf = {part[0][0], part[0][1], part[0][2], part[0][3],
+                             part[1][0], part[1][1], part[1][2], part[1][3]};
+          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[t][kk2], O[cb], 0, 0, 0);
+        }
+    asm volatile("s_barrier" ::: "memory");   // every wave is done with this stage
+  }
+  // normalise and store: O[cb][e] is value column 32 cb + 8 (e / 4) + 4 g + e % 4
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    l_run += __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(l_run)));
+  }
+  if (!tok_ok) return;
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int cb = 0; cb < PD_V / 32; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const floatx4 v = {O[cb][4 * q4] * inv, O[cb][4 * q4 + 1] * inv, O[cb][4 * q4 + 2] * inv,
+                         O[cb][4 * q4 + 3] * inv};
+      *(floatx4*)(orow + 32 * cb + 8 * q4 + 4 * g) = v;
+    }
+  if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok) * PN_H + h] = (m_run + log2f(l_run)) * kLn2;
+}
+
+}  // namespace
+
+bool prefill_v3_supported(const Shape& s) {
+  return s.bf16 && s.n_h == PN_H && s.d_c == PD_C && s.d_r == PD_R && s.d_h == PD_H && s.d_v == PD_V;
+}
+
+// workspace: explicit keys and values [rows, n_h, 256] fp16, k^R [rows, 64]
+// fp16, rotated queries [B, n_q, n_h, 192] fp16 (each 256-byte aligned)
+size_t prefill_v3_workspace(int B, int n_q, int64_t rows) {
+  const size_t kv = (size_t)rows * PN_H * KVW * 2;
+  const size_t kr = (size_t)rows * PD_R * 2;
+  const size_t qr = (size_t)B * n_q * PN_H * PQK * 2;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(kv) + al(kr) + al(qr);
+}
+
+hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, const void* cache, int64_t rows,
+                             const int32_t* offsets, const int32_t* lens, const void* W_UK, const void* W_UV,
+                             float* o, float* lse, int32_t* err_flag, void* ws, hipStream_t st) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  _Float16* kv = (_Float16*)ws;
+  _Float16* kr = (_Float16*)((char*)ws + al((size_t)rows * PN_H * KVW * 2));
+  _Float16* q_rot = (_Float16*)((char*)kr + al((size_t)rows * PD_R * 2));
+  const int64_t nth = (int64_t)B * n_q * PN_H * (PQK / 2);
+  k_q_rope<<<(unsigned)((nth + 255) / 256), 256, 0, st>>>(B, n_q, s.rope_base, (const __bf16*)q, lens, q_rot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_kr_f16<<<(unsigned)((rows * PD_R + 255) / 256), 256, 0, st>>>(rows, (const __bf16*)cache, kr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_upproj<<<dim3(PN_H, (unsigned)((rows + U_ROWS - 1) / U_ROWS)), 256, 0, st>>>(
+      (int)rows, (const __bf16*)cache, (const __bf16*)W_UK, (const __bf16*)W_UV, kv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PrefillArgs a;
+  a.q_rot = q_rot;
+  a.kr = kr;
+  a.kv = kv;
+  a.offsets = offsets;
+  a.lens = lens;
+  a.o = o;
+  a.lse = lse;
+  a.err_flag = err_flag;
+  a.B = B;
+  a.n_q = n_q;
+  a.rows = (int)rows;
+  a.scale_log2 = s.scale * kLog2e;
+  k_prefill<<<dim3((n_q + F_TQ - 1) / F_TQ, PN_H, B), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -60,7 +60,8 @@ extern "C" {
  * the decode entry points reject more than 65535 query tokens up front.
  * 3: adds mla_decode_attn_noalloc, the paged pool (mla_decode_attn_paged,
  * mla_append_cache_paged), MLA_DEVERR_TABLE and the 8-bit cache
- * (mla_append_cache_fp8, mla_decode_attn_fp8). */
+ * (mla_append_cache_fp8, mla_decode_attn_fp8) and the un-absorbed prefill
+ * (mla_prefill_attn). */
 #define MLA_ABI_VERSION 3
 
 typedef enum {
@@ -234,6 +235,38 @@ mla_status_t mla_decode_attn_causal(const mla_dims_t* dims, int32_t B, int32_t n
                                     int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
 size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q,
                                         int64_t total_rows_hint);
+
+/* Many new tokens at once (prefill) by the un-absorbed branch
+ * ("MLA模型结构详解", section "结合 DeepSeek 推理代码看 MLA": the naive branch
+ * recovers the full keys and values, k^C = W^UK c and v = W^UV c, and scores
+ * [q^C; q^R] . [k^C; k^R]; worked example step 4: causal mask).  For a long
+ * prompt the explicit keys cost d_h + d_R + d_v per (token, key, head) against
+ * the absorbed route's 2 d_c + d_R, and the up-projection is paid once per
+ * cached row.
+ *   The step's n_q tokens are the last n_q of the lens[b] cached rows (append
+ *   them first, e.g. mla_append_cache with n_new = n_q); token i sits at row
+ *   p = lens[b] - n_q + i and sees rows 0 .. p:
+ *   o[b,i,h,:] = sum_{j <= p} softmax_j(scale [q^C; RoPE(q^R, p)] . [W_UK[h] c_j; kR_j]) W_UV[h] c_j
+ *   lse[b,i,h] = log sum_j exp(scale ...).
+ * q [B, n_q, n_h, d_h + d_r] (per head [content | rope], q^R NOT yet rotated:
+ * it is rotated at p) in dims->dtype; cache [cache_rows, d_c + d_r] with
+ * sequence b at rows offsets[b] ..; W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c];
+ * o [B, n_q, n_h, d_v] fp32; lse [B, n_q, n_h] fp32 or NULL.  Every cache row
+ * 0 .. cache_rows - 1 is up-projected (into the workspace, bf16), so pass the
+ * rows the batch occupies.  V3 dims in bf16 only (else MLA_ERR_SHAPE);
+ * B <= 65535.  lens[b] must be in [n_q, offsets[b+1] - offsets[b]] with
+ * offsets[b] + lens[b] <= cache_rows, else sequence b's outputs are NaN and
+ * MLA_DEVERR_LENS is set.
+ * The explicit keys, values and queries are held in fp16 (finer than bf16,
+ * so a token that sees few keys keeps the tolerance); they must lie within
+ * the fp16 range.
+ * ws: at least mla_prefill_attn_workspace(dims, B, n_q, cache_rows) bytes
+ * (cache_rows x n_h x (d_h + d_v) x 2 for the explicit keys and values). */
+mla_status_t mla_prefill_attn(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q, const void* cache,
+                              int64_t cache_rows, const int32_t* offsets, const int32_t* lens, const void* W_UK,
+                              const void* W_UV, float* o, float* lse, int32_t* err_flag, void* ws,
+                              size_t ws_bytes, void* stream);
+size_t mla_prefill_attn_workspace(const mla_dims_t* dims, int32_t B, int32_t n_q, int64_t cache_rows);
 
 /* Paged latent cache pool, shared by the layers of a model.
  *

@@ -201,3 +201,19 @@ def test_fp8_validation(lib):
     bad = v3(d_r=3)
     assert lib.mla_decode_attn_fp8(ctypes.byref(bad), 1, one, one, one, one, one, one, 100, one, None, None,
                                    one, 1 << 30, None) == 2
+
+
+def test_prefill_validation(lib):
+    d = v3()
+    one = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+    call = lambda dims, B, n_q, rows, ws_bytes: lib.mla_prefill_attn(
+        ctypes.byref(dims), B, n_q, one, one, rows, one, one, one, one, one, None, None, one, ws_bytes, None)
+    assert call(v3(n_h=64), 1, 4, 100, 1 << 40) == 2                 # not the V3 fast-path dims
+    assert call(d, 1, 0, 100, 1 << 40) == 2 and call(d, 70000, 4, 100, 1 << 40) == 2
+    assert call(d, 1, 4, 0, 1 << 40) == 2
+    assert call(d, 1, 4, 100, 10) == 4                                # workspace too small
+    need = lib.mla_prefill_attn_workspace(ctypes.byref(d), 2, 8, 100)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(100 * 128 * 256 * 2) + al(100 * 64 * 2) + al(2 * 8 * 128 * 192 * 2)
+    assert lib.mla_prefill_attn(ctypes.byref(d), 1, 4, None, one, 100, one, one, one, one, one, None, None, one,
+                                1 << 40, None) == 1
