@@ -54,7 +54,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     # default: the largest single-GPU attention workload (ragged, 1.29 GB of cache per step)
     p.add_argument("--workload", default="ragged",
-                   choices=["uniform", "ragged", "long", "layer", "causal", "paged", "fp8"])
+                   choices=["uniform", "ragged", "long", "layer", "causal", "paged", "fp8", "prefill"])
+    p.add_argument("--prefill-len", type=int, default=4096, help="prefill workload: prompt tokens per sequence")
+    p.add_argument("--prefill-batch", type=int, default=4, help="prefill workload: sequences")
     p.add_argument("--block-rows", type=int, default=64, help="paged workload: rows per pool block")
     p.add_argument("--n-q", type=int, default=4, help="causal workload: new tokens per sequence")
     p.add_argument("--norms", action="store_true",
@@ -154,6 +156,77 @@ def cpu_baseline(w, budget_s):
                       f"head-weighted cache tokens / s"}
 
 
+def bench_prefill(args):
+    """Un-absorbed prefill of B fresh prompts of T tokens (every token is new:
+    n_q = T), mla_prefill_attn timed: explicit K/V up-projection of the B T
+    cache rows, then causal attention.  Compute-bound: reported against the
+    dense fp16/bf16 MFMA peak."""
+    import torch
+
+    from head_latent_attention_16_amd import _lib as L
+    from head_latent_attention_16_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    B, T = args.prefill_batch, args.prefill_len
+    rng = np.random.default_rng(0)
+    log(f"generating prefill B={B} T={T} ...")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    lens = np.full(B, T, np.int32)
+    offsets = (np.arange(B + 1) * T).astype(np.int32)
+    cache = dev(I.bf16_bits(rng.standard_normal((B * T, 576), dtype=np.float32)))
+    q = dev(I.bf16_bits(rng.standard_normal((B, T, 128, 192), dtype=np.float32)))
+    W_UK = dev(I.bf16_bits(rng.standard_normal((128, 128, 512), dtype=np.float32) * np.float32(512 ** -0.5)))
+    W_UV = dev(I.bf16_bits(rng.standard_normal((128, 128, 512), dtype=np.float32) * np.float32(512 ** -0.5)))
+    dims = L.Dims.make(128, 512, 64, 128, 128, dtype="bf16")
+    o = torch.empty(B, T, 128, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, T, 128, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.prefill_attn_workspace(dims, B, T, B * T), dtype=torch.uint8, device="cuda")
+    lens_d, offs_d = torch.from_numpy(lens).cuda(), torch.from_numpy(offsets).cuda()
+
+    def step():
+        L.prefill_attn(dims, q, cache, offs_d, lens_d, W_UK, W_UV, o, lse, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    pairs = B * T * (T + 1) // 2
+    flops_attn = pairs * 128 * 2 * (192 + 128)
+    flops_up = 2 * B * T * 512 * (128 * 256)
+    flops = flops_attn + flops_up
+    tf = flops / (call_ms * 1e-3) / 1e12
+    log(f"prefill {call_ms * 1e3:.0f} us per call, {tf:.0f} TFLOP/s")
+    out = {
+        "metric": METRIC, "value": B * T / (ms * 1e-3), "unit": "new-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"un-absorbed prefill, B={B} fresh prompts of T={T} tokens (DeepSeek-V3 dims "
+                               f"n_h=128 d_c=512 d_R=64 d_h=d_v=128), explicit K/V in fp16",
+                   "B": B, "new_tokens": B * T, "step": "prefill_attn (up-projection + causal attention)"},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "mla_prefill_attn (k_q_rope, k_kr_f16, k_upproj, k_prefill)",
+                     "call_us": call_ms * 1e3, "flops": flops, "flops_upproj": flops_up, "flops_attention": flops_attn},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -166,6 +239,8 @@ def main():
     from head_latent_attention_16_amd import inputs as I
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "prefill":
+        return bench_prefill(args)
     torch.cuda.set_device(0)
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20

@@ -71,31 +71,34 @@ __device__ __forceinline__ void vm_wait_barrier() {
 
 // ---------------------------------------------------------------------------
 // q^R rotation: q_rot[t, h] = [q^C | RoPE(q^R, pos_t)] in fp16, pos_t the
-// token's row.  One thread per (token, head, rotation pair); the content part
-// is copied by the same threads.
+// token's row.  One block per token: the 32 rotation angles of the token are
+// formed once (fp64) and shared by its 128 heads; then 256 threads cover the
+// 128 heads x 96 value pairs.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_q_rope(int B, int n_q, double base, const __bf16* __restrict__ q,
+__global__ void __launch_bounds__(256) k_q_rope(int n_q, double base, const __bf16* __restrict__ q,
                                                 const int32_t* __restrict__ lens, _Float16* __restrict__ q_rot) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_tok = (int64_t)PN_H * (PQK / 2);
-  if (idx >= (int64_t)B * n_q * per_tok) return;
-  const int64_t t = idx / per_tok;
-  const int rem = (int)(idx - t * per_tok);
-  const int h = rem / (PQK / 2), k = rem - h * (PQK / 2);   // k < 96
+  __shared__ float s_cos[PD_R / 2], s_sin[PD_R / 2];
+  const int64_t t = blockIdx.x;   // token
   const int b = (int)(t / n_q), i = (int)(t - (int64_t)b * n_q);
-  const __bf16* src = q + (t * PN_H + h) * PQK;
-  _Float16* dst = q_rot + (t * PN_H + h) * PQK;
-  if (k < PD_H / 2) {   // content: two values per thread
-    dst[2 * k] = (_Float16)(float)src[2 * k];
-    dst[2 * k + 1] = (_Float16)(float)src[2 * k + 1];
-  } else {              // rope pair j = k - 64 of 32
-    const int j = k - PD_H / 2;
+  if (threadIdx.x < PD_R / 2) {
     const int64_t pos = (int64_t)lens[b] - n_q + i;
-    float cs, sn;
-    rope_cos_sin(pos < 0 ? 0 : pos, j, PD_R, base, &cs, &sn);
-    const float lo = (float)src[PD_H + j], hi = (float)src[PD_H + PD_R / 2 + j];
-    dst[PD_H + j] = (_Float16)(lo * cs - hi * sn);
-    dst[PD_H + PD_R / 2 + j] = (_Float16)(hi * cs + lo * sn);
+    rope_cos_sin(pos < 0 ? 0 : pos, threadIdx.x, PD_R, base, &s_cos[threadIdx.x], &s_sin[threadIdx.x]);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < PN_H * (PQK / 2); idx += 256) {
+    const int h = idx / (PQK / 2), k = idx - h * (PQK / 2);   // k < 96
+    const __bf16* src = q + (t * PN_H + h) * PQK;
+    _Float16* dst = q_rot + (t * PN_H + h) * PQK;
+    if (k < PD_H / 2) {   // content: two values per thread
+      dst[2 * k] = (_Float16)(float)src[2 * k];
+      dst[2 * k + 1] = (_Float16)(float)src[2 * k + 1];
+    } else {              // rope pair j of 32
+      const int j = k - PD_H / 2;
+      const float cs = s_cos[j], sn = s_sin[j];
+      const float lo = (float)src[PD_H + j], hi = (float)src[PD_H + PD_R / 2 + j];
+      dst[PD_H + j] = (_Float16)(lo * cs - hi * sn);
+      dst[PD_H + PD_R / 2 + j] = (_Float16)(hi * cs + lo * sn);
+    }
   }
 }
 
@@ -251,7 +254,10 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-__global__ void __launch_bounds__(256, 1) k_prefill(PrefillArgs a) {
+// Two workgroups per compute unit (80 KiB of LDS and at most 256 registers
+// per lane each), so one workgroup's softmax and barriers overlap the other's
+// matrix work.
+__global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * F_STAGE];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -339,64 +345,59 @@ __global__ void __launch_bounds__(256, 1) k_prefill(PrefillArgs a) {
     }
     const MLA_LDS char* Ks = (const MLA_LDS char*)lds + (kb & 1) * F_STAGE;
     const MLA_LDS char* Vs = Ks + F_KB_BYTES;
-    // S^T[keys x tokens] for the two 32-key halves
-    floatx16 S[2];
-#pragma unroll
+    // The block's two 32-key halves are taken one after the other, each a
+    // step of the online softmax: S^T[32 keys x 32 tokens] = K Q^T, the
+    // causal mask, the running max (rescaling what was accumulated when it
+    // moves), the weights, O^T += V^T P^T.
+#pragma unroll 1
     for (int t = 0; t < 2; ++t) {
+      floatx16 S;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
+      for (int e = 0; e < 16; ++e) S[e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < PQK / 16; ++kk) {
         const int kr = 32 * t + n32, c = 2 * kk + g;
         const halfx8 kf = *(const MLA_LDS halfx8*)(Ks + kr * F_KROWB + ((c ^ ksw(kr)) << 4));
-        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[kk], S[t], 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[kk], S, 0, 0, 0);
       }
-    }
-    // scores -> log2 units with the causal mask; key of S[t][e] is
-    // 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4
-    float x[2][16];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+      // scores in log2 units, -inf where masked; key of S[e] is
+      // 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4
+      float bmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kb * F_KB + 32 * t + 8 * (e >> 2) + 4 * g + (e & 3);
         const bool ok = key <= pos && key < len;
-        x[t][e] = ok ? S[t][e] * a.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, x[t][e]);
+        S[e] = ok ? S[e] * a.scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, S[e]);
       }
-    // the token's max over both lane halves
-    {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
-    }
-    const float m_new = fmaxf(m_run, bmax);
-    // rescale what was accumulated when the max moved (no lane's token can
-    // have m_new = -inf here: every token sees key 0 in block 0)
-    if (__any(m_new > m_run)) {
-      const float al = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-      l_run *= al;
+      // the token's max over both lane halves
+      {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
+      }
+      const float m_new = fmaxf(m_run, bmax);
+      // rescale what was accumulated when the max moved (a token whose half
+      // is fully masked keeps m_new = m_run; every token sees key 0 first)
+      if (__any(m_new > m_run)) {
+        const float al = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        l_run *= al;
 #pragma unroll
-      for (int cb = 0; cb < PD_V / 32; ++cb)
+        for (int cb = 0; cb < PD_V / 32; ++cb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) O[cb][e] *= al;
-    }
-    m_run = m_new;
-    // weights as the PV operand: P[t][kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3}
-    halfx8 P[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+          for (int e = 0; e < 16; ++e) O[cb][e] *= al;
+      }
+      m_run = m_new;
+      // weights as the PV operand: P[kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3}
+      halfx8 P[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(x[t][e] - m_new);
+        const float p = m_new == -INFINITY ? 0.f : exp2f(S[e] - m_new);
         const _Float16 ph = (_Float16)p;
-        P[t][e >> 3][e & 7] = ph;
+        P[e >> 3][e & 7] = ph;
         l_run += (float)ph;
       }
-    // O^T[value cols x tokens] += V^T . P^T, four 32-column blocks
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+      // O^T[value cols x tokens] += V^T . P^T, four 32-column blocks
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2)
 #pragma unroll
@@ -411,8 +412,9 @@ __global__ void __launch_bounds__(256, 1) k_prefill(PrefillArgs a) {
           }
           const halfx8 vf = {part[0][0], part[0][1], part[0][2], part[0][3],
                              part[1][0], part[1][1], part[1][2], part[1][3]};
-          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[t][kk2], O[cb], 0, 0, 0);
+          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[kk2], O[cb], 0, 0, 0);
         }
+    }
     asm volatile("s_barrier" ::: "memory");   // every wave is done with this stage
   }
   // normalise and store: O[cb][e] is value column 32 cb + 8 (e / 4) + 4 g + e % 4
@@ -457,8 +459,7 @@ hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, cons
   _Float16* kv = (_Float16*)ws;
   _Float16* kr = (_Float16*)((char*)ws + al((size_t)rows * PN_H * KVW * 2));
   _Float16* q_rot = (_Float16*)((char*)kr + al((size_t)rows * PD_R * 2));
-  const int64_t nth = (int64_t)B * n_q * PN_H * (PQK / 2);
-  k_q_rope<<<(unsigned)((nth + 255) / 256), 256, 0, st>>>(B, n_q, s.rope_base, (const __bf16*)q, lens, q_rot);
+  k_q_rope<<<(unsigned)((int64_t)B * n_q), 256, 0, st>>>(n_q, s.rope_base, (const __bf16*)q, lens, q_rot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_kr_f16<<<(unsigned)((rows * PD_R + 255) / 256), 256, 0, st>>>(rows, (const __bf16*)cache, kr);
