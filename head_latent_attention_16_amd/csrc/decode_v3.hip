@@ -74,27 +74,30 @@ constexpr int SPL_PER = SPL_MAXB / THREADS;           // sequences per lane
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 // Largest |O / l| a partial may carry in fp16 (max finite 65504); a piece
 // above it is flagged and its sequence recomputed by the fallback.
 constexpr float PART_MAX = 65000.0f;
 
 
 // 8-bit cache rows (E4M3 codes, one power-of-two scale per row, stored as
-// fp32): a 32-row tile is
-// 18 KiB of codes plus 128 bytes of scales.  Each wave issues five DMAs per
-// tile: waves 0-2 five 1 KiB code chunks each, wave 3 the last three
-// chunks, the scales (one dword per lane) and a repeat of the last chunk, so
-// that every wave waits for the same count.  Four 8-bit stages are followed
-// in LDS by two bf16 tiles in the layout of the 16-bit path: after a tile
-// lands, the workgroup converts it (code value x scale, exact in bf16) into
-// one of them, and the QK / PV code of the 16-bit path runs unchanged.
+// fp32): a 32-row tile is 18 KiB of codes plus 128 bytes of scales.  Each
+// wave issues five DMAs per tile: waves 0-2 five 1 KiB code chunks each,
+// wave 3 the last three chunks, the scales (one dword per lane) and a repeat
+// of the last chunk, so that every wave waits for the same count.  The codes
+// stay 8-bit in LDS: QK reads 16-byte fragments (two MFMAs' worth) and PV
+// 8-bit transpose fragments straight into registers and converts them there
+// (QK with its row's scale; for PV the scale is folded into the weights), so
+// a tile costs half the LDS reads of the 16-bit path and no converted copy.
 constexpr int F8_ROWB = DK;                       // 576 bytes per row
+constexpr int F8_CHUNKS = F8_ROWB / 16;           // 36 chunks of 16 bytes
 constexpr int F8_TILEB = TILE * F8_ROWB;          // 18432
 constexpr int F8_STAGE = F8_TILEB + 256;          // codes + scale area
 constexpr int F8_DPW = 5;
-constexpr int F8_BF16_OFF = NSTAGE * F8_STAGE;    // 74752: first bf16 tile
-constexpr int F8_LDS = F8_BF16_OFF + 2 * TILEB;   // 148480
-static_assert(F8_TILEB / 1024 == 18 && F8_BF16_OFF % 1024 == 0, "8-bit tile layout");
+constexpr int QK_PF8 = 4;                         // 16-byte QK fragments in flight
+constexpr int PV_PF8 = 6;                         // PV transpose fragments in flight
+static_assert(F8_TILEB / 1024 == 18 && NSTAGE * F8_STAGE <= NSTAGE * TILEB, "8-bit tile layout");
 
 static_assert(DMA_PER_TILE * 1024 == TILEB, "tile must be whole KiB");
 static_assert(DMA_PER_WAVE * WAVES == DMA_PER_TILE, "DMA split over the waves");
@@ -494,6 +497,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void mfma_first(floatx16& S, const bf16x8& A, const bf16x8& B) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(A), "v"(B));
 }
+// The same, for an A operand converted by VALU instructions just before: a
+// VALU write of a VGPR that an MFMA reads needs two wait states, which the
+// compiler cannot see to insert in front of an asm MFMA.  (Later fragments
+// of the 8-bit path are converted two MFMAs ahead of their use.)
+__device__ __forceinline__ void mfma_first_valu(floatx16& S, const bf16x8& A, const bf16x8& B) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(A), "v"(B));
+}
 __device__ __forceinline__ void mfma_acc(floatx16& S, const bf16x8& A, const bf16x8& B) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(A), "v"(B));
 }
@@ -512,6 +522,32 @@ __device__ __forceinline__ int swz(int r) {
   return ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
 }
 
+// Bank swizzle of a 576-byte 8-bit row: its 16-byte chunk c is stored at
+// c ^ f8sw(r) (within the aligned group of four chunks).  Row r starts at
+// bank group 4 r (mod 16), so with f8sw = bits 2..3 of r (a) 16 consecutive
+// rows at one chunk (a QK fragment read) and (b) rows {0..3, 8..11} or
+// {4..7, 12..15} (mod 16) at two neighbouring chunks (one 32-lane half of a
+// PV transpose read) each cover 16 distinct groups.
+__device__ __forceinline__ int f8sw(int r) { return (r >> 2) & 3; }
+
+// 8-bit cache: DMA slot k of wave w -> code chunk (0..17) of the tile, or -1
+// for the scales (wave 3, slot 3); wave 3's slot 4 repeats chunk 17.
+__device__ __forceinline__ int f8_chunk(int w, int k) {
+  if (w < 3) return 5 * w + k;
+  return k < 3 ? 15 + k : (k == 3 ? -1 : 17);
+}
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// eight E4M3 codes (two dwords, byte order) -> eight bf16 of code x s
+// (exact for a power-of-two s: the products are bf16 values)
+__device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, float s) {
+  const bf16x2v a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+  const bf16x2v b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+  const bf16x2v c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+  const bf16x2v d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Wave w owns heads 32w .. 32w+31.  Per 32-row tile it computes
 //   S^T[32 rows x 32 heads] = K[rows x 576] . Q^T[576 x heads]          (36 MFMA 32x32x16)
 //   O^T[512 cols x 32 heads] += C^T[cols x 32 rows] . P^T[rows x heads]  (32 MFMA 32x32x16)
@@ -524,7 +560,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   constexpr bool PAGED = MODE == 1;
   constexpr bool FP8 = MODE == 2;
   constexpr int DPW = FP8 ? F8_DPW : DMA_PER_WAVE;   // DMAs per wave and tile
-  __shared__ __attribute__((aligned(1024))) char lds[FP8 ? F8_LDS : NSTAGE * TILEB];
+  // (the 8-bit stages use the first NSTAGE * F8_STAGE bytes; all of it
+  // stages the query rows at the start of a piece)
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * TILEB];
   // in-kernel scan (SCAN): prefix of the valid lengths and the offsets
   __shared__ int64_t s_pre[SCAN ? SPL_MAXB + 1 : 1];
   __shared__ int32_t s_off[SCAN ? SPL_MAXB : 1];
@@ -856,11 +894,23 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
   #pragma unroll
     for (int j = 0; j < (DMA_PER_WAVE + 1) / 2; ++j) dma_pk[j] = 0;
   #pragma unroll
-    for (int k = 0; k < DMA_PER_WAVE; ++k) {
-      const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
-      const int r = p / CHUNKS;
-      const int c = (p % CHUNKS) ^ swz(r);
-      dma_pk[k >> 1] |= (uint32_t)(r * ROWB + c * 16) << (16 * (k & 1));
+    for (int k = 0; k < DPW; ++k) {
+      uint32_t off;
+      if constexpr (FP8) {
+        // 8-bit: LDS chunk p = 64 j + i of the tile holds logical chunk
+        // (p % 36) ^ f8sw(row) of row p / 36 (the scale slot's offset is unused)
+        const int j = f8_chunk(wave, k);
+        const int p = 64 * (j < 0 ? 0 : j) + lane;
+        const int r = p / F8_CHUNKS;
+        const int c = (p % F8_CHUNKS) ^ f8sw(r);
+        off = (uint32_t)(r * F8_ROWB + c * 16);
+      } else {
+        const int p = (wave * DMA_PER_WAVE + k) * 64 + lane;
+        const int r = p / CHUNKS;
+        const int c = (p % CHUNKS) ^ swz(r);
+        off = (uint32_t)(r * ROWB + c * 16);
+      }
+      dma_pk[k >> 1] |= off << (16 * (k & 1));
     }
     auto dma_off = [&](int k) -> uint32_t { return (dma_pk[k >> 1] >> (16 * (k & 1))) & 0xffffu; };
 
@@ -911,7 +961,17 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       make_qk_off(qo);
       const MLA_LDS char* T = (const MLA_LDS char*)lds + wave * TILEB;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) q[kk] = *(const MLA_LDS bf16x8*)(T + qo[kk & 3] + (kk >> 2) * 128);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        if constexpr (FP8) {
+          // 8-bit path: MFMA kk takes features 32 (kk/2) + 16 g32 + 8 (kk%2) .. +8,
+          // the order of its 16-byte code fragments (logical bf16 chunk
+          // 4 (kk/2) + 2 g32 + kk%2, stored at that ^ swz(n32))
+          const int L = 4 * (kk >> 1) + 2 * g32 + (kk & 1);
+          q[kk] = *(const MLA_LDS bf16x8*)(T + n32 * ROWB + ((L ^ swz(n32)) << 4));
+        } else {
+          q[kk] = *(const MLA_LDS bf16x8*)(T + qo[kk & 3] + (kk >> 2) * 128);
+        }
+      }
       barrier_all_lds();   // every wave has its Q before the tiles overwrite the stages
     }
 
@@ -983,20 +1043,14 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
     auto stage_of = [&](int t) -> uint32_t {
       return lds0 + (uint32_t)((t % NSTAGE) * (FP8 ? F8_STAGE : TILEB));
     };
-    // 8-bit cache: the DMA slot k of this wave -> code chunk (0..17), or -1
-    // for the scales (wave 3, slot 3); wave 3's slot 4 repeats chunk 17.
-    auto f8_chunk = [&](int k) -> int {
-      if (wave < 3) return 5 * wave + k;
-      return k < 3 ? 15 + k : (k == 3 ? -1 : 17);
-    };
     // the k-th DMA of this wave for a tile
     auto dma_slot = [&](int k, uint32_t stage_lds, const TileSrc& src) {
       if constexpr (FP8) {
-        const int j = f8_chunk(k);
+        const int j = f8_chunk(wave, k);
         if (j < 0) {
           dma_4B_at(stage_lds + F8_TILEB, src.scl + 4 * (lane_id < src.nv ? lane_id : src.nv - 1));
         } else {
-          dma_16B(stage_lds + (uint32_t)(j * 1024), min((uint32_t)((64 * j + lane_id) * 16), src.bound), src.a0);
+          dma_16B(stage_lds + (uint32_t)(j * 1024), min(dma_off(k), src.bound), src.a0);
         }
       } else {
         dma(stage_lds + (uint32_t)((wave * DMA_PER_WAVE + k) * 1024), min(dma_off(k), src.bound), src);
@@ -1008,41 +1062,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 #pragma unroll
       for (int k = 0; k < DPW; ++k) dma_slot(k, stage_lds, src);
     };
-    // bf16 tile read by QK / PV for tile t
+    // tile read by QK / PV for tile t (its stage)
     auto ctile = [&](int t) -> const MLA_LDS char* {
-      if constexpr (FP8) return (const MLA_LDS char*)lds + F8_BF16_OFF + (t & 1) * TILEB;
-      else return (const MLA_LDS char*)lds + (t % NSTAGE) * TILEB;
-    };
-    // 8-bit cache: convert the landed tile t into its bf16 tile (the whole
-    // workgroup; 2304 chunks of 8 codes, nine per thread): code value x row
-    // scale (exact in bf16: a power-of-two scale), stored at the swizzled chunk position.
-    auto convert_tile = [&](int t) {
-      if constexpr (FP8) {
-        const MLA_LDS char* src = (const MLA_LDS char*)lds + (t % NSTAGE) * F8_STAGE;
-        const MLA_LDS float* sc = (const MLA_LDS float*)(src + F8_TILEB);
-        MLA_LDS char* dst = (MLA_LDS char*)lds + F8_BF16_OFF + (t & 1) * TILEB;
-#pragma unroll 3
-        for (int k = 0; k < (TILE * CHUNKS) / THREADS; ++k) {
-          const int q = (int)threadIdx.x + THREADS * k;
-          const int r = q / CHUNKS, c = q - r * CHUNKS;
-          const u32x2 raw = *(const MLA_LDS u32x2*)(src + r * F8_ROWB + c * 8);
-          const float sr = sc[r];
-          bf16x8 o;
-          const floatx2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[0], false);
-          const floatx2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[0], true);
-          const floatx2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[1], false);
-          const floatx2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[1], true);
-          o[0] = (__bf16)(f0[0] * sr);
-          o[1] = (__bf16)(f0[1] * sr);
-          o[2] = (__bf16)(f1[0] * sr);
-          o[3] = (__bf16)(f1[1] * sr);
-          o[4] = (__bf16)(f2[0] * sr);
-          o[5] = (__bf16)(f2[1] * sr);
-          o[6] = (__bf16)(f3[0] * sr);
-          o[7] = (__bf16)(f3[1] * sr);
-          *(MLA_LDS bf16x8*)(dst + r * ROWB + ((c ^ swz(r)) << 4)) = o;
-        }
-      }
+      return (const MLA_LDS char*)lds + (t % NSTAGE) * (FP8 ? F8_STAGE : TILEB);
     };
     // Wait for tile `it`: the tiles it+1 and it+2 were issued after it.
 
@@ -1129,15 +1151,106 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       ovf_any = ovf_any || (smax > s_thr);
     };
 
+    // ---- 8-bit path: fragments straight from the code tile ----
+    // QK A-fragment pair c2 (MFMAs 2 c2 and 2 c2 + 1): lane (n32, g32) reads the
+    // 16 codes of row n32 at logical chunk 2 c2 + g32 (features 32 c2 + 16 g32
+    // .. +16: the first eight feed MFMA 2 c2, the rest MFMA 2 c2 + 1), stored at
+    // 4 (c2 / 2) + ((2 (c2 % 2) + g32) ^ f8sw(n32)).
+    auto make_qk8_off = [&](uint32_t (&o)[2]) {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      ln &= 63;
+      const int n = ln & 31, h = ln >> 5;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) o[v] = (uint32_t)(n * F8_ROWB + (((2 * v + h) ^ f8sw(n)) << 4));
+    };
+    auto qk8_frag = [&](const MLA_LDS char* Tt, const uint32_t (&o)[2], int c2) -> u32x4 {
+      return *(const MLA_LDS u32x4*)(Tt + o[c2 & 1] + (c2 >> 1) * 64);
+    };
+    // scale of this lane's QK row (n32) of a tile
+    auto row_scale = [&](const MLA_LDS char* Tt) -> float {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      ln &= 31;
+      return *(const MLA_LDS float*)(Tt + F8_TILEB + 4 * ln);
+    };
+    // PV A-fragment by 8-bit transpose reads.  In each 16-lane group G
+    // (i = lane % 16) lanes 2k and 2k+1 read the two 8-byte halves of row
+    // rho_k = 16 kk2 + 8 (k / 4) + 4 g32 + k % 4 at columns 32 cb + 16 (G & 1)
+    // .. +16; after the transpose lane j of the group holds column
+    // 32 cb + 16 (G & 1) + j of rows rho_0 .. rho_7, the rows whose weights
+    // the lane holds in P[kk2].  f8sw(rho_k) = 2 (k / 4) + g32 for both kk2,
+    // so logical chunk 2 cb + (G & 1) sits at 4 (cb / 2) + ((2 (cb % 2) + (G & 1)) ^ f).
+    auto make_tr8_base = [&](uint32_t (&t)[2]) {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      ln &= 63;
+      const int i16 = ln & 15, k = i16 >> 1;
+      const int rho = 8 * (k >> 2) + 4 * (ln >> 5) + (k & 3);
+      const int f = f8sw(rho);
+      const int gh = (ln >> 4) & 1;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        t[v] = (uint32_t)(rho * F8_ROWB + (((2 * v + gh) ^ f) << 4) + 8 * (i16 & 1));
+    };
+    // QK of tile t (no softmax beside it): the prologue
+    auto qk8 = [&](int t, floatx16& S) {
+      const MLA_LDS char* Tt = ctile(t);
+      uint32_t o8[2];
+      make_qk8_off(o8);
+      const float sq = row_scale(Tt);
+      u32x4 kf[QK_PF8];
+#pragma unroll
+      for (int j = 0; j < QK_PF8; ++j) kf[j] = qk8_frag(Tt, o8, j);
+      bf16x8 A[3];
+      A[0] = cvt8(kf[0][0], kf[0][1], sq);
+      A[1] = cvt8(kf[0][2], kf[0][3], sq);
+      kf[0] = qk8_frag(Tt, o8, QK_PF8);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        if (kk == 0)
+          mfma_first_valu(S, A[0], q[0]);
+        else
+          mfma_acc(S, A[kk % 3], q[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nk = kk + 2;
+        if (nk < KSTEPS) {
+          const int c2 = nk >> 1;
+          const u32x4 f = kf[c2 % QK_PF8];
+          A[nk % 3] = (nk & 1) ? cvt8(f[2], f[3], sq) : cvt8(f[0], f[1], sq);
+          if ((nk & 1) && c2 + QK_PF8 < KSTEPS / 2) kf[c2 % QK_PF8] = qk8_frag(Tt, o8, c2 + QK_PF8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_drain(S);
+    };
+    // softmax of tile it spread over the QK steps of tile it+1: one pair of
+    // weights after each odd step, their row sums later (the 16-bit loop
+    // below writes the same steps inline)
+    auto sm_step = [&](int kk, const floatx16& Sc, float& smax, float (&x)[16], float (&e)[16],
+                       bf16x8 (&P)[2]) {
+      if (kk < 16) {
+        x[kk] = fmaf(Sc[kk], a.scale_log2, -m_ref);
+        if (kk & 1) smax = max3f(smax, Sc[kk - 1], Sc[kk]);
+      }
+      if (kk >= 4 && kk < 20) e[kk - 4] = __builtin_amdgcn_exp2f(x[kk - 4]);
+      if (kk >= 9 && kk < 25 && (kk & 1)) {
+        const int j = (kk - 9) / 2;
+        P[j >> 2][2 * (j & 3)] = (__bf16)e[2 * j];
+        P[j >> 2][2 * (j & 3) + 1] = (__bf16)e[2 * j + 1];
+      }
+      if (kk >= 26 && kk < 34) sm_sum(P, kk - 26);
+    };
+
     // ---- prologue: QK of tile 0 and the reference max ----
     floatx16 S_cur;
     wait_vm_then_barrier<(NSTAGE - 2) * DPW>();   // tile 0 landed
     if constexpr (FP8) {
-      convert_tile(0);
-      barrier_all_lds();
+      qk8(0, S_cur);
+    } else {
+      qk(0, S_cur);
+      qk_schedule();
     }
-    qk(0, S_cur);
-    qk_schedule();
     {
       float mloc = -INFINITY;
 #pragma unroll
@@ -1148,6 +1261,113 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       m_ref = fmaxf(mloc, swap_halves(mloc, lane));
       s_thr = (m_ref + OVF_TH) / a.scale_log2;
     }
+
+    // ---- 8-bit software pipeline: the same steps, fragments converted in registers ----
+    if constexpr (FP8) {
+      for (int it = 0; it < ntiles; ++it) {
+        const int nvalid = seg_len - it * TILE;
+        const TileSrc nsrc = dma_src(it + NSTAGE - 1);
+        const MLA_LDS char* T = ctile(it);
+        bf16x8 P[2], Pv[2];
+        floatx16 S_next;
+        uint32_t tr8b[2];
+        i32x2 pa8[PV_PF8];
+        auto pv8_frag = [&](int j) {
+          const int kk2 = j / (DC / 32), cb = j % (DC / 32);
+          pa8[j % PV_PF8] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (MLA_LDS i32x2*)(T + tr8b[cb & 1] + kk2 * 16 * F8_ROWB + (cb >> 1) * 64));
+        };
+        // PV weights with the row scales folded in: weight i of this lane
+        // belongs to row 8 (i / 4) + 4 g32 + i % 4; bf16 x power of two is exact
+        floatx4 s4[4];
+        auto load_s4 = [&]() {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            s4[r4] = *(const MLA_LDS floatx4*)(T + F8_TILEB + 4 * (8 * r4 + 4 * g32));
+        };
+        auto pv_scale = [&](int j) {
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int i = 2 * j + e2;
+            Pv[i >> 3][i & 7] = (__bf16)((float)P[i >> 3][i & 7] * s4[i >> 2][i & 3]);
+          }
+        };
+        if (it + 1 < ntiles) {
+          uint32_t o8[2];
+          make_qk8_off(o8);
+          wait_vm_then_barrier<(NSTAGE - 3) * DPW>();
+          floatx16 Sc = S_cur;
+          asm volatile("" : "+v"(Sc));
+          const MLA_LDS char* Tn = ctile(it + 1);
+          const float sq = row_scale(Tn);
+          u32x4 kf[QK_PF8];
+#pragma unroll
+          for (int j = 0; j < QK_PF8; ++j) kf[j] = qk8_frag(Tn, o8, j);
+          bf16x8 A[3];
+          A[0] = cvt8(kf[0][0], kf[0][1], sq);
+          A[1] = cvt8(kf[0][2], kf[0][3], sq);
+          kf[0] = qk8_frag(Tn, o8, QK_PF8);
+          float smax = -INFINITY;
+          float x[16], e[16];
+#pragma unroll
+          for (int kk = 0; kk < KSTEPS; ++kk) {
+            if (kk == 0)
+              mfma_first_valu(S_next, A[0], q[0]);
+            else
+              mfma_acc(S_next, A[kk % 3], q[kk]);
+            __builtin_amdgcn_sched_barrier(0);
+            // fragment of MFMA kk+2, converted two steps ahead of its use
+            const int nk = kk + 2;
+            if (nk < KSTEPS) {
+              const int c2 = nk >> 1;
+              const u32x4 f = kf[c2 % QK_PF8];
+              A[nk % 3] = (nk & 1) ? cvt8(f[2], f[3], sq) : cvt8(f[0], f[1], sq);
+              if ((nk & 1) && c2 + QK_PF8 < KSTEPS / 2) kf[c2 % QK_PF8] = qk8_frag(Tn, o8, c2 + QK_PF8);
+            }
+            sm_step(kk, Sc, smax, x, e, P);
+            if (kk == 20) load_s4();
+            if (kk >= 26 && kk < 34) pv_scale(kk - 26);
+            if (kk == KSTEPS - PV_PF8 - 2) make_tr8_base(tr8b);
+            if (kk >= KSTEPS - PV_PF8 - 1 && kk < KSTEPS - 1) pv8_frag(kk - (KSTEPS - PV_PF8 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          mfma_drain(S_next);
+          ovf_any = ovf_any || (smax > s_thr);
+        } else {
+          barrier_all_lds();
+          floatx16 Sc = S_cur;
+          asm volatile("" : "+v"(Sc));
+          softmax(Sc, nvalid, P);
+          load_s4();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv_scale(j);
+          make_tr8_base(tr8b);
+#pragma unroll
+          for (int j = 0; j < PV_PF8; ++j) pv8_frag(j);
+        }
+
+        // ---- O^T += C^T . P'^T; tile it+3's DMAs spread as in the 16-bit loop ----
+        {
+          const int nt = it + NSTAGE - 1;
+          const uint32_t stage_lds = stage_of(nt);
+          bf16x8 cf = cvt8((uint32_t)pa8[0][0], (uint32_t)pa8[0][1], 1.0f);
+#pragma unroll
+          for (int s = 0; s < 2 * (DC / 32); ++s) {
+            const int kk2 = s / (DC / 32), cb = s % (DC / 32);
+            // fragment s + PV_PF8 into the slot of fragment s (converted)
+            if (s + PV_PF8 < 2 * (DC / 32)) pv8_frag(s + PV_PF8);
+            O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, Pv[kk2], O[cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < 2 * (DC / 32)) {
+              cf = cvt8((uint32_t)pa8[(s + 1) % PV_PF8][0], (uint32_t)pa8[(s + 1) % PV_PF8][1], 1.0f);
+            }
+            if (s % 3 == 2 && s / 3 < DPW) dma_slot(s / 3, stage_lds, nsrc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        S_cur = S_next;
+      }
+    } else {
 
     // ---- software pipeline: [QK(it+1) || softmax(it)], then PV(it) ----
     for (int it = 0; it < ntiles; ++it) {
@@ -1180,12 +1400,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         uint32_t qk_off[4];
         make_qk_off(qk_off);   // lane arithmetic only: ahead of the wait
         wait_vm_then_barrier<(NSTAGE - 3) * DPW>();
-        if constexpr (FP8) {
-          // tile it+1 landed for every wave; its bf16 tile held tile it-1,
-          // whose PV every wave has finished
-          convert_tile(it + 1);
-          barrier_all_lds();
-        }
         floatx16 Sc = S_cur;
         asm volatile("" : "+v"(Sc));
         // QK of tile it+1 with the softmax of tile it in its MFMA gaps: one
@@ -1275,6 +1489,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       }
       S_cur = S_next;
     }
+    }   // 16-bit loop
     const size_t slot = (size_t)g + (size_t)b;
     // DMAs issued during the last tiles only fill stages this piece no
     // longer reads; they must land before a next piece reuses the stages.

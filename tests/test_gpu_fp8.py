@@ -1,9 +1,11 @@
 """The 8-bit latent cache: rows stored as E4M3 codes with one power-of-two
 scale per row.  The append must produce the oracle's codes and scales bit for
 bit (where both sides see the same fp32 row values); the decode must match
-the oracle over the dequantised rows and, since code x scale is exact in bf16,
-give exactly the bits of the 16-bit decode over a bf16 cache holding the
-dequantised values."""
+the oracle over the dequantised rows and agree closely with the 16-bit decode
+over a bf16 cache holding the dequantised values (code x scale is exact in
+bf16; the 8-bit kernel groups the 576 score features into MFMAs in another
+order, so the fp32 scores, and through them a weight's bf16 rounding, may
+differ in the last bits)."""
 
 import math
 
@@ -54,6 +56,15 @@ def _decode_pair(u, codes, scales, bf16_cache, hint):
         assert int(err.item()) == 0
         out.append((o_lat, lse))
     return out, host_f64(q_lat), host_f64(q_pe)
+
+
+def _close_to_16bit(a, b, la, lb, tag):
+    """The 8-bit decode against the 16-bit decode over the dequantised rows:
+    the same products, summed in another grouping."""
+    compare(host_f64(a), host_f64(b), f"{tag} o_lat vs 16-bit", max_abs=2e-3, mean_abs=2e-5, norm_max=1e-2,
+            norm_mean=2e-5)
+    compare(host_f64(la), host_f64(lb), f"{tag} lse vs 16-bit", max_abs=1e-4, mean_abs=1e-5, norm_max=1e-4,
+            norm_mean=1e-5)
 
 
 def _check_oracle(w, codes_np, scales_np, o_lat, lse, ql, qp, b, heads, tag):
@@ -121,14 +132,14 @@ def test_fp8_decode_small(lens):
     codes, scales, bf = _quantized(w)
     pair, ql, qp = _decode_pair(u, dev(codes), dev(scales), dev(bf), w.total_rows)
     (a, la), (b, lb) = pair
-    assert torch.equal(a, b) and torch.equal(la, lb)
+    _close_to_16bit(a, b, la, lb, f"fp8 lens={lens}")
     for s in range(w.B):
         _check_oracle(w, codes, scales, a, la, ql, qp, s, list(range(128)), "fp8")
 
 
 def test_fp8_full_size_ragged():
-    """The ragged workload (B=64, 1.1M rows) quantised to 8 bits: identical
-    bits to the 16-bit decode over the rounded values, and the oracle over
+    """The ragged workload (B=64, 1.1M rows) quantised to 8 bits: close to
+    the 16-bit decode over the rounded values, and the oracle over
     the dequantised rows on every head of the shortest and longest sequence."""
     w = I.make("ragged")
     say(f"fp8 full size ragged: rows={w.total_rows}")
@@ -137,7 +148,7 @@ def test_fp8_full_size_ragged():
     del u.cache
     pair, ql, qp = _decode_pair(u, dev(codes), dev(scales), dev(bf), w.total_rows)
     (a, la), (b, lb) = pair
-    assert torch.equal(a, b) and torch.equal(la, lb)
+    _close_to_16bit(a, b, la, lb, "fp8 ragged")
     for s in (int(np.argmin(w.lens)), int(np.argmax(w.lens))):
         _check_oracle(w, codes, scales, a, la, ql, qp, s, list(range(128)), "fp8 ragged")
 
