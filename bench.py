@@ -318,7 +318,6 @@ def main():
     tok_pos = torch.from_numpy((np.repeat(w.lens.astype(np.int64), n_q) - n_q
                                 + np.tile(np.arange(n_q), B)).astype(np.int32)).cuda()
     u = torch.empty(B, d["d_model"], dtype=torch.float32, device="cuda") if layer else None
-    pos = [s["lens"].clone() for s in sets]
     ws_dec = torch.empty(L.decode_attn_causal_workspace(dims, B, n_q, hint), dtype=torch.uint8, device="cuda")
 
     def attend(s):
@@ -347,14 +346,15 @@ def main():
         """One pass of the hot path over input copy c (launches only)."""
         s = sets[c]
         if layer:
-            pos[c].copy_(s["lens"])   # query position = current length
+            # query position = current length: the absorb runs before the
+            # append on the stream, so it reads lens before the increment
             if args.norms:
-                L.absorb_q_normed(dims, q_lat, q_pe, s["W_UK"], pos[c], s["h_t"], s["W_DQ"], s["q_norm_w"],
+                L.absorb_q_normed(dims, q_lat, q_pe, s["W_UK"], s["lens"], s["h_t"], s["W_DQ"], s["q_norm_w"],
                                   s["W_UQ"], ws=ws_abs)
                 L.append_cache_normed(dims, s["cache"], s["offsets"], s["lens"], 1, s["h_t"], s["W_DKV"],
                                       s["kv_norm_w"], s["W_KR"], ws=ws_app)
             else:
-                L.absorb_q(dims, q_lat, q_pe, s["W_UK"], pos[c], h_t=s["h_t"], W_DQ=s["W_DQ"],
+                L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["lens"], h_t=s["h_t"], W_DQ=s["W_DQ"],
                            W_UQ=s["W_UQ"], ws=ws_abs)
                 L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
                                W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)

@@ -75,8 +75,8 @@ bool force_generic() { return env_flag("MLA_FORCE_GENERIC"); }
 bool fast_linear(const Shape& s, int M, int N, int K) {
   return !force_generic() && s.bf16 && gemm_v3_supported(M, N, K);
 }
-size_t linear_ws(const Shape& s, int M, int N, int K) {
-  return fast_linear(s, M, N, K) ? gemm_v3_workspace(M, N, K) : 0;
+size_t linear_ws(const Shape& s, int M, int N, int K, bool x_f32) {
+  return fast_linear(s, M, N, K) ? gemm_v3_workspace(M, N, K, x_f32) : 0;
 }
 hipError_t linear(const Shape& s, int M, int N, int K, const void* X, bool x_f32, const void* W,
                   float* Y, void* part, hipStream_t st) {
@@ -90,9 +90,10 @@ size_t absorb_ws(const Shape& s, int B, bool from_hidden) {
   const int qw = s.n_h * (s.d_h + s.d_r);
   size_t cq = s.d_q > 0 ? align256((size_t)B * s.d_q * sizeof(float)) : 0;
   size_t q = align256((size_t)B * qw * sizeof(float));
-  size_t part = linear_ws(s, B, qw, s.d_q > 0 ? s.d_q : s.d_model);
+  // W^UQ reads the fp32 c^Q (or h_t directly), W^DQ reads h_t
+  size_t part = linear_ws(s, B, qw, s.d_q > 0 ? s.d_q : s.d_model, s.d_q > 0 || !s.bf16);
   if (s.d_q > 0) {
-    const size_t p1 = linear_ws(s, B, s.d_q, s.d_model);
+    const size_t p1 = linear_ws(s, B, s.d_q, s.d_model, !s.bf16);
     if (p1 > part) part = p1;
   }
   return cq + q + align256(part);
@@ -105,10 +106,10 @@ size_t append_ws(const Shape& s, int B, int n_new, bool from_hidden) {
   const int M = B * n_new;
   size_t part = 0;
   if (fused_kv(s, M)) {
-    part = gemm_v3_workspace(M, s.d_c + s.d_r, s.d_model);
+    part = gemm_v3_workspace(M, s.d_c + s.d_r, s.d_model, false);
   } else {
-    part = linear_ws(s, M, s.d_c, s.d_model);
-    const size_t p2 = linear_ws(s, M, s.d_r, s.d_model);
+    part = linear_ws(s, M, s.d_c, s.d_model, !s.bf16);
+    const size_t p2 = linear_ws(s, M, s.d_r, s.d_model, !s.bf16);
     if (p2 > part) part = p2;
   }
   return align256((size_t)M * (s.d_c + s.d_r) * sizeof(float)) + align256(part);
@@ -116,7 +117,7 @@ size_t append_ws(const Shape& s, int B, int n_new, bool from_hidden) {
 size_t project_ws(const Shape& s, int B, bool with_u) {
   if (!with_u) return 0;
   return align256((size_t)B * s.n_h * s.d_v * sizeof(float)) +
-         align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v));
+         align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v, true));
 }
 // Query tokens per call (B n_q): the combine and generic decode grids index
 // them in their second dimension.

@@ -18,7 +18,9 @@
 //   k-step j; A and B use the same order, so the dot products are unchanged.
 // * fp32 X (an intermediate such as c^Q, or the attention output o) enters
 //   the bf16 MFMA as hi + lo with hi = bf16(x), lo = bf16(x - hi): two MFMAs
-//   per step, about 16 significant bits of x instead of 8.
+//   per step, about 16 significant bits of x instead of 8.  The split is done
+//   once per call by k_hilo into two bf16 planes in the workspace, not by
+//   every column block that stages the same X.
 // * X is loaded in whole-row 16-byte pieces (every wave instruction reads
 //   full cache lines) and staged in LDS one chunk ahead.  The X and W loads
 //   of the chunk PD ahead and that staging are spread over the MFMA stream
@@ -44,7 +46,7 @@ constexpr int SLOTS = 256;        // workgroups per round (one per compute unit)
 constexpr int FPF = 8;            // A fragments read ahead
 
 struct GemmArgs {
-  const void* X;        // [M][K], bf16 or fp32
+  const __bf16* X;      // [NPL][M][K] bf16: X, or its hi and lo planes
   const __bf16* W1;     // rows 0 .. N1-1: W1[n][K]
   const __bf16* W2;     // rows N1 .. N-1: W2[n - N1][K] (may equal W1 + N1 K)
   float* Y;             // [M][N] when splits == 1
@@ -60,9 +62,24 @@ struct GemmArgs {
 // groups.
 __device__ __forceinline__ int xsw(int r) { return (r >> 1) & 7; }
 
-template <bool XF32>
+// hi = bf16(x), lo = bf16(x - hi) of fp32 X [n4 x 4], planes [2][n4 x 4]
+__global__ void __launch_bounds__(256) k_hilo(size_t n4, const floatx4* __restrict__ X, bf16x4* __restrict__ hi,
+                                              bf16x4* __restrict__ lo) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const floatx4 x = X[i];
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (__bf16)x[e];
+      l[e] = (__bf16)(x[e] - (float)h[e]);
+    }
+    hi[i] = h;
+    lo[i] = l;
+  }
+}
+
+template <int NPLANE>   // 1: bf16 X; 2: hi and lo planes of fp32 X
 __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
-  constexpr int NPLANE = XF32 ? 2 : 1;   // hi (and lo) planes
   __shared__ __attribute__((aligned(16))) char xs[2][NPLANE][GMR * XROWB];
 
   const int nb = blockIdx.x, sk = blockIdx.y, mc = blockIdx.z;
@@ -81,9 +98,9 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
                                     : a.W2 + (size_t)(nrow - a.N1) * a.K) + kb + 32 * g32;
 
   // X staging, coalesced: load i of thread t covers 16 bytes at flat index
-  // f = 256 i + t of the chunk, so each wave instruction reads whole rows.
-  // fp32: 16 per row (rows 16 i + t / 16); bf16: 8 per row (rows 32 i + t / 8).
-  constexpr int XPR = XF32 ? 16 : 8;   // 16-byte pieces per row per chunk
+  // f = 256 i + t of a plane's chunk, so each wave instruction reads whole
+  // rows: 8 per row (rows 32 i + t / 8), four per plane.
+  constexpr int XPR = 8;               // 16-byte pieces per row per chunk
   const int xq = tid % XPR;            // this thread's piece within its row
   const int xrb = tid / XPR;           // its row within each group of 256 pieces
   constexpr int XRS = 256 / XPR;       // rows per load index
@@ -102,58 +119,33 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   // X staging registers, PD chunks deep: X(k) and W(k) are issued in the
   // same chunk (X first), so waiting for X(c+1) before storing it to LDS
   // never forces a newer W chunk to complete -- vmcnt completes in issue
-  // order.
-  floatx4 xf[XF32 ? PD : 1][8];
-  bf16x8 xb[XF32 ? 1 : PD][4];
+  // order.  Piece i = 4 p + i4 is row group i4 of plane p.
+  constexpr int XPIECES = 4 * NPLANE;       // 16-byte X loads per thread per chunk
+  bf16x8 xb[PD][XPIECES];
   // Every global load in the main loop is unconditional (indices are clamped
   // to valid data and rows past M are zeroed when stored to LDS), so that the
   // compiler can count outstanding loads exactly.
-  auto xrow_src = [&](int i) { return (size_t)min(m0 + xrb + XRS * i, a.M - 1) * a.K + kb; };
-  auto load_x = [&](int slot, int c) {
-    if constexpr (XF32) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        xf[slot][i] = *(const floatx4*)((const float*)a.X + xrow_src(i) + (size_t)c * KC + 4 * xq);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xb[slot][i] = *(const bf16x8*)((const __bf16*)a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
-    }
+  const size_t plane = (size_t)a.M * a.K;
+  auto xrow_src = [&](int i) {
+    return (size_t)(i >> 2) * plane + (size_t)min(m0 + xrb + XRS * (i & 3), a.M - 1) * a.K + kb;
   };
-  auto store_x = [&](int slot, int stage) {
-    if constexpr (XF32) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = xrb + XRS * i;
-        const bool ok = m0 + r < a.M;
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = ok ? xf[slot][i][e] : 0.f;
-          hi[e] = (__bf16)x;
-          lo[e] = (__bf16)(x - (float)hi[e]);
-        }
-        // k = 4 xq .. +4: 16-byte chunk xq / 2, half xq & 1
-        const int off = r * XROWB + ((((xq >> 1) ^ xsw(r)) << 4) | ((xq & 1) << 3));
-        *(bf16x4*)(xs[stage][0] + off) = hi;
-        *(bf16x4*)(xs[stage][NPLANE - 1] + off) = lo;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = xrb + XRS * i;
-        const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
-        *(bf16x8*)(xs[stage][0] + off) = m0 + r < a.M ? xb[slot][i] : bf16x8{};
-      }
-    }
+  auto load_x_piece = [&](int slot, int c, int i) {
+    xb[slot][i] = *(const bf16x8*)(a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
+  };
+  auto store_x_piece = [&](int slot, int stage, int i) {
+    const int r = xrb + XRS * (i & 3);
+    const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
+    *(bf16x8*)(xs[stage][i >> 2] + off) = m0 + r < a.M ? xb[slot][i] : bf16x8{};
   };
 
 #pragma unroll
   for (int s = 0; s < PD; ++s) {
-    load_x(s, min(s, nch - 1));
+#pragma unroll
+    for (int i = 0; i < XPIECES; ++i) load_x_piece(s, min(s, nch - 1), i);
     load_w(s, min(s, nch - 1));
   }
-  store_x(0, 0);
+#pragma unroll
+  for (int i = 0; i < XPIECES; ++i) store_x_piece(0, 0, i);
   __syncthreads();
 
   // A-fragment LDS offsets for step j of block mb: row 32 mb + n32,
@@ -163,34 +155,6 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   for (int mb = 0; mb < GMB; ++mb) aoff[mb] = (uint32_t)((32 * mb + n32) * XROWB);
   const int asw = xsw(n32);   // (32 mb + n32) >> 1 & 7 == n32 >> 1 & 7
 
-  // Per-piece forms of the staging steps, so they can be spread over the
-  // MFMA stream of a chunk.
-  auto load_x_piece = [&](int slot, int c, int i) {
-    if constexpr (XF32)
-      xf[slot][i] = *(const floatx4*)((const float*)a.X + xrow_src(i) + (size_t)c * KC + 4 * xq);
-    else
-      xb[slot][i] = *(const bf16x8*)((const __bf16*)a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
-  };
-  auto store_x_piece = [&](int slot, int stage, int i) {
-    const int r = xrb + XRS * i;
-    const bool ok = m0 + r < a.M;
-    if constexpr (XF32) {
-      bf16x4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = ok ? xf[slot][i][e] : 0.f;
-        hi[e] = (__bf16)x;
-        lo[e] = (__bf16)(x - (float)hi[e]);
-      }
-      const int off = r * XROWB + ((((xq >> 1) ^ xsw(r)) << 4) | ((xq & 1) << 3));
-      *(bf16x4*)(xs[stage][0] + off) = hi;
-      *(bf16x4*)(xs[stage][NPLANE - 1] + off) = lo;
-    } else {
-      const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
-      *(bf16x8*)(xs[stage][0] + off) = ok ? xb[slot][i] : bf16x8{};
-    }
-  };
-  constexpr int XPIECES = XF32 ? 8 : 4;     // 16-byte X loads per thread per chunk
   constexpr int NF = 4 * NPLANE * GMB;      // MFMAs (= A fragments) per chunk
   constexpr int PER_J = NPLANE * GMB;       // MFMAs per W fragment
   constexpr int ST0 = NF / 2 - XPIECES;     // first step of the X staging
@@ -289,17 +253,34 @@ bool gemm_v3_supported(int M, int N, int K) {
   return M >= 1 && N >= 32 && N % 32 == 0 && K >= KC * PD && K % (KC * PD) == 0;
 }
 
-size_t gemm_v3_workspace(int M, int N, int K) {
+// Workspace: the split partials [splits][M][N] fp32 (when splits > 1), then
+// for fp32 X its hi and lo planes [2][M][K] bf16.
+static size_t part_bytes(const Plan& p, int M, int N) {
+  return p.splits > 1 ? ((size_t)p.splits * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+}
+
+size_t gemm_v3_workspace(int M, int N, int K, bool x_f32) {
   if (!gemm_v3_supported(M, N, K)) return 0;
   const Plan p = plan(M, N, K);
-  return p.splits > 1 ? ((size_t)p.splits * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+  return part_bytes(p, M, N) + (x_f32 ? ((size_t)2 * M * K * sizeof(__bf16) + 255) / 256 * 256 : 0);
 }
 
 hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32, const void* W1,
                           const void* W2, float* Y, void* ws, hipStream_t st) {
   const Plan p = plan(M, N, K);
   GemmArgs a;
-  a.X = X;
+  a.X = (const __bf16*)X;
+  if (x_f32) {
+    __bf16* planes = (__bf16*)((char*)ws + part_bytes(p, M, N));
+    const size_t n4 = (size_t)M * K / 4;   // K is a multiple of 256
+    size_t blocks = (n4 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    k_hilo<<<(unsigned)blocks, 256, 0, st>>>(n4, (const floatx4*)X, (bf16x4*)planes,
+                                              (bf16x4*)(planes + (size_t)M * K));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.X = planes;
+  }
   a.W1 = (const __bf16*)W1;
   a.W2 = (const __bf16*)(W2 ? W2 : W1);
   a.Y = Y;
@@ -312,9 +293,9 @@ hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32
   a.splits = p.splits;
   dim3 grid(p.nblk, p.splits, p.mch);
   if (x_f32)
-    k_gemm<true><<<grid, GT, 0, st>>>(a);
+    k_gemm<2><<<grid, GT, 0, st>>>(a);
   else
-    k_gemm<false><<<grid, GT, 0, st>>>(a);
+    k_gemm<1><<<grid, GT, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t n4 = (size_t)M * N / 4;

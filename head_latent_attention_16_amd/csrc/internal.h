@@ -97,9 +97,10 @@ hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, co
 // bf16-weight linear layer Y[M,N] (fp32) = X[M,K] . W^T, X bf16 or fp32.
 // Rows n < N1 of W come from W1 (stride K), rows >= N1 from W2 (W2 == NULL:
 // all rows from W1).  Needs N % 32 == 0 and K % 256 == 0, and a workspace of
-// gemm_v3_workspace(M, N, K) bytes for the split partials (may be 0).
+// gemm_v3_workspace(M, N, K, x_f32) bytes for the split partials and, with
+// fp32 X, its bf16 hi / lo planes (may be 0).
 bool gemm_v3_supported(int M, int N, int K);
-size_t gemm_v3_workspace(int M, int N, int K);
+size_t gemm_v3_workspace(int M, int N, int K, bool x_f32);
 hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32, const void* W1,
                           const void* W2, float* Y, void* ws, hipStream_t st);
 // o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 in and out).
