@@ -468,7 +468,7 @@ def main():
                    "input_copies_rotated": copies,
                    "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name if name != "causal" else f"causal_nq{n_q}"),
                      "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn_paged" if paged
                                 else "mla_decode_attn_fp8" if fp8 else "mla_decode_attn")
                      + " (split attention with length scan + combine)",
