@@ -25,9 +25,9 @@
 // * k_prefill: flash attention per (sequence, head, 128 new tokens): four
 //   waves of 32 tokens; 64-key blocks of [K^C | k^R] (384 B per row) and V
 //   (256 B per row) are DMA'd into LDS one block ahead; S^T = K Q^T and
-//   O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T fragments by transpose
-//   reads), an online softmax in base 2 with the running max, the causal mask
-//   on the diagonal blocks.
+//   O^T += V^T P^T on v_mfma_f32_32x32x16_f16 (V^T fragments by transpose
+//   reads) in 32-key steps, an online softmax in base 2 with the running
+//   max, the causal mask on the diagonal blocks.
 #include <math.h>
 
 #include "common.h"

@@ -252,7 +252,7 @@ size_t mla_decode_attn_causal_workspace(const mla_dims_t* dims, int32_t B, int32
  * it is rotated at p) in dims->dtype; cache [cache_rows, d_c + d_r] with
  * sequence b at rows offsets[b] ..; W_UK [n_h, d_h, d_c], W_UV [n_h, d_v, d_c];
  * o [B, n_q, n_h, d_v] fp32; lse [B, n_q, n_h] fp32 or NULL.  Every cache row
- * 0 .. cache_rows - 1 is up-projected (into the workspace, bf16), so pass the
+ * 0 .. cache_rows - 1 is up-projected (into the workspace, fp16), so pass the
  * rows the batch occupies.  V3 dims in bf16 only (else MLA_ERR_SHAPE);
  * B <= 65535.  lens[b] must be in [n_q, offsets[b+1] - offsets[b]] with
  * offsets[b] + lens[b] <= cache_rows, else sequence b's outputs are NaN and
