@@ -10,21 +10,21 @@
 //   over a range of K; several K ranges ("splits") per column block give the
 //   chip enough independent streams, and a second kernel adds the split
 //   partials in a fixed order (deterministic).
-// * v_mfma_f32_32x32x16_bf16 with A = X (rows), B = W^T: both operands are
-//   "8 consecutive k per lane", so W fragments come straight from global
-//   memory into registers (64 contiguous bytes per lane per 64-wide k chunk,
-//   PD chunks in flight) and X fragments from LDS, read FPF MFMAs ahead.
-// * Within a 64-wide k chunk, lane half g holds k = 32 g + 8 j .. +8 for
-//   k-step j; A and B use the same order, so the dot products are unchanged.
+// * Both operands go through LDS: per 64-wide k chunk the workgroup's W tile
+//   (128 columns x 128 bytes) and X tile (128 rows x 128 bytes per plane) are
+//   copied straight from global memory into LDS stages with
+//   global_load_lds_dwordx4, eight lanes per 128-byte row, so every wave
+//   instruction covers whole 64-byte segments (a lane loading 16 bytes of
+//   its own W row would touch 64 segments per instruction and keep the
+//   address unit busy for four times as long).  Several chunks are in
+//   flight; completion is counted by hand with s_waitcnt vmcnt.
+// * v_mfma_f32_32x32x16_bf16 with A = X (rows), B = W^T: both fragments are
+//   "8 consecutive k per lane" reads from LDS; within a 64-wide k chunk, lane
+//   half g holds k = 32 g + 8 j .. +8 for k-step j, in both operands.
 // * fp32 X (an intermediate such as c^Q, or the attention output o) enters
 //   the bf16 MFMA as hi + lo with hi = bf16(x), lo = bf16(x - hi): two MFMAs
 //   per step, about 16 significant bits of x instead of 8.  The split is done
-//   once per call by k_hilo into two bf16 planes in the workspace, not by
-//   every column block that stages the same X.
-// * X is loaded in whole-row 16-byte pieces (every wave instruction reads
-//   full cache lines) and staged in LDS one chunk ahead.  The X and W loads
-//   of the chunk PD ahead and that staging are spread over the MFMA stream
-//   of the current chunk instead of stalling between chunks.
+//   once per call by k_hilo into two bf16 planes in the workspace.
 // * The K splits are chosen so that all workgroups run in one round on the
 //   256 compute units.
 #include "common.h"
@@ -40,10 +40,19 @@ constexpr int GMR = GMB * 32;     // rows per workgroup
 constexpr int GNW = 32;           // output columns per wave
 constexpr int GNT = 4 * GNW;      // columns per workgroup
 constexpr int KC = 64;            // k per chunk
-constexpr int XROWB = KC * 2;     // LDS bytes per row per chunk (bf16)
-constexpr int PD = 4;             // chunks of X and W in flight per wave
+constexpr int ROWB = KC * 2;      // LDS bytes per row (or column) per chunk (bf16)
+constexpr int TILEB = 128 * ROWB; // one operand tile per chunk: 16 KiB
+constexpr int KGROUP = 256;       // k granularity of the split plan
 constexpr int SLOTS = 256;        // workgroups per round (one per compute unit)
 constexpr int FPF = 8;            // A fragments read ahead
+
+// Stage = [W tile | X plane 0 (| X plane 1)]; NST stages in LDS.
+template <int NPL> struct GemmCfg {
+  static constexpr int PARTS = 1 + NPL;
+  static constexpr int STAGE = PARTS * TILEB;             // 32 or 48 KiB
+  static constexpr int NST = NPL == 2 ? 3 : 4;            // 144 or 128 KiB
+  static constexpr int DPW = PARTS * (TILEB / 1024) / 4;  // DMAs per wave per chunk: 8 or 12
+};
 
 struct GemmArgs {
   const __bf16* X;      // [NPL][M][K] bf16: X, or its hi and lo planes
@@ -52,15 +61,30 @@ struct GemmArgs {
   float* Y;             // [M][N] when splits == 1
   float* part;          // [splits][M][N] when splits > 1
   int M, N, N1, K;
-  int kper;             // k per split, a multiple of KC
+  int kper;             // k per split, a multiple of KGROUP
   int splits;
 };
 
-// X chunk rows are 128 bytes (8 chunks of 16 B) in LDS; the 16-byte chunk c
-// of row r is stored at c ^ ((r >> 1) & 7), which makes the 16-lane groups
-// of both the staging writes and the fragment reads hit 16 distinct bank
-// groups.
+// Tile rows are 128 bytes (8 chunks of 16 B) in LDS; the 16-byte chunk c of
+// row r is stored at c ^ ((r >> 1) & 7), which makes the 16-lane groups of
+// the fragment reads hit 16 distinct bank groups.
 __device__ __forceinline__ int xsw(int r) { return (r >> 1) & 7; }
+
+// Direct global -> LDS, 16 bytes per lane from a per-lane address (lane i's
+// bytes land at M0 + 16 i).  Issued from inline asm so that the compiler does
+// not add waits it cannot size; completion is counted by hand below.
+__device__ __forceinline__ void gdma_16B(uint32_t lds_addr, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void gwait_vm_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // hi = bf16(x), lo = bf16(x - hi) of fp32 X [n4 x 4], planes [2][n4 x 4]
 __global__ void __launch_bounds__(256) k_hilo(size_t n4, const floatx4* __restrict__ X, bf16x4* __restrict__ hi,
@@ -80,30 +104,49 @@ __global__ void __launch_bounds__(256) k_hilo(size_t n4, const floatx4* __restri
 
 template <int NPLANE>   // 1: bf16 X; 2: hi and lo planes of fp32 X
 __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char xs[2][NPLANE][GMR * XROWB];
+  using C = GemmCfg<NPLANE>;
+  constexpr int NST = C::NST, DPW = C::DPW, STAGE = C::STAGE;
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
 
   const int nb = blockIdx.x, sk = blockIdx.y, mc = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5, n32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = nb * GNT + wave * GNW;
-  const bool active = n0 < a.N;   // wave-uniform
+  const int nw = nb * GNT;        // the workgroup's first column
   const int m0 = mc * GMR;
   const int kb = sk * a.kper;
   const int ke = min(a.K, kb + a.kper);
-  const int nch = (ke - kb) / KC;
+  const int nch = (ke - kb) / KC;   // >= 1
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
-  // Waves past N (only in the last column block) stream row 0 and store nothing.
-  const int nrow = active ? n0 + n32 : 0;
-  const __bf16* wrow = (nrow < a.N1 ? a.W1 + (size_t)nrow * a.K
-                                    : a.W2 + (size_t)(nrow - a.N1) * a.K) + kb + 32 * g32;
-
-  // X staging, coalesced: load i of thread t covers 16 bytes at flat index
-  // f = 256 i + t of a plane's chunk, so each wave instruction reads whole
-  // rows: 8 per row (rows 32 i + t / 8), four per plane.
-  constexpr int XPR = 8;               // 16-byte pieces per row per chunk
-  const int xq = tid % XPR;            // this thread's piece within its row
-  const int xrb = tid / XPR;           // its row within each group of 256 pieces
-  constexpr int XRS = 256 / XPR;       // rows per load index
+  // DMA plan of one chunk: instruction q = DPW wave + k (0 .. 16 PARTS - 1)
+  // fills part q / 16 of the stage (0: W, 1 + p: X plane p); lane i writes
+  // the 16 bytes at 16 u, u = 64 (q % 16) + i, which hold logical chunk
+  // (u % 8) ^ xsw(r) of tile row r = u / 8.  Rows past M and columns past N
+  // read the last valid row (their results are not stored).
+  const char* src[DPW];
+#pragma unroll
+  for (int k = 0; k < DPW; ++k) {
+    const int q = wave * DPW + k;
+    const int part = q / 16;
+    const int u = 64 * (q % 16) + lane;
+    const int r = u >> 3;
+    const int c = (u & 7) ^ xsw(r);
+    if (part == 0) {
+      const int n = min(nw + r, a.N - 1);
+      const __bf16* row = n < a.N1 ? a.W1 + (size_t)n * a.K : a.W2 + (size_t)(n - a.N1) * a.K;
+      src[k] = (const char*)(row + kb + 8 * c);
+    } else {
+      const int m = min(m0 + r, a.M - 1);
+      src[k] = (const char*)(a.X + (size_t)(part - 1) * a.M * a.K + (size_t)m * a.K + kb + 8 * c);
+    }
+  }
+  // DMA k of chunk t into its stage; t past the end re-copies the last chunk
+  // into the free stage, so every chunk index issues exactly DPW DMAs and
+  // the wait count below is constant.
+  auto dma = [&](int k, int t) {
+    const int q = wave * DPW + k;
+    gdma_16B(lds0 + (uint32_t)((t % NST) * STAGE + q * 1024), src[k] + (size_t)min(t, nch - 1) * ROWB);
+  };
 
   floatx16 acc[GMB];
 #pragma unroll
@@ -111,95 +154,59 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
-  bf16x8 wf[PD][4];
-  auto load_w = [&](int slot, int c) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8*)(wrow + (size_t)c * KC + 8 * j);
-  };
-  // X staging registers, PD chunks deep: X(k) and W(k) are issued in the
-  // same chunk (X first), so waiting for X(c+1) before storing it to LDS
-  // never forces a newer W chunk to complete -- vmcnt completes in issue
-  // order.  Piece i = 4 p + i4 is row group i4 of plane p.
-  constexpr int XPIECES = 4 * NPLANE;       // 16-byte X loads per thread per chunk
-  bf16x8 xb[PD][XPIECES];
-  // Every global load in the main loop is unconditional (indices are clamped
-  // to valid data and rows past M are zeroed when stored to LDS), so that the
-  // compiler can count outstanding loads exactly.
-  const size_t plane = (size_t)a.M * a.K;
-  auto xrow_src = [&](int i) {
-    return (size_t)(i >> 2) * plane + (size_t)min(m0 + xrb + XRS * (i & 3), a.M - 1) * a.K + kb;
-  };
-  auto load_x_piece = [&](int slot, int c, int i) {
-    xb[slot][i] = *(const bf16x8*)(a.X + xrow_src(i) + (size_t)c * KC + 8 * xq);
-  };
-  auto store_x_piece = [&](int slot, int stage, int i) {
-    const int r = xrb + XRS * (i & 3);
-    const int off = r * XROWB + ((xq ^ xsw(r)) << 4);
-    *(bf16x8*)(xs[stage][i >> 2] + off) = m0 + r < a.M ? xb[slot][i] : bf16x8{};
-  };
-
-#pragma unroll
-  for (int s = 0; s < PD; ++s) {
-#pragma unroll
-    for (int i = 0; i < XPIECES; ++i) load_x_piece(s, min(s, nch - 1), i);
-    load_w(s, min(s, nch - 1));
-  }
-#pragma unroll
-  for (int i = 0; i < XPIECES; ++i) store_x_piece(0, 0, i);
-  __syncthreads();
-
-  // A-fragment LDS offsets for step j of block mb: row 32 mb + n32,
-  // logical chunk 4 g32 + j.
-  uint32_t aoff[GMB];
-#pragma unroll
-  for (int mb = 0; mb < GMB; ++mb) aoff[mb] = (uint32_t)((32 * mb + n32) * XROWB);
-  const int asw = xsw(n32);   // (32 mb + n32) >> 1 & 7 == n32 >> 1 & 7
+  // fragment offsets: A = X row 32 mb + n32, B = W column 32 wave + n32, both
+  // at logical chunk 4 g32 + j, stored at (4 g32 + j) ^ xsw(n32)
+  const int asw = xsw(n32);
+  const uint32_t arow = (uint32_t)(n32 * ROWB);
+  const uint32_t brow = (uint32_t)((GNW * wave + n32) * ROWB);
 
   constexpr int NF = 4 * NPLANE * GMB;      // MFMAs (= A fragments) per chunk
   constexpr int PER_J = NPLANE * GMB;       // MFMAs per W fragment
-  constexpr int ST0 = NF / 2 - XPIECES;     // first step of the X staging
-  // (steps ST0, ST0 + 2, ... stage X(c + 1); after the last chunk this
-  // rewrites the idle stage with data nobody reads)
 
-  // Chunk c: NF steps, each one MFMA and the A-fragment read FPF ahead; the
-  // loads of chunk c + PD (X pieces first, then each W fragment as soon as
-  // the MFMAs of chunk c are done with its register) and the staging of
-  // X(c + 1) into the other LDS stage ride along in the MFMA gaps.
-  // nch is a multiple of PD (K % (KC PD) == 0 and kper is a multiple of
-  // KC PD), so the unrolled body has no early exit.
-  for (int cb = 0; cb < nch; cb += PD) {
 #pragma unroll
-    for (int s = 0; s < PD; ++s) {
-      const int c = cb + s;
-      const int stage = s & 1;   // == c & 1: cb is a multiple of PD (even)
-      const int cn = min(c + PD, nch - 1);
+  for (int t = 0; t < NST - 1; ++t)
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) dma(k, t);
+
+  // Chunk c: every wave has finished chunk c - 1 and chunk c has landed
+  // (only chunks c + 1 .. c + NST - 2 may still be in flight); chunk
+  // c + NST - 1 goes into the stage of chunk c - 1, its DMAs spread over the
+  // MFMAs of chunk c.
+  for (int c0 = 0; c0 < nch; c0 += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int c = c0 + s;
+      if (c >= nch) break;
+      gwait_vm_then_barrier<(NST - 2) * DPW>();
+      const MLA_LDS char* st = (const MLA_LDS char*)lds + s * STAGE;
       auto frag_addr = [&](int f) {
         const int mb = f % GMB, pl = (f / GMB) % NPLANE, j = f / PER_J;
-        return xs[stage][pl] + aoff[mb] + (((4 * g32 + j) ^ asw) << 4);
+        return st + (1 + pl) * TILEB + mb * 32 * ROWB + arow + (((4 * g32 + j) ^ asw) << 4);
       };
+      bf16x8 wf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = *(const MLA_LDS bf16x8*)(st + brow + (((4 * g32 + j) ^ asw) << 4));
       bf16x8 fr[FPF];
 #pragma unroll
-      for (int f = 0; f < FPF; ++f) fr[f] = *(const bf16x8*)frag_addr(f);
+      for (int f = 0; f < FPF; ++f) fr[f] = *(const MLA_LDS bf16x8*)frag_addr(f);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int mb = f % GMB, j = f / PER_J;
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % FPF], wf[s][j], acc[mb], 0, 0, 0);
-        if (f + FPF < NF) fr[f % FPF] = *(const bf16x8*)frag_addr(f + FPF);
-        if (f < XPIECES) load_x_piece(s, cn, f);
-        if (f % PER_J == PER_J - 1 && j < 3)   // W fragment j of chunk c is done
-          wf[s][j] = *(const bf16x8*)(wrow + (size_t)cn * KC + 8 * j);
-        if (f >= ST0 && f < ST0 + 2 * XPIECES && (f - ST0) % 2 == 0)
-          store_x_piece((s + 1) % PD, stage ^ 1, (f - ST0) / 2);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % FPF], wf[j], acc[mb], 0, 0, 0);
+        if (f + FPF < NF) fr[f % FPF] = *(const MLA_LDS bf16x8*)frag_addr(f + FPF);
+#pragma unroll
+        for (int k = 0; k < DPW; ++k)
+          if (f == (k * NF) / DPW) dma(k, c + NST - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wf[s][3] = *(const bf16x8*)(wrow + (size_t)cn * KC + 24);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the last DMAs (past the end) must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (!active) return;
+  const int n0 = nw + GNW * wave;
+  if (n0 >= a.N) return;   // wave-uniform
   // D layout: lane holds column n0 + n32, rows 32 mb + 8 (e/4) + 4 g32 + e%4.
   float* out = a.splits == 1 ? a.Y : a.part + (size_t)sk * a.M * a.N;
 #pragma unroll
@@ -235,14 +242,14 @@ Plan plan(int M, int N, int K) {
   Plan p;
   p.nblk = (N + GNT - 1) / GNT;
   p.mch = (M + GMR - 1) / GMR;
-  const int kgr = K / (KC * PD);   // groups of PD chunks
+  const int kgr = K / KGROUP;   // groups of k
   int splits = SLOTS / (p.nblk * p.mch);   // one round of workgroups
   int cap = kgr / 2;   // every split streams at least 2 groups (512 k)
   if (cap < 1) cap = 1;
   if (splits > cap) splits = cap;
   if (splits < 1) splits = 1;
   const int per = (kgr + splits - 1) / splits;
-  p.kper = per * KC * PD;
+  p.kper = per * KGROUP;
   p.splits = (kgr + per - 1) / per;
   return p;
 }
@@ -250,7 +257,7 @@ Plan plan(int M, int N, int K) {
 }  // namespace
 
 bool gemm_v3_supported(int M, int N, int K) {
-  return M >= 1 && N >= 32 && N % 32 == 0 && K >= KC * PD && K % (KC * PD) == 0;
+  return M >= 1 && N >= 32 && N % 32 == 0 && K >= KGROUP && K % KGROUP == 0;
 }
 
 // Workspace: the split partials [splits][M][N] fp32 (when splits > 1), then
