@@ -44,6 +44,7 @@ constexpr int CROWB = (PD_C + PD_R) * 2;  // 1152 cache row bytes
 
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx4v __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ const char* uni_ptr(const char* p) {
@@ -360,27 +361,33 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
         const halfx8 kf = *(const MLA_LDS halfx8*)(Ks + kr * F_KROWB + ((c ^ ksw(kr)) << 4));
         S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[kk], S, 0, 0, 0);
       }
-      // scores in log2 units, -inf where masked; key of S[e] is
-      // 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4
-      float bmax = -INFINITY;
+      // key of S[e] is 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4.  Off the
+      // diagonal (every key of this half at or before the workgroup's first
+      // token) nothing is masked; on it, masked scores become -inf.  The max
+      // is taken on the raw scores (the scale is positive) and the scale is
+      // folded into the exponent's fma.
+      const int kbase = kb * F_KB + 32 * t;
+      if (kbase + 31 > p_first) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb * F_KB + 32 * t + 8 * (e >> 2) + 4 * g + (e & 3);
-        const bool ok = key <= pos && key < len;
-        S[e] = ok ? S[e] * a.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, S[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = kbase + 8 * (e >> 2) + 4 * g + (e & 3);
+          S[e] = (key <= pos && key < len) ? S[e] : -INFINITY;
+        }
       }
-      // the token's max over both lane halves
+      float bmax = fmaxf(S[0], S[1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) bmax = fmaxf(bmax, fmaxf(S[e], S[e + 1]));
+      // the token's max over both lane halves, in log2 units
       {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
       }
-      const float m_new = fmaxf(m_run, bmax);
-      // rescale what was accumulated when the max moved (a token whose half
-      // is fully masked keeps m_new = m_run; every token sees key 0 first)
+      // every token sees key 0 in the first half-block, so m_new is finite
+      const float m_new = fmaxf(m_run, bmax * a.scale_log2);
+      // rescale what was accumulated when the max moved
       if (__any(m_new > m_run)) {
-        const float al = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        const float al = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf: 0
         l_run *= al;
 #pragma unroll
         for (int cb = 0; cb < PD_V / 32; ++cb)
@@ -388,14 +395,17 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
           for (int e = 0; e < 16; ++e) O[cb][e] *= al;
       }
       m_run = m_new;
-      // weights as the PV operand: P[kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3}
+      // weights as the PV operand: P[kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3};
+      // l sums the same fp16 weights, two per dot instruction
       halfx8 P[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = m_new == -INFINITY ? 0.f : exp2f(S[e] - m_new);
-        const _Float16 ph = (_Float16)p;
-        P[e >> 3][e & 7] = ph;
-        l_run += (float)ph;
+      for (int e = 0; e < 16; ++e)
+        P[e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(S[e], a.scale_log2, -m_new));
+      const halfx2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const halfx2 pr = {P[e >> 3][e & 7], P[e >> 3][(e & 7) + 1]};
+        l_run = __builtin_amdgcn_fdot2(pr, one2, l_run, false);
       }
       // O^T[value cols x tokens] += V^T . P^T, four 32-column blocks
 #pragma unroll
