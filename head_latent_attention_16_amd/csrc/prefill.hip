@@ -17,7 +17,8 @@
 // the explicit keys, values and queries must lie within the fp16 range.
 //
 // Kernels (gfx950, wave64, MFMA with fp32 accumulation):
-// * k_q_rope: q^R rotated at each token's position (fp64 angle), q -> fp16.
+// * k_rope_table: cos and sin of each new token's rotation angles (fp64
+//   angle); k_prefill rotates q^R with them as it loads the query (fp16).
 // * k_upproj: KV[r, h] = [W^UK[h] c_r | W^UV[h] c_r] (fp16) for every cache
 //   row r, a bf16 [rows x 512] . [512 x n_h 256] GEMM; a workgroup owns one head's 256
 //   output columns for 128 rows, the 512-deep reduction in 64-wide chunks
@@ -71,36 +72,23 @@ __device__ __forceinline__ void vm_wait_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// q^R rotation: q_rot[t, h] = [q^C | RoPE(q^R, pos_t)] in fp16, pos_t the
-// token's row.  One block per token: the 32 rotation angles of the token are
-// formed once (fp64) and shared by its 128 heads; then 256 threads cover the
-// 128 heads x 96 value pairs.
+// Rotation angles of the new tokens: table[t][i] = (cos, sin)(pos_t theta_i),
+// pos_t the token's row, i < d_R / 2 (fp64 angle, see rope_cos_sin).  The
+// attention kernel rotates each token's q^R with them as it loads the query,
+// so the 128 heads of a token share one angle computation and no rotated
+// copy of the queries is written.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_q_rope(int n_q, double base, const __bf16* __restrict__ q,
-                                                const int32_t* __restrict__ lens, _Float16* __restrict__ q_rot) {
-  __shared__ float s_cos[PD_R / 2], s_sin[PD_R / 2];
-  const int64_t t = blockIdx.x;   // token
-  const int b = (int)(t / n_q), i = (int)(t - (int64_t)b * n_q);
-  if (threadIdx.x < PD_R / 2) {
-    const int64_t pos = (int64_t)lens[b] - n_q + i;
-    rope_cos_sin(pos < 0 ? 0 : pos, threadIdx.x, PD_R, base, &s_cos[threadIdx.x], &s_sin[threadIdx.x]);
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < PN_H * (PQK / 2); idx += 256) {
-    const int h = idx / (PQK / 2), k = idx - h * (PQK / 2);   // k < 96
-    const __bf16* src = q + (t * PN_H + h) * PQK;
-    _Float16* dst = q_rot + (t * PN_H + h) * PQK;
-    if (k < PD_H / 2) {   // content: two values per thread
-      dst[2 * k] = (_Float16)(float)src[2 * k];
-      dst[2 * k + 1] = (_Float16)(float)src[2 * k + 1];
-    } else {              // rope pair j of 32
-      const int j = k - PD_H / 2;
-      const float cs = s_cos[j], sn = s_sin[j];
-      const float lo = (float)src[PD_H + j], hi = (float)src[PD_H + PD_R / 2 + j];
-      dst[PD_H + j] = (_Float16)(lo * cs - hi * sn);
-      dst[PD_H + PD_R / 2 + j] = (_Float16)(hi * cs + lo * sn);
-    }
-  }
+__global__ void __launch_bounds__(256) k_rope_table(int64_t ntok, int n_q, double base,
+                                                    const int32_t* __restrict__ lens, float2* __restrict__ table) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= ntok * (PD_R / 2)) return;
+  const int64_t t = idx / (PD_R / 2);
+  const int i = (int)(idx - t * (PD_R / 2));
+  const int b = (int)(t / n_q), k = (int)(t - (int64_t)b * n_q);
+  const int64_t pos = (int64_t)lens[b] - n_q + k;
+  float c, sn;
+  rope_cos_sin(pos < 0 ? 0 : pos, i, PD_R, base, &c, &sn);
+  table[idx] = make_float2(c, sn);
 }
 
 // k^R in fp16: kr[r] = cache[r, d_c ..] (one thread per value).
@@ -243,7 +231,8 @@ __device__ __forceinline__ int ksw(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int vsw(int r) { return 4 * (r & 3); }
 
 struct PrefillArgs {
-  const _Float16* q_rot;   // [B, n_q, n_h, 192]
+  const __bf16* q;          // [B, n_q, n_h, 192] (q^R not rotated)
+  const float2* rope;       // [B n_q, 32] (cos, sin) of each token
   const _Float16* kr;      // [rows, 64]
   const _Float16* kv;      // [rows, n_h, 256]
   const int32_t* offsets;
@@ -288,12 +277,33 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
   const int pos = len - a.n_q + min(tok, a.n_q - 1);   // this lane's token position
   const int nblk = (p_last + 1 + F_KB - 1) / F_KB;     // key blocks any token sees
 
-  // Q^T fragments (B operand): token n32 of this wave, features 16 kk + 8 g.
+  // Q^T fragments (B operand): token n32 of this wave, features 16 kk + 8 g,
+  // in fp16.  Rope feature r = 16 (kk - 8) + 8 g + j pairs with r + 32: the
+  // lane holds both (kk = 8 with 10, 9 with 11) and rotates them with the
+  // angle of frequency r (rotate-half).
   halfx8 q[PQK / 16];
   {
-    const _Float16* qr = a.q_rot + (((size_t)b * a.n_q + min(tok, a.n_q - 1)) * PN_H + h) * PQK;
+    const size_t t = (size_t)b * a.n_q + min(tok, a.n_q - 1);
+    const __bf16* qr = a.q + (t * PN_H + h) * PQK;
+    bf16x8 raw[PQK / 16];
 #pragma unroll
-    for (int kk = 0; kk < PQK / 16; ++kk) q[kk] = *(const halfx8*)(qr + 16 * kk + 8 * g);
+    for (int kk = 0; kk < PQK / 16; ++kk) raw[kk] = *(const bf16x8*)(qr + 16 * kk + 8 * g);
+#pragma unroll
+    for (int kk = 0; kk < PD_H / 16; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[kk][j] = (_Float16)(float)raw[kk][j];
+    const float2* rt = a.rope + t * (PD_R / 2);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {          // kk = 8 + hh pairs with 10 + hh
+      const int kl = PD_H / 16 + hh, khi = kl + 2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 cs = rt[16 * hh + 8 * g + j];
+        const float lo = (float)raw[kl][j], hi = (float)raw[khi][j];
+        q[kl][j] = (_Float16)(lo * cs.x - hi * cs.y);
+        q[khi][j] = (_Float16)(hi * cs.x + lo * cs.y);
+      }
+    }
   }
 
   const char* kvb = (const char*)(a.kv + (size_t)h * KVW);     // row r at kvb + r * n_h * 512
@@ -453,11 +463,11 @@ bool prefill_v3_supported(const Shape& s) {
 }
 
 // workspace: explicit keys and values [rows, n_h, 256] fp16, k^R [rows, 64]
-// fp16, rotated queries [B, n_q, n_h, 192] fp16 (each 256-byte aligned)
+// fp16, rotation table [B n_q, 32] (cos, sin) (each 256-byte aligned)
 size_t prefill_v3_workspace(int B, int n_q, int64_t rows) {
   const size_t kv = (size_t)rows * PN_H * KVW * 2;
   const size_t kr = (size_t)rows * PD_R * 2;
-  const size_t qr = (size_t)B * n_q * PN_H * PQK * 2;
+  const size_t qr = (size_t)B * n_q * (PD_R / 2) * sizeof(float2);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al(kv) + al(kr) + al(qr);
 }
@@ -468,8 +478,9 @@ hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, cons
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   _Float16* kv = (_Float16*)ws;
   _Float16* kr = (_Float16*)((char*)ws + al((size_t)rows * PN_H * KVW * 2));
-  _Float16* q_rot = (_Float16*)((char*)kr + al((size_t)rows * PD_R * 2));
-  k_q_rope<<<(unsigned)((int64_t)B * n_q), 256, 0, st>>>(n_q, s.rope_base, (const __bf16*)q, lens, q_rot);
+  float2* rope = (float2*)((char*)kr + al((size_t)rows * PD_R * 2));
+  const int64_t ntok = (int64_t)B * n_q;
+  k_rope_table<<<(unsigned)((ntok * (PD_R / 2) + 255) / 256), 256, 0, st>>>(ntok, n_q, s.rope_base, lens, rope);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_kr_f16<<<(unsigned)((rows * PD_R + 255) / 256), 256, 0, st>>>(rows, (const __bf16*)cache, kr);
@@ -480,7 +491,8 @@ hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, cons
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillArgs a;
-  a.q_rot = q_rot;
+  a.q = (const __bf16*)q;
+  a.rope = rope;
   a.kr = kr;
   a.kv = kv;
   a.offsets = offsets;

@@ -214,6 +214,7 @@ def test_prefill_validation(lib):
     assert call(d, 1, 4, 100, 10) == 4                                # workspace too small
     need = lib.mla_prefill_attn_workspace(ctypes.byref(d), 2, 8, 100)
     al = lambda x: (x + 255) // 256 * 256
-    assert need == al(100 * 128 * 256 * 2) + al(100 * 64 * 2) + al(2 * 8 * 128 * 192 * 2)
+    # explicit keys and values (fp16), k^R (fp16), each token's 32 rotation (cos, sin) pairs
+    assert need == al(100 * 128 * 256 * 2) + al(100 * 64 * 2) + al(2 * 8 * 32 * 8)
     assert lib.mla_prefill_attn(ctypes.byref(d), 1, 4, None, one, 100, one, one, one, one, one, None, None, one,
                                 1 << 40, None) == 1
