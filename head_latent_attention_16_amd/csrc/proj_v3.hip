@@ -200,29 +200,29 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
 // ---------------------------------------------------------------------------
 // uv: one workgroup per (head, 32-row block of W_UV); it keeps its 32 x 512
 // weight block in registers and walks the batch in blocks of 32.  The four
-// waves split the 512-long contraction and add their partial sums through LDS.
+// waves split the 512-long contraction (wave w: columns 128 w .. +128) and
+// add their partial sums through LDS.
 //   o^T[v x batch] = W_UV[h][v x c] . o_lat^T[c x batch]   (32x32x16)
 // o_lat is fp32; it enters the bf16 product as hi + lo with hi = bf16(x) and
 // lo = bf16(x - hi), two MFMAs per step, so the result keeps about 16
 // significant bits of o_lat instead of the 8 a single bf16 rounding leaves.
+// Each wave loads its 128 columns of the block's 32 o_lat rows with whole
+// 512-byte row pieces (two rows per wave instruction), splits them into hi
+// and lo planes in its own LDS region, and reads the MFMA fragments from
+// there; the next block's loads are in flight during the current block's
+// MFMAs.  Plane rows are 256 bytes, 16-byte chunk c of row r stored at
+// c ^ (r % 16), so 16 rows at one chunk hit 16 distinct bank groups.
 // ---------------------------------------------------------------------------
 constexpr int UV_KS = DC / 16 / 4;   // 8 k-steps per wave
-
-__device__ __forceinline__ void split_bf16(const floatx4& x0, const floatx4& x1, bf16x8& hi,
-                                           bf16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = (__bf16)x0[i];
-    hi[4 + i] = (__bf16)x1[i];
-    lo[i] = (__bf16)(x0[i] - (float)hi[i]);
-    lo[4 + i] = (__bf16)(x1[i] - (float)hi[4 + i]);
-  }
-}
+constexpr int UV_COLS = DC / 4;      // 128 columns per wave
+constexpr int UV_ROWB = UV_COLS * 2; // 256 bytes per plane row
+constexpr int UV_PLANE = 32 * UV_ROWB;   // 8 KiB
 
 __global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ o_lat,
                                                const __bf16* __restrict__ W_UV,
                                                float* __restrict__ o) {
   __shared__ floatx16 red[3][64];
+  __shared__ __attribute__((aligned(16))) char xs[4][2][UV_PLANE];   // [wave][hi, lo]
   const int h = blockIdx.x, vb = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g32 = lane >> 5;
   const int v = 32 * vb + (lane & 31);
@@ -231,21 +231,50 @@ __global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ 
 #pragma unroll
   for (int j = 0; j < UV_KS; ++j) aw[j] = *(const bf16x8*)(wrow + 16 * (wave * UV_KS + j) + 8 * g32);
 
+  // load i of a block: row 2 i + g32 of the block, columns 128 wave + 4 q .. +4
+  const int q = lane & 31;
+  floatx4 xl[16];
+  auto load_block = [&](int nb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bq = 32 * nb + 2 * i + g32;
+      xl[i] = bq < B ? *(const floatx4*)(o_lat + ((size_t)bq * NH + h) * DC + UV_COLS * wave + 4 * q)
+                     : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  MLA_LDS char* hp = (MLA_LDS char*)xs[wave][0];
+  MLA_LDS char* lp = (MLA_LDS char*)xs[wave][1];
+  auto stage_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + g32;
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)xl[i][e];
+        lo[e] = (__bf16)(xl[i][e] - (float)hi[e]);
+      }
+      // columns 4 q .. +4: 16-byte chunk q / 2, half q % 2
+      const int off = r * UV_ROWB + ((((q >> 1) ^ (r & 15)) << 4) | ((q & 1) << 3));
+      *(MLA_LDS bf16x4*)(hp + off) = hi;
+      *(MLA_LDS bf16x4*)(lp + off) = lo;
+    }
+  };
+  load_block(0);
+  const int br = lane & 31;   // B-fragment row (batch row of the block)
   for (int nb = 0; nb * 32 < B; ++nb) {
-    const int bq = 32 * nb + (lane & 31);
-    const bool bok = bq < B;
-    const float* orow = o_lat + ((size_t)(bok ? bq : 0) * NH + h) * DC;
+    stage_block();   // the wave's own region: its previous fragment reads came first
+    if ((nb + 1) * 32 < B) load_block(nb + 1);
+    const int bq = 32 * nb + br;
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < UV_KS; ++j) {
-      const int c = 16 * (wave * UV_KS + j) + 8 * g32;
-      floatx4 x0 = *(const floatx4*)(orow + c);
-      floatx4 x1 = *(const floatx4*)(orow + c + 4);
-      if (!bok) x0 = x1 = floatx4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 hi, lo;
-      split_bf16(x0, x1, hi, lo);
+      // k = 16 j + 8 g32 .. +8 of the wave's columns: chunk 2 j + g32
+      const int off = br * UV_ROWB + (((2 * j + g32) ^ (br & 15)) << 4);
+      const bf16x8 hi = *(const MLA_LDS bf16x8*)(hp + off);
+      const bf16x8 lo = *(const MLA_LDS bf16x8*)(lp + off);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], lo, acc, 0, 0, 0);
     }
@@ -259,7 +288,7 @@ __global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ 
         for (int i = 0; i < 16; ++i) acc[i] += r[i];
       }
       // lane: batch bq, rows v = 32 vb + 8 (i/4) + 4 g32 + i%4
-      if (bok) {
+      if (bq < B) {
         float* dst = o + ((size_t)bq * NH + h) * DV + 32 * vb + 4 * g32;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
