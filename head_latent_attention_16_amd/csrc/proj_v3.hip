@@ -60,9 +60,9 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
                                                            __bf16* __restrict__ q_lat,
                                                            __bf16* __restrict__ q_pe) {
   __shared__ __attribute__((aligned(16))) char w[DH * ABS_ROWB];
-  // fp32 query: one batch block's q_C of this head as bf16 hi and lo planes,
-  // split once per workgroup instead of once per wave
-  __shared__ __attribute__((aligned(16))) char qs[QF32 ? 2 : 1][QF32 ? 32 * ABS_QROWB : 16];
+  // one batch block's q_C of this head, staged once per workgroup (fp32
+  // query: as bf16 hi and lo planes)
+  __shared__ __attribute__((aligned(16))) char qs[QF32 ? 2 : 1][32 * ABS_QROWB];
   const int h = blockIdx.x, qt = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g32 = lane >> 5;
 
@@ -75,12 +75,12 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
     wv[j] = *(const floatx4*)(src + (size_t)r * DC + c * 8);
   }
 
-  // B operand: q_C[bq][h][16 ks + 8 g32 .. +8] (and its low part)
-  bf16x8 qb[DH / 16];
-  // fp32: the batch block's 32 x 128 query values, 16 per thread, read here
-  // and split into the LDS planes by stage_q (after the previous block's
-  // fragment reads); bf16: the B fragments straight into registers.
+  // The batch block's 32 x 128 query values are read with whole-row pieces
+  // (fp32: 16 per thread; bf16: 16 per thread as two 16-byte pieces) and
+  // written to LDS by stage_q (fp32 split into the hi and lo planes), where
+  // every wave reads its B fragments.
   floatx4 qf[QF32 ? 4 : 1];
+  bf16x8 qh[QF32 ? 1 : 2];
   auto load_q = [&](int nb) {
     if constexpr (QF32) {
 #pragma unroll
@@ -91,27 +91,34 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
                        : floatx4{0.f, 0.f, 0.f, 0.f};
       }
     } else {
-      const int bq = nb * 32 + (lane & 31);
-      const bool bok = bq < B;
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        const size_t e0 = ((size_t)(bok ? bq : 0) * NH + h) * QW + 16 * ks + 8 * g32;
-        qb[ks] = bok ? *(const bf16x8*)((const __bf16*)qv + e0) : bf16x8{};
+      for (int u = 0; u < 2; ++u) {
+        const int idx = u * ABS_THREADS + tid, r = idx >> 4, c8 = idx & 15;   // row, 8-value piece
+        const int bq = nb * 32 + r;
+        qh[u] = bq < B ? *(const bf16x8*)((const __bf16*)qv + ((size_t)bq * NH + h) * QW + 8 * c8) : bf16x8{};
       }
     }
   };
   auto stage_q = [&]() {
+    if constexpr (QF32) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = u * ABS_THREADS + tid, r = idx >> 5, c4 = idx & 31;
-      bf16x4 hi, lo;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = u * ABS_THREADS + tid, r = idx >> 5, c4 = idx & 31;
+        bf16x4 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)qf[u][e];
-        lo[e] = (__bf16)(qf[u][e] - (float)hi[e]);
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (__bf16)qf[u][e];
+          lo[e] = (__bf16)(qf[u][e] - (float)hi[e]);
+        }
+        *(bf16x4*)(qs[0] + r * ABS_QROWB + 8 * c4) = hi;
+        *(bf16x4*)(qs[QF32 ? 1 : 0] + r * ABS_QROWB + 8 * c4) = lo;
       }
-      *(bf16x4*)(qs[0] + r * ABS_QROWB + 8 * c4) = hi;
-      *(bf16x4*)(qs[QF32 ? 1 : 0] + r * ABS_QROWB + 8 * c4) = lo;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = u * ABS_THREADS + tid, r = idx >> 4, c8 = idx & 15;
+        *(bf16x8*)(qs[0] + r * ABS_QROWB + 16 * c8) = qh[u];
+      }
     }
   };
   load_q(0);
@@ -143,7 +150,7 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
     const int idx = j * ABS_THREADS + tid, r = idx >> 4, c = idx & 15;
     *(floatx4*)(w + r * ABS_ROWB + c * 16) = wv[j];
   }
-  if constexpr (QF32) stage_q();
+  stage_q();
   __syncthreads();
 
   // Transpose-read addressing (see the decode kernel): in 16-lane group G,
@@ -154,14 +161,8 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
   const uint32_t tr_off = (uint32_t)((i16 >> 2) * ABS_ROWB + 32 * h16 + 8 * (i16 & 3));
 
   for (int nb = 0; nb * 32 < B; ++nb) {
-    if (nb > 0) {
-      load_q(nb);
-      if constexpr (QF32) {
-        __syncthreads();   // every wave is done with the previous block's planes
-        stage_q();
-        __syncthreads();
-      }
-    }
+    const bool more = (nb + 1) * 32 < B;
+    if (more) load_q(nb + 1);   // in flight during this block's MFMAs
     const int bq = nb * 32 + (lane & 31);
     floatx16 acc;
 #pragma unroll
@@ -173,15 +174,13 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
       const bf16x4 hi =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(MLA_LDS char*)(p + 4 * ABS_ROWB));
       const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      // B fragment: batch row lane & 31, k = 16 ks + 8 g32 .. +8 (from both planes)
+      const int off = (lane & 31) * ABS_QROWB + (16 * ks + 8 * g32) * 2;
+      const bf16x8 bh = *(const bf16x8*)(qs[0] + off);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
       if constexpr (QF32) {
-        // B fragment: batch row lane & 31, k = 16 ks + 8 g32 .. +8, from both planes
-        const int off = (lane & 31) * ABS_QROWB + (16 * ks + 8 * g32) * 2;
-        const bf16x8 bh = *(const bf16x8*)(qs[0] + off);
         const bf16x8 bl = *(const bf16x8*)(qs[1] + off);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
       }
     }
     // lane: batch bq, columns 8 (i/4) + 4 g32 + i%4 of the block
@@ -193,6 +192,11 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
                           (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
         *(bf16x4*)(dst + 8 * q4) = v;
       }
+    }
+    if (more) {
+      __syncthreads();   // every wave is done with this block's fragments
+      stage_q();
+      __syncthreads();
     }
   }
 }
