@@ -1946,9 +1946,10 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   c.G = G;
   c.scale_log2 = a.scale_log2;
   // about G / B pieces per sequence: fewer pieces, more column blocks per
-  // workgroup (CPW * pieces loads in flight per lane)
+  // workgroup (CPW * pieces loads in flight per lane).  Measured: ragged
+  // B=64 (G/B = 4) best at CPW 8, uniform B=16 (16) at 2, long B=8 (32) at 1.
   int cpw = 1;
-  while (cpw < CMB_NCB && cpw * G < 8 * B) cpw *= 2;
+  while (cpw < CMB_NCB && cpw * G < 32 * B) cpw *= 2;
   c.cpw = cpw;
   k_combine<<<dim3((NH / CMB_HB) * (CMB_NCB / cpw), B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();
