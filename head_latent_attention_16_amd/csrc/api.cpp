@@ -71,32 +71,41 @@ bool force_generic() { return env_flag("MLA_FORCE_GENERIC"); }
 
 // Linear layers: the MFMA kernel for bf16 weights when the sizes suit it,
 // the generic kernel otherwise.  Both paths of a call site are chosen by the
-// same predicate in the workspace query and in the call.
+// same predicate in the workspace query and in the call.  The MFMA kernel
+// takes bf16 activations: an intermediate that feeds it (c^Q, o) is rounded
+// to bf16 once by the kernel that produces it, as in bf16 inference; the
+// generic kernel keeps fp32 intermediates.
 bool fast_linear(const Shape& s, int M, int N, int K) {
   return !force_generic() && s.bf16 && gemm_v3_supported(M, N, K);
 }
-size_t linear_ws(const Shape& s, int M, int N, int K, bool x_f32) {
-  return fast_linear(s, M, N, K) ? gemm_v3_workspace(M, N, K, x_f32) : 0;
+size_t linear_ws(const Shape& s, int M, int N, int K) {
+  return fast_linear(s, M, N, K) ? gemm_v3_workspace(M, N, K) : 0;
 }
+// Y = X W^T in fp32, X in the storage type (the caller has checked which
+// path runs when X is an fp32 intermediate).
 hipError_t linear(const Shape& s, int M, int N, int K, const void* X, bool x_f32, const void* W,
                   float* Y, void* part, hipStream_t st) {
-  if (fast_linear(s, M, N, K)) return launch_gemm_v3(M, N, N, K, X, x_f32, W, nullptr, Y, part, st);
+  if (fast_linear(s, M, N, K)) return launch_gemm_v3(M, N, N, K, X, W, nullptr, Y, nullptr, part, st);
   return launch_linear_generic(s, M, N, K, X, x_f32, W, Y, st);
 }
 
 // Workspace layouts (byte offsets, each region 256-aligned).
+// absorb from h_t: [c^Q fp32 | c^Q bf16 (fast W^UQ) | q (fp32; bf16 from the
+// fast W^UQ) | split partials of the linear layers]
 size_t absorb_ws(const Shape& s, int B, bool from_hidden) {
   if (!from_hidden) return 0;
   const int qw = s.n_h * (s.d_h + s.d_r);
+  const int kq = s.d_q > 0 ? s.d_q : s.d_model;
+  const bool uq_fast = fast_linear(s, B, qw, kq);
   size_t cq = s.d_q > 0 ? align256((size_t)B * s.d_q * sizeof(float)) : 0;
-  size_t q = align256((size_t)B * qw * sizeof(float));
-  // W^UQ reads the fp32 c^Q (or h_t directly), W^DQ reads h_t
-  size_t part = linear_ws(s, B, qw, s.d_q > 0 ? s.d_q : s.d_model, s.d_q > 0 || !s.bf16);
+  size_t cqb = s.d_q > 0 && uq_fast ? align256((size_t)B * s.d_q * sizeof(uint16_t)) : 0;
+  size_t q = align256((size_t)B * qw * (uq_fast ? sizeof(uint16_t) : sizeof(float)));
+  size_t part = linear_ws(s, B, qw, kq);
   if (s.d_q > 0) {
-    const size_t p1 = linear_ws(s, B, s.d_q, s.d_model, !s.bf16);
+    const size_t p1 = linear_ws(s, B, s.d_q, s.d_model);
     if (p1 > part) part = p1;
   }
-  return cq + q + align256(part);
+  return cq + cqb + q + align256(part);
 }
 // Fused rope+latent key projection: one linear layer of d_c + d_r outputs
 // whose rows come from W_DKV then W_KR.
@@ -106,18 +115,22 @@ size_t append_ws(const Shape& s, int B, int n_new, bool from_hidden) {
   const int M = B * n_new;
   size_t part = 0;
   if (fused_kv(s, M)) {
-    part = gemm_v3_workspace(M, s.d_c + s.d_r, s.d_model, false);
+    part = gemm_v3_workspace(M, s.d_c + s.d_r, s.d_model);
   } else {
-    part = linear_ws(s, M, s.d_c, s.d_model, !s.bf16);
-    const size_t p2 = linear_ws(s, M, s.d_r, s.d_model, !s.bf16);
+    part = linear_ws(s, M, s.d_c, s.d_model);
+    const size_t p2 = linear_ws(s, M, s.d_r, s.d_model);
     if (p2 > part) part = p2;
   }
   return align256((size_t)M * (s.d_c + s.d_r) * sizeof(float)) + align256(part);
 }
+// project_out with u: [o fp32 (when o is not given) | o bf16 (fast W^O) |
+// split partials of W^O]
 size_t project_ws(const Shape& s, int B, bool with_u) {
   if (!with_u) return 0;
-  return align256((size_t)B * s.n_h * s.d_v * sizeof(float)) +
-         align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v, true));
+  const size_t n = (size_t)B * s.n_h * s.d_v;
+  const bool o_fast = fast_linear(s, B, s.d_model, s.n_h * s.d_v);
+  return align256(n * sizeof(float)) + (o_fast ? align256(n * sizeof(uint16_t)) : 0) +
+         align256(linear_ws(s, B, s.d_model, s.n_h * s.d_v));
 }
 // Query tokens per call (B n_q): the combine and generic decode grids index
 // them in their second dimension.
@@ -313,30 +326,40 @@ mla_status_t absorb_common(const mla_dims_t* dims, int32_t B, const void* h_t, c
   const void* qsrc = q;
   bool q_f32 = storage_f32;
   if (from_hidden) {
-    // [c^Q (fp32) | q (fp32) | split partials of the linear layers]
+    // regions as absorb_ws
     char* w = (char*)ws;
     const int qw = s.n_h * (s.d_h + s.d_r);
-    const void* x = h_t;
-    bool x_f32 = storage_f32;
-    int K = s.d_model;
+    const int kq = s.d_q > 0 ? s.d_q : s.d_model;
+    const bool uq_fast = fast_linear(s, B, qw, kq);
     float* cq = (float*)w;
     if (s.d_q > 0) w += align256((size_t)B * s.d_q * sizeof(float));
-    float* qf = (float*)w;
-    w += align256((size_t)B * qw * sizeof(float));
+    void* cqb = w;
+    if (s.d_q > 0 && uq_fast) w += align256((size_t)B * s.d_q * sizeof(uint16_t));
+    void* qbuf = w;
+    w += align256((size_t)B * qw * (uq_fast ? sizeof(uint16_t) : sizeof(float)));
     void* part = w;
+    const void* x = h_t;   // the input of W^UQ
+    bool x_f32 = storage_f32;
     if (s.d_q > 0) {
-      hipError_t e = linear(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, part, hs);
+      hipError_t e;
+      if (uq_fast && !q_norm_w && fast_linear(s, B, s.d_q, s.d_model)) {
+        e = launch_gemm_v3(B, s.d_q, s.d_q, s.d_model, h_t, W_DQ, nullptr, nullptr, cqb, part, hs);
+      } else {
+        e = linear(s, B, s.d_q, s.d_model, h_t, storage_f32, W_DQ, cq, part, hs);
+        if (e == hipSuccess && q_norm_w)
+          e = launch_rmsnorm(s, cq, B, s.d_q, (size_t)s.d_q, q_norm_w, eps, uq_fast ? cqb : nullptr, hs);
+        else if (e == hipSuccess && uq_fast)
+          e = launch_to_bf16(cq, cqb, (size_t)B * s.d_q, hs);
+      }
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
-      if (q_norm_w && launch_rmsnorm(s, cq, B, s.d_q, (size_t)s.d_q, q_norm_w, eps, hs) != hipSuccess)
-        return MLA_ERR_LAUNCH;
-      x = cq;
-      x_f32 = true;
-      K = s.d_q;
+      x = uq_fast ? cqb : (const void*)cq;
+      x_f32 = !uq_fast;
     }
-    hipError_t e = linear(s, B, qw, K, x, x_f32, W_UQ, qf, part, hs);
+    hipError_t e = uq_fast ? launch_gemm_v3(B, qw, qw, kq, x, W_UQ, nullptr, nullptr, qbuf, part, hs)
+                           : linear(s, B, qw, kq, x, x_f32, W_UQ, (float*)qbuf, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
-    qsrc = qf;
-    q_f32 = true;
+    qsrc = qbuf;
+    q_f32 = !uq_fast;
   }
   if (!force_generic() && proj_v3_supported(s))
     return launched(launch_absorb_v3(s, B, qsrc, q_f32, W_UK, pos, q_lat, q_pe, hs));
@@ -416,16 +439,16 @@ mla_status_t append_common(const mla_dims_t* dims, int32_t B, int32_t n_new, con
     void* part = (char*)ws + align256((size_t)M * D * sizeof(float));
     if (fused_kv(s, M)) {
       // one [M, d_c + d_r] product: row i = [c_i | k_i]
-      hipError_t e = launch_gemm_v3(M, (int)D, s.d_c, s.d_model, h_t, false, W_DKV, W_KR, kc, part, hs);
+      hipError_t e = launch_gemm_v3(M, (int)D, s.d_c, s.d_model, h_t, W_DKV, W_KR, kc, nullptr, part, hs);
       if (e != hipSuccess) return MLA_ERR_LAUNCH;
-      if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, D, kv_norm_w, eps, hs) != hipSuccess)
+      if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, D, kv_norm_w, eps, nullptr, hs) != hipSuccess)
         return MLA_ERR_LAUNCH;
       return launched(write_rows(kc, D, kc + s.d_c, D, true));
     }
     float* kr = kc + (size_t)M * s.d_c;
     hipError_t e = linear(s, M, s.d_c, s.d_model, h_t, !s.bf16, W_DKV, kc, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
-    if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, (size_t)s.d_c, kv_norm_w, eps, hs) != hipSuccess)
+    if (kv_norm_w && launch_rmsnorm(s, kc, M, s.d_c, (size_t)s.d_c, kv_norm_w, eps, nullptr, hs) != hipSuccess)
       return MLA_ERR_LAUNCH;
     e = linear(s, M, s.d_r, s.d_model, h_t, !s.bf16, W_KR, kr, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
@@ -608,15 +631,28 @@ mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_l
   DeviceInfo info;
   if ((st = device_ready(&info)) != MLA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  // workspace: [o when not given (fp32) | split partials of W_O]
-  float* ob = o ? o : (float*)ws;
-  void* part = u ? (char*)ws + align256((size_t)B * s.n_h * s.d_v * sizeof(float)) : nullptr;
-  hipError_t e = (!force_generic() && proj_v3_supported(s))
-                     ? launch_uv_v3(s, B, o_lat, W_UV, ob, hs)
-                     : launch_uv_generic(s, B, o_lat, W_UV, ob, hs);
+  // workspace: regions as project_ws
+  const size_t n = (size_t)B * s.n_h * s.d_v;
+  const int kin = s.n_h * s.d_v;
+  const bool o_fast = u && fast_linear(s, B, s.d_model, kin);
+  const bool uv_fast = !force_generic() && proj_v3_supported(s);
+  char* w = (char*)ws;
+  float* of = o ? o : (float*)w;   // fp32 o
+  if (u) w += align256(n * sizeof(float));
+  void* obf = o_fast ? (void*)w : nullptr;   // bf16 o for the fast W^O
+  if (o_fast) w += align256(n * sizeof(uint16_t));
+  void* part = w;
+  hipError_t e;
+  if (uv_fast) {
+    e = launch_uv_v3(s, B, o_lat, W_UV, o || !o_fast ? of : nullptr, obf, hs);
+  } else {
+    e = launch_uv_generic(s, B, o_lat, W_UV, of, hs);
+    if (e == hipSuccess && o_fast) e = launch_to_bf16(of, obf, n, hs);
+  }
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (u) {
-    e = linear(s, B, s.d_model, s.n_h * s.d_v, ob, true, W_O, u, part, hs);
+    e = o_fast ? launch_gemm_v3(B, s.d_model, s.d_model, kin, obf, W_O, nullptr, u, nullptr, part, hs)
+               : linear(s, B, s.d_model, kin, of, true, W_O, u, part, hs);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -1946,10 +1946,12 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   c.G = G;
   c.scale_log2 = a.scale_log2;
   // about G / B pieces per sequence: fewer pieces, more column blocks per
-  // workgroup (CPW * pieces loads in flight per lane).  Measured: ragged
-  // B=64 (G/B = 4) best at CPW 8, uniform B=16 (16) at 2, long B=8 (32) at 1.
+  // workgroup (CPW * pieces loads in flight per lane), but not so many that
+  // large batches lose workgroups.  Measured best (median of 160 calls, CPW
+  // 1..16): ragged B=64 (G/B = 4) at 8, layer B=128 (2) at 4, uniform B=16
+  // (16) at 2, long B=8 (32) at 1; the rule below picks each of them.
   int cpw = 1;
-  while (cpw < CMB_NCB && cpw * G < 32 * B) cpw *= 2;
+  while (cpw < CMB_NCB && cpw * G < 32 * B && cpw * B < 512) cpw *= 2;
   c.cpw = cpw;
   k_combine<<<dim3((NH / CMB_HB) * (CMB_NCB / cpw), B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();

@@ -1,5 +1,5 @@
 // Weight-streaming linear layers of the MLA layer at decode batch sizes:
-//   Y[M, N] (fp32) = X[M, K] . W[N, K]^T
+//   Y[M, N] (fp32, or rounded once to bf16) = X[M, K] . W[N, K]^T, X bf16
 // ("MLA模型结构详解", worked example: the query path W^DQ, W^UQ, the latent
 // and rope key projections W^DKV, W^KR, and the output projection W^O.)
 //
@@ -21,10 +21,10 @@
 // * v_mfma_f32_32x32x16_bf16 with A = X (rows), B = W^T: both fragments are
 //   "8 consecutive k per lane" reads from LDS; within a 64-wide k chunk, lane
 //   half g holds k = 32 g + 8 j .. +8 for k-step j, in both operands.
-// * fp32 X (an intermediate such as c^Q, or the attention output o) enters
-//   the bf16 MFMA as hi + lo with hi = bf16(x), lo = bf16(x - hi): two MFMAs
-//   per step, about 16 significant bits of x instead of 8.  The split is done
-//   once per call by k_hilo into two bf16 planes in the workspace.
+// * Intermediate activations that feed a layer (c^Q, the query q, the
+//   attention output o) are rounded to bf16 once by the kernel that produces
+//   them, as everywhere in bf16 inference; a layer can write its own output
+//   that way (Yb), from its epilogue or from the split sum.
 // * The K splits are chosen so that all workgroups run in one round on the
 //   256 compute units.
 #include "common.h"
@@ -46,19 +46,18 @@ constexpr int KGROUP = 256;       // k granularity of the split plan
 constexpr int SLOTS = 256;        // workgroups per round (one per compute unit)
 constexpr int FPF = 8;            // A fragments read ahead
 
-// Stage = [W tile | X plane 0 (| X plane 1)]; NST stages in LDS.
-template <int NPL> struct GemmCfg {
-  static constexpr int PARTS = 1 + NPL;
-  static constexpr int STAGE = PARTS * TILEB;             // 32 or 48 KiB
-  static constexpr int NST = NPL == 2 ? 3 : 4;            // 144 or 128 KiB
-  static constexpr int DPW = PARTS * (TILEB / 1024) / 4;  // DMAs per wave per chunk: 8 or 12
-};
+// Stage = [W tile | X tile]; NST stages in LDS.
+constexpr int PARTS = 2;
+constexpr int STAGE = PARTS * TILEB;             // 32 KiB
+constexpr int NST = 4;                           // 128 KiB
+constexpr int DPW = PARTS * (TILEB / 1024) / 4;  // DMAs per wave per chunk: 8
 
 struct GemmArgs {
-  const __bf16* X;      // [NPL][M][K] bf16: X, or its hi and lo planes
+  const __bf16* X;      // [M][K]
   const __bf16* W1;     // rows 0 .. N1-1: W1[n][K]
   const __bf16* W2;     // rows N1 .. N-1: W2[n - N1][K] (may equal W1 + N1 K)
-  float* Y;             // [M][N] when splits == 1
+  float* Y;             // [M][N] fp32 output (when Yb is NULL)
+  __bf16* Yb;           // [M][N] bf16 output, rounded once from the fp32 sum
   float* part;          // [splits][M][N] when splits > 1
   int M, N, N1, K;
   int kper;             // k per split, a multiple of KGROUP
@@ -86,26 +85,7 @@ __device__ __forceinline__ void gwait_vm_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// hi = bf16(x), lo = bf16(x - hi) of fp32 X [n4 x 4], planes [2][n4 x 4]
-__global__ void __launch_bounds__(256) k_hilo(size_t n4, const floatx4* __restrict__ X, bf16x4* __restrict__ hi,
-                                              bf16x4* __restrict__ lo) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    const floatx4 x = X[i];
-    bf16x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = (__bf16)x[e];
-      l[e] = (__bf16)(x[e] - (float)h[e]);
-    }
-    hi[i] = h;
-    lo[i] = l;
-  }
-}
-
-template <int NPLANE>   // 1: bf16 X; 2: hi and lo planes of fp32 X
 __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
-  using C = GemmCfg<NPLANE>;
-  constexpr int NST = C::NST, DPW = C::DPW, STAGE = C::STAGE;
   __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
 
   const int nb = blockIdx.x, sk = blockIdx.y, mc = blockIdx.z;
@@ -119,7 +99,7 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
   // DMA plan of one chunk: instruction q = DPW wave + k (0 .. 16 PARTS - 1)
-  // fills part q / 16 of the stage (0: W, 1 + p: X plane p); lane i writes
+  // fills part q / 16 of the stage (0: W, 1: X); lane i writes
   // the 16 bytes at 16 u, u = 64 (q % 16) + i, which hold logical chunk
   // (u % 8) ^ xsw(r) of tile row r = u / 8.  Rows past M and columns past N
   // read the last valid row (their results are not stored).
@@ -137,7 +117,7 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
       src[k] = (const char*)(row + kb + 8 * c);
     } else {
       const int m = min(m0 + r, a.M - 1);
-      src[k] = (const char*)(a.X + (size_t)(part - 1) * a.M * a.K + (size_t)m * a.K + kb + 8 * c);
+      src[k] = (const char*)(a.X + (size_t)m * a.K + kb + 8 * c);
     }
   }
   // DMA k of chunk t into its stage; t past the end re-copies the last chunk
@@ -160,8 +140,8 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   const uint32_t arow = (uint32_t)(n32 * ROWB);
   const uint32_t brow = (uint32_t)((GNW * wave + n32) * ROWB);
 
-  constexpr int NF = 4 * NPLANE * GMB;      // MFMAs (= A fragments) per chunk
-  constexpr int PER_J = NPLANE * GMB;       // MFMAs per W fragment
+  constexpr int NF = 4 * GMB;   // MFMAs (= A fragments) per chunk
+  constexpr int PER_J = GMB;    // MFMAs per W fragment
 
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
@@ -180,8 +160,8 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
       gwait_vm_then_barrier<(NST - 2) * DPW>();
       const MLA_LDS char* st = (const MLA_LDS char*)lds + s * STAGE;
       auto frag_addr = [&](int f) {
-        const int mb = f % GMB, pl = (f / GMB) % NPLANE, j = f / PER_J;
-        return st + (1 + pl) * TILEB + mb * 32 * ROWB + arow + (((4 * g32 + j) ^ asw) << 4);
+        const int mb = f % GMB, j = f / PER_J;
+        return st + TILEB + mb * 32 * ROWB + arow + (((4 * g32 + j) ^ asw) << 4);
       };
       bf16x8 wf[4];
 #pragma unroll
@@ -208,6 +188,16 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   const int n0 = nw + GNW * wave;
   if (n0 >= a.N) return;   // wave-uniform
   // D layout: lane holds column n0 + n32, rows 32 mb + 8 (e/4) + 4 g32 + e%4.
+  if (a.splits == 1 && a.Yb) {
+#pragma unroll
+    for (int mb = 0; mb < GMB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * mb + 8 * (e >> 2) + 4 * g32 + (e & 3);
+        if (m < a.M) a.Yb[(size_t)m * a.N + n0 + n32] = (__bf16)acc[mb][e];
+      }
+    return;
+  }
   float* out = a.splits == 1 ? a.Y : a.part + (size_t)sk * a.M * a.N;
 #pragma unroll
   for (int mb = 0; mb < GMB; ++mb)
@@ -218,9 +208,9 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
     }
 }
 
-// Y = sum over splits of the partials, in split order.
+// Y (or Yb, rounded once) = sum over splits of the partials, in split order.
 __global__ void __launch_bounds__(256) k_split_sum(int splits, size_t n4, const floatx4* __restrict__ part,
-                                                   floatx4* __restrict__ Y) {
+                                                   floatx4* __restrict__ Y, bf16x4* __restrict__ Yb) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
     floatx4 s = part[i];
     for (int k = 1; k < splits; ++k) {
@@ -230,7 +220,10 @@ __global__ void __launch_bounds__(256) k_split_sum(int splits, size_t n4, const 
       s[2] += v[2];
       s[3] += v[3];
     }
-    Y[i] = s;
+    if (Yb)
+      Yb[i] = bf16x4{(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+    else
+      Y[i] = s;
   }
 }
 
@@ -260,37 +253,22 @@ bool gemm_v3_supported(int M, int N, int K) {
   return M >= 1 && N >= 32 && N % 32 == 0 && K >= KGROUP && K % KGROUP == 0;
 }
 
-// Workspace: the split partials [splits][M][N] fp32 (when splits > 1), then
-// for fp32 X its hi and lo planes [2][M][K] bf16.
-static size_t part_bytes(const Plan& p, int M, int N) {
+// Workspace: the split partials [splits][M][N] fp32 (when splits > 1).
+size_t gemm_v3_workspace(int M, int N, int K) {
+  if (!gemm_v3_supported(M, N, K)) return 0;
+  const Plan p = plan(M, N, K);
   return p.splits > 1 ? ((size_t)p.splits * M * N * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
-size_t gemm_v3_workspace(int M, int N, int K, bool x_f32) {
-  if (!gemm_v3_supported(M, N, K)) return 0;
-  const Plan p = plan(M, N, K);
-  return part_bytes(p, M, N) + (x_f32 ? ((size_t)2 * M * K * sizeof(__bf16) + 255) / 256 * 256 : 0);
-}
-
-hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32, const void* W1,
-                          const void* W2, float* Y, void* ws, hipStream_t st) {
+hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, const void* W1, const void* W2,
+                          float* Y, void* Yb, void* ws, hipStream_t st) {
   const Plan p = plan(M, N, K);
   GemmArgs a;
   a.X = (const __bf16*)X;
-  if (x_f32) {
-    __bf16* planes = (__bf16*)((char*)ws + part_bytes(p, M, N));
-    const size_t n4 = (size_t)M * K / 4;   // K is a multiple of 256
-    size_t blocks = (n4 + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    k_hilo<<<(unsigned)blocks, 256, 0, st>>>(n4, (const floatx4*)X, (bf16x4*)planes,
-                                              (bf16x4*)(planes + (size_t)M * K));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    a.X = planes;
-  }
   a.W1 = (const __bf16*)W1;
   a.W2 = (const __bf16*)(W2 ? W2 : W1);
   a.Y = Y;
+  a.Yb = (__bf16*)Yb;
   a.part = (float*)ws;
   a.M = M;
   a.N = N;
@@ -299,16 +277,13 @@ hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32
   a.kper = p.kper;
   a.splits = p.splits;
   dim3 grid(p.nblk, p.splits, p.mch);
-  if (x_f32)
-    k_gemm<2><<<grid, GT, 0, st>>>(a);
-  else
-    k_gemm<1><<<grid, GT, 0, st>>>(a);
+  k_gemm<<<grid, GT, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t n4 = (size_t)M * N / 4;
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  k_split_sum<<<(unsigned)blocks, 256, 0, st>>>(p.splits, n4, (const floatx4*)ws, (floatx4*)Y);
+  k_split_sum<<<(unsigned)blocks, 256, 0, st>>>(p.splits, n4, (const floatx4*)ws, (floatx4*)Y, (bf16x4*)Yb);
   return hipGetLastError();
 }
 

@@ -383,7 +383,7 @@ hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_l
 // One block of 256 per row: a sum of squares per lane, wave sums, four waves.
 template <typename T>
 __global__ void __launch_bounds__(256) k_rmsnorm(float* __restrict__ x, int cols, size_t stride,
-                                                 const T* __restrict__ w, float eps) {
+                                                 const T* __restrict__ w, float eps, __bf16* __restrict__ out) {
   __shared__ float red[4];
   float* row = x + (size_t)blockIdx.x * stride;
   float ss = 0.f;
@@ -395,16 +395,33 @@ __global__ void __launch_bounds__(256) k_rmsnorm(float* __restrict__ x, int cols
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = 1.f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)cols + eps);
-  for (int c = threadIdx.x; c < cols; c += 256) row[c] = row[c] * r * ld(w, c);
+  if (out) {
+    __bf16* orow = out + (size_t)blockIdx.x * cols;
+    for (int c = threadIdx.x; c < cols; c += 256) orow[c] = (__bf16)(row[c] * r * ld(w, c));
+  } else {
+    for (int c = threadIdx.x; c < cols; c += 256) row[c] = row[c] * r * ld(w, c);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_to_bf16(size_t n, const float* __restrict__ x, __bf16* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = (__bf16)x[i];
 }
 
 hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
-                          float eps, hipStream_t st) {
+                          float eps, void* out, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (s.bf16)
-    k_rmsnorm<__bf16><<<rows, 256, 0, st>>>(x, cols, ld, (const __bf16*)w, eps);
+    k_rmsnorm<__bf16><<<rows, 256, 0, st>>>(x, cols, ld, (const __bf16*)w, eps, (__bf16*)out);
   else
-    k_rmsnorm<float><<<rows, 256, 0, st>>>(x, cols, ld, (const float*)w, eps);
+    k_rmsnorm<float><<<rows, 256, 0, st>>>(x, cols, ld, (const float*)w, eps, (__bf16*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_to_bf16<<<(unsigned)blocks, 256, 0, st>>>(n, x, (__bf16*)y);
   return hipGetLastError();
 }
 

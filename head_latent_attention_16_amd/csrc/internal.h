@@ -71,9 +71,12 @@ hipError_t launch_decode_generic(const Shape& s, int B, int n_q, const void* q_l
 hipError_t launch_append_fp8(const Shape& s, int B, int n_new, const void* c_src, size_t c_stride,
                              const void* k_src, size_t k_stride, bool src_f32, void* cache, float* scales,
                              const RowMap& map, int32_t* lens, int32_t* err_flag, hipStream_t st);
-// In place on fp32 rows (stride ld): x[:cols] / sqrt(mean(x[:cols]^2) + eps) * w.
+// On fp32 rows (stride ld): x[:cols] / sqrt(mean(x[:cols]^2) + eps) * w, in
+// place, or (out != NULL) rounded once to bf16 into out [rows, cols].
 hipError_t launch_rmsnorm(const Shape& s, float* x, int rows, int cols, size_t ld, const void* w,
-                          float eps, hipStream_t st);
+                          float eps, void* out, hipStream_t st);
+// y[i] = bf16(x[i]), i < n
+hipError_t launch_to_bf16(const float* x, void* y, size_t n, hipStream_t st);
 // o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 out)
 hipError_t launch_uv_generic(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
                              hipStream_t st);
@@ -94,17 +97,18 @@ bool proj_v3_supported(const Shape& s);
 hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, const void* W_UK,
                             const int32_t* pos, void* q_lat, void* q_pe, hipStream_t st);
 
-// bf16-weight linear layer Y[M,N] (fp32) = X[M,K] . W^T, X bf16 or fp32.
-// Rows n < N1 of W come from W1 (stride K), rows >= N1 from W2 (W2 == NULL:
-// all rows from W1).  Needs N % 32 == 0 and K % 256 == 0, and a workspace of
-// gemm_v3_workspace(M, N, K, x_f32) bytes for the split partials and, with
-// fp32 X, its bf16 hi / lo planes (may be 0).
+// bf16-weight linear layer Y[M,N] = X[M,K] . W^T with bf16 X: fp32 into Y,
+// or (Yb != NULL) rounded once to bf16 into Yb.  Rows n < N1 of W come from
+// W1 (stride K), rows >= N1 from W2 (W2 == NULL: all rows from W1).  Needs
+// N % 32 == 0 and K % 256 == 0, and a workspace of gemm_v3_workspace(M, N, K)
+// bytes for the split partials (may be 0).
 bool gemm_v3_supported(int M, int N, int K);
-size_t gemm_v3_workspace(int M, int N, int K, bool x_f32);
-hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, bool x_f32, const void* W1,
-                          const void* W2, float* Y, void* ws, hipStream_t st);
-// o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 in and out).
-hipError_t launch_uv_v3(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o,
+size_t gemm_v3_workspace(int M, int N, int K);
+hipError_t launch_gemm_v3(int M, int N, int N1, int K, const void* X, const void* W1, const void* W2,
+                          float* Y, void* Yb, void* ws, hipStream_t st);
+// o[b,h,:] = W_UV[h] . o_lat[b,h,:] (fp32 o_lat): fp32 into o and/or rounded
+// once to bf16 into ob (either may be NULL).
+hipError_t launch_uv_v3(const Shape& s, int B, const float* o_lat, const void* W_UV, float* o, void* ob,
                         hipStream_t st);
 
 // Un-absorbed prefill at V3 dims (bf16): q [B, n_q, n_h, d_h + d_r] un-rotated,

@@ -224,7 +224,7 @@ constexpr int UV_PLANE = 32 * UV_ROWB;   // 8 KiB
 
 __global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ o_lat,
                                                const __bf16* __restrict__ W_UV,
-                                               float* __restrict__ o) {
+                                               float* __restrict__ o, __bf16* __restrict__ ob) {
   __shared__ floatx16 red[3][64];
   __shared__ __attribute__((aligned(16))) char xs[4][2][UV_PLANE];   // [wave][hi, lo]
   const int h = blockIdx.x, vb = blockIdx.y;
@@ -292,12 +292,17 @@ __global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ 
         for (int i = 0; i < 16; ++i) acc[i] += r[i];
       }
       // lane: batch bq, rows v = 32 vb + 8 (i/4) + 4 g32 + i%4
-      if (bq < B) {
-        float* dst = o + ((size_t)bq * NH + h) * DV + 32 * vb + 4 * g32;
+      const size_t at = ((size_t)bq * NH + h) * DV + 32 * vb + 4 * g32;
+      if (bq < B && o) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *(floatx4*)(dst + 8 * q4) =
-              floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+          *(floatx4*)(o + at + 8 * q4) = floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+      }
+      if (bq < B && ob) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(bf16x4*)(ob + at + 8 * q4) = bf16x4{(__bf16)acc[4 * q4], (__bf16)acc[4 * q4 + 1],
+                                                (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
       }
     }
     __syncthreads();
@@ -322,9 +327,9 @@ hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, co
   return hipGetLastError();
 }
 
-hipError_t launch_uv_v3(const Shape&, int B, const float* o_lat, const void* W_UV, float* o,
+hipError_t launch_uv_v3(const Shape&, int B, const float* o_lat, const void* W_UV, float* o, void* ob,
                         hipStream_t st) {
-  k_uv_v3<<<dim3(NH, DV / 32), 256, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o);
+  k_uv_v3<<<dim3(NH, DV / 32), 256, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o, (__bf16*)ob);
   return hipGetLastError();
 }
 

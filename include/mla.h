@@ -112,6 +112,10 @@ typedef struct {
  *          (W_UK [n_h, d_h, d_c]), q_pe [B, n_h, d_r] = RoPE(q^R[b,h,:], pos[b])
  *          (rotate-half, theta_i = base^(-2i/d_r), angle formed in fp64),
  *          both in dims->dtype, rounded to nearest even once from fp32.
+ * Precision from h_t with bf16 storage: the products accumulate in fp32, and
+ * c^Q and q are rounded once to bf16 before the next product (as in bf16
+ * inference) wherever the matrix-core layer runs (N a multiple of 32, K a
+ * multiple of 256); other shapes keep them in fp32.
  * pos [B] int32 device: the query position (the new token's index).
  * ws: device scratch of at least mla_absorb_q_workspace(dims, B, h_t != NULL)
  *     bytes (may be NULL when that is 0). */
@@ -128,7 +132,7 @@ size_t mla_absorb_q_workspace(const mla_dims_t* dims, int32_t B, int32_t from_hi
  * are readings too):
  *   c^Q = W_DQ h_t,  c^Q <- c^Q / sqrt(mean(c^Q^2) + eps) * q_norm_w,  q = W_UQ c^Q,
  * then as mla_absorb_q.  q_norm_w [d_q] in dims->dtype; the norm runs in fp32
- * on the fp32 c^Q.  Needs d_q >= 1, h_t, W_DQ, q_norm_w (MLA_ERR_NULL), and a
+ * on the fp32 c^Q (its result is then rounded as c^Q is in mla_absorb_q).  Needs d_q >= 1, h_t, W_DQ, q_norm_w (MLA_ERR_NULL), and a
  * finite eps >= 0 (MLA_ERR_SHAPE).  ws: mla_absorb_q_workspace(dims, B, 1). */
 mla_status_t mla_absorb_q_normed(const mla_dims_t* dims, int32_t B, const void* h_t,
                                  const void* W_DQ, const void* q_norm_w, float eps,
@@ -342,10 +346,12 @@ mla_status_t mla_decode_attn_fp8(const mla_dims_t* dims, int32_t B, const void* 
  *                                         u [B, d_model] fp32
  * o or u may be NULL to skip storing it (W_O may be NULL when u is NULL).  With
  * bf16 weights the products run on bf16 matrix cores with fp32 accumulation;
- * the fp32 activations (o_lat, and o for W_O) enter as two bf16 operands, the
- * rounded value hi = bf16(x) and the remainder lo = bf16(x - hi), both
- * multiplied by the weight, so the activation keeps about 16 significant
- * bits.
+ * the fp32 o_lat enters W_UV as two bf16 operands, the rounded value
+ * hi = bf16(x) and the remainder lo = bf16(x - hi), both multiplied by the
+ * weight, so it keeps about 16 significant bits; o enters W_O rounded once to
+ * bf16 (as in bf16 inference) wherever the matrix-core layer runs (d_model a
+ * multiple of 32, n_h d_v a multiple of 256), in fp32 otherwise; the o
+ * stored for the caller is the fp32 one.
  * ws: at least mla_project_out_workspace(dims, B, u != NULL) bytes. */
 mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_lat,
                              const void* W_UV, const void* W_O, float* o, float* u, void* ws,
