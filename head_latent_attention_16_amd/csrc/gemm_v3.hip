@@ -34,23 +34,25 @@ namespace mla {
 
 namespace {
 
-constexpr int GT = 256;           // threads per workgroup
+constexpr int GW = 4;             // waves per workgroup
+constexpr int GT = 64 * GW;       // threads per workgroup
 constexpr int GMB = 4;            // 32-row blocks per workgroup (128 rows)
 constexpr int GMR = GMB * 32;     // rows per workgroup
 constexpr int GNW = 32;           // output columns per wave
-constexpr int GNT = 4 * GNW;      // columns per workgroup
+constexpr int GNT = GW * GNW;     // columns per workgroup
 constexpr int KC = 64;            // k per chunk
 constexpr int ROWB = KC * 2;      // LDS bytes per row (or column) per chunk (bf16)
-constexpr int TILEB = 128 * ROWB; // one operand tile per chunk: 16 KiB
+constexpr int WTB = GNT * ROWB;   // W tile per chunk
+constexpr int XTB = GMR * ROWB;   // X tile per chunk: 16 KiB
 constexpr int KGROUP = 256;       // k granularity of the split plan
 constexpr int SLOTS = 256;        // workgroups per round (one per compute unit)
 constexpr int FPF = 8;            // A fragments read ahead
 
-// Stage = [W tile | X tile]; NST stages in LDS.
-constexpr int PARTS = 2;
-constexpr int STAGE = PARTS * TILEB;             // 32 KiB
-constexpr int NST = 4;                           // 128 KiB
-constexpr int DPW = PARTS * (TILEB / 1024) / 4;  // DMAs per wave per chunk: 8
+// Stage = [W tile | X tile]; as many stages as fit in 144 KiB of LDS.
+constexpr int STAGE = WTB + XTB;
+constexpr int NST = 144 * 1024 / STAGE;
+constexpr int DPW = STAGE / 1024 / GW;   // DMAs per wave per chunk
+static_assert(STAGE % (1024 * GW) == 0 && NST >= 3, "stage plan");
 
 struct GemmArgs {
   const __bf16* X;      // [M][K]
@@ -98,20 +100,21 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
   const int nch = (ke - kb) / KC;   // >= 1
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MLA_LDS char*)lds;
 
-  // DMA plan of one chunk: instruction q = DPW wave + k (0 .. 16 PARTS - 1)
-  // fills part q / 16 of the stage (0: W, 1: X); lane i writes
-  // the 16 bytes at 16 u, u = 64 (q % 16) + i, which hold logical chunk
-  // (u % 8) ^ xsw(r) of tile row r = u / 8.  Rows past M and columns past N
-  // read the last valid row (their results are not stored).
+  // DMA plan of one chunk: instruction q = DPW wave + k fills the 1024 bytes
+  // at 1024 q of the stage (the W tile, then the X tile); lane i writes the
+  // 16 bytes at 16 u of its tile, u = 64 q' + i (q' = q, or q minus the W
+  // tile's instructions), which hold logical chunk (u % 8) ^ xsw(r) of tile
+  // row r = u / 8.  Rows past M and columns past N read the last valid row
+  // (their results are not stored).
   const char* src[DPW];
 #pragma unroll
   for (int k = 0; k < DPW; ++k) {
     const int q = wave * DPW + k;
-    const int part = q / 16;
-    const int u = 64 * (q % 16) + lane;
+    const bool wpart = q < WTB / 1024;
+    const int u = 64 * (wpart ? q : q - WTB / 1024) + lane;
     const int r = u >> 3;
     const int c = (u & 7) ^ xsw(r);
-    if (part == 0) {
+    if (wpart) {
       const int n = min(nw + r, a.N - 1);
       const __bf16* row = n < a.N1 ? a.W1 + (size_t)n * a.K : a.W2 + (size_t)(n - a.N1) * a.K;
       src[k] = (const char*)(row + kb + 8 * c);
@@ -161,7 +164,7 @@ __global__ void __launch_bounds__(GT, 1) k_gemm(GemmArgs a) {
       const MLA_LDS char* st = (const MLA_LDS char*)lds + s * STAGE;
       auto frag_addr = [&](int f) {
         const int mb = f % GMB, j = f / PER_J;
-        return st + TILEB + mb * 32 * ROWB + arow + (((4 * g32 + j) ^ asw) << 4);
+        return st + WTB + mb * 32 * ROWB + arow + (((4 * g32 + j) ^ asw) << 4);
       };
       bf16x8 wf[4];
 #pragma unroll

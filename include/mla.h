@@ -351,7 +351,7 @@ mla_status_t mla_decode_attn_fp8(const mla_dims_t* dims, int32_t B, const void* 
  * weight, so it keeps about 16 significant bits; o enters W_O rounded once to
  * bf16 (as in bf16 inference) wherever the matrix-core layer runs (d_model a
  * multiple of 32, n_h d_v a multiple of 256), in fp32 otherwise; the o
- * stored for the caller is the fp32 one.
+ * stored for the caller is the fp32 product.
  * ws: at least mla_project_out_workspace(dims, B, u != NULL) bytes. */
 mla_status_t mla_project_out(const mla_dims_t* dims, int32_t B, const float* o_lat,
                              const void* W_UV, const void* W_O, float* o, float* u, void* ws,
