@@ -227,7 +227,7 @@ def bench_prefill(args):
                    "B": B, "new_tokens": B * T, "step": "prefill_attn (up-projection + causal attention)"},
         "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "mla_prefill_attn (k_q_rope, k_kr_f16, k_upproj, k_prefill)",
+                     "kernel": "mla_prefill_attn (k_rope_table, k_kr_f16, k_upproj, k_prefill)",
                      "call_us": call_ms * 1e3, "flops": flops, "flops_upproj": flops_up, "flops_attention": flops_attn},
         "cpu_baseline": None,
     }
