@@ -21,11 +21,12 @@
 //   angle); k_prefill rotates q^R with them as it loads the query (fp16).
 // * k_upproj: KV[r, h] = [W^UK[h] c_r | W^UV[h] c_r] (fp16) for every cache
 //   row r, a bf16 [rows x 512] . [512 x n_h 256] GEMM; a workgroup owns one head's 256
-//   output columns for 128 rows, the 512-deep reduction in 64-wide chunks
+//   output columns for 256 rows, the 512-deep reduction in 64-wide chunks
 //   double-buffered in LDS through direct global -> LDS loads.
-// * k_prefill: flash attention per (sequence, head, 128 new tokens): four
-//   waves of 32 tokens; 64-key blocks of [K^C | k^R] (384 B per row) and V
-//   (256 B per row) are DMA'd into LDS one block ahead; S^T = K Q^T and
+// * k_prefill: flash attention per (sequence, head, 256 new tokens): eight
+//   waves of 32 tokens; 64-key blocks of [K^C | k^R]
+//   (384 B per row) and V (256 B per row) are DMA'd into three LDS stages,
+//   two blocks ahead; S^T = K Q^T and
 //   O^T += V^T P^T on v_mfma_f32_32x32x16_f16 (V^T fragments by transpose
 //   reads) in 32-key steps, an online softmax in base 2 with the running
 //   max, the causal mask on the diagonal blocks.
@@ -103,18 +104,21 @@ __global__ void __launch_bounds__(256) k_kr_f16(int64_t rows, const __bf16* __re
 
 // ---------------------------------------------------------------------------
 // Up-projection GEMM.  KV^T tile of one head: rows of the output are the 256
-// weight rows (W^UK[h] then W^UV[h]), columns 128 cache rows.  Wave w:
-// weight rows 64 w .. +64 (two 32-row blocks) for all 128 cache rows (four
-// blocks): 8 accumulators.  Per 64-wide k chunk the
-// stage holds W [256 x 64] (32 KiB) and X [128 x 64] (16 KiB), rows of 128 B
-// with the 16-byte chunk c of row r at c ^ ((r >> 1) & 7).
+// weight rows (W^UK[h] then W^UV[h]), columns U_ROWS = 256 cache rows.  Wave
+// w: weight rows 64 w .. +64 (two 32-row blocks) for all 256 cache rows
+// (eight blocks): 16 accumulators (in the accumulation registers).  Per
+// 64-wide k chunk the stage holds W [256 x 64] (32 KiB) and X [256 x 64]
+// (32 KiB), rows of 128 B with the 16-byte chunk c of row r at
+// c ^ ((r >> 1) & 7).  Each workgroup streams its head's 256 KiB of weights
+// once per 256 rows (128 rows per workgroup: 0.91 ms at B = 4, T = 4096;
+// 256 rows: 0.84 ms).
 // ---------------------------------------------------------------------------
-constexpr int U_ROWS = 128;                      // cache rows per workgroup
+constexpr int U_ROWS = 256;                      // cache rows per workgroup
 constexpr int U_KC = 64;                         // k per chunk
 constexpr int U_WB = KVW * U_KC * 2;             // 32768
-constexpr int U_XB = U_ROWS * U_KC * 2;          // 16384
-constexpr int U_STAGE = U_WB + U_XB;             // 49152
-constexpr int U_DPW = U_STAGE / 1024 / 4;        // 12 DMAs per wave per chunk
+constexpr int U_XB = U_ROWS * U_KC * 2;          // 32768
+constexpr int U_STAGE = U_WB + U_XB;             // 65536
+constexpr int U_DPW = U_STAGE / 1024 / 4;        // DMAs per wave per chunk
 static_assert(U_DPW * 4 * 1024 == U_STAGE, "whole DMA instructions per wave");
 
 __device__ __forceinline__ int usw(int r) { return (r >> 1) & 7; }
@@ -132,8 +136,8 @@ __global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __res
   const char* wuv = (const char*)(W_UV + (size_t)h * PD_V * PD_C);
   const char* crow = (const char*)cache;
 
-  // DMA k of this wave for chunk kc: LDS chunk p = 64 (12 wave + k) + lane of
-  // the stage; p < 2048: W row p / 8, else X row (p - 2048) / 8; physical
+  // DMA k of this wave for chunk kc: LDS chunk p = 64 (U_DPW wave + k) + lane
+  // of the stage; p < 2048: W row p / 8, else X row (p - 2048) / 8; physical
   // 16-byte position p % 8 holds logical chunk (p % 8) ^ usw(row).
   auto dma_chunk = [&](int kc, int stage) {
 #pragma unroll
@@ -152,11 +156,12 @@ __global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __res
     }
   };
 
-  floatx16 acc[2][4];
+  constexpr int NJ = U_ROWS / 32;   // 32-row blocks of cache rows
+  floatx16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -175,28 +180,28 @@ __global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __res
 #pragma unroll
     for (int ks = 0; ks < U_KC / 16; ++ks) {
       const int c = 2 * ks + g;   // logical 16-byte chunk of this lane's 8 k values
-      bf16x8 A[2], Bx[4];
+      bf16x8 A[2], Bx[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int wr = 64 * wave + 32 * i + n32;
         A[i] = *(const MLA_LDS bf16x8*)(Ws + wr * 128 + ((c ^ usw(wr)) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int xr = 32 * j + n32;
         Bx[j] = *(const MLA_LDS bf16x8*)(Xs + xr * 128 + ((c ^ usw(xr)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], Bx[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], Bx[j], acc[i][j], 0, 0, 0);
     }
     asm volatile("s_barrier" ::: "memory");   // the stage is refilled next
   }
   // acc[i][j]: weight rows 64 wave + 32 i + {8 (e / 4) + 4 g + e % 4}, cache
   // row 32 j + n32; four consecutive weight rows -> 8 contiguous bytes.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int r = r0 + 32 * j + n32;
     if (r >= rows) continue;
     _Float16* out = kv + ((size_t)r * PN_H + h) * KVW;
@@ -218,14 +223,17 @@ __global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __res
 // c ^ ((r >> 1) & 7)) then V [64 x 128] (rows of 256 B, 16 chunks; chunk c of
 // row r at c ^ (4 (r & 3))).  40 KiB = 10 DMAs per wave; two stages.
 // ---------------------------------------------------------------------------
-constexpr int F_TQ = 128;                 // new tokens per workgroup
+constexpr int F_WAVES = 8;                // waves per workgroup
+constexpr int F_TB = 1;                   // 32-token blocks per wave
+constexpr int F_TQ = F_WAVES * 32 * F_TB; // new tokens per workgroup (256)
 constexpr int F_KB = 64;                  // keys per block
+constexpr int F_NST = 3;                  // LDS stages: two blocks in flight
 constexpr int F_KROWB = PQK * 2;          // 384
 constexpr int F_VROWB = PD_V * 2;         // 256
 constexpr int F_KB_BYTES = F_KB * F_KROWB;   // 24576
 constexpr int F_STAGE = F_KB_BYTES + F_KB * F_VROWB;   // 40960
-constexpr int F_DPW = F_STAGE / 1024 / 4;    // 10
-static_assert(F_DPW * 4 * 1024 == F_STAGE, "whole DMA instructions per wave");
+constexpr int F_DPW = F_STAGE / 1024 / F_WAVES;    // DMAs per wave and block
+static_assert(F_DPW * F_WAVES * 1024 == F_STAGE, "whole DMA instructions per wave");
 
 __device__ __forceinline__ int ksw(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int vsw(int r) { return 4 * (r & 3); }
@@ -244,12 +252,25 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// Two workgroups per compute unit (80 KiB of LDS and at most 256 registers
-// per lane each), so one workgroup's softmax and barriers overlap the other's
-// matrix work.
-__global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * F_STAGE];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// One workgroup of F_WAVES waves per compute unit (120 KiB of LDS, two waves
+// per SIMD), 256 new tokens: each key block streamed into LDS serves all of
+// them.  Each wave holds F_TB blocks of 32 tokens; with more than one, every
+// key and value fragment read from LDS feeds F_TB MFMAs (two blocks per wave
+// with four waves needs more than one wave's registers: it spilled and ran
+// 3x slower).
+__global__ void __launch_bounds__(64 * F_WAVES, 1) k_prefill(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[F_NST * F_STAGE];
+  // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs
+  // round-robin in launch order; each XCD takes a contiguous run of work
+  // items instead, so the token blocks of one (sequence, head), which stream
+  // the same keys and values, share that XCD's L2 (B = 4, T = 4096, 128
+  // tokens per workgroup: 5.9 -> 4.1 ms).  Within a (sequence, head) the
+  // longest token blocks go first.
+  const int nqb = gridDim.x;
+  const int total = nqb * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + nqb * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int W = (total % 8 == 0) ? (L % 8) * (total / 8) + L / 8 : L;
+  const int qb = nqb - 1 - W % nqb, h = (W / nqb) % gridDim.y, b = W / (nqb * gridDim.y);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, g = lane >> 5;
@@ -261,29 +282,45 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
   const int i0 = qb * F_TQ;                       // first token of the workgroup
   const int nq_wg = min(F_TQ, a.n_q - i0);        // tokens of the workgroup
   const bool valid = len >= a.n_q && len <= cap && (int64_t)off + len <= a.rows && off >= 0;
-  const int tok = i0 + 32 * wave + n32;           // this lane's token (column of S^T)
-  const bool tok_ok = 32 * wave + n32 < nq_wg;
-  float* orow = a.o + (((size_t)b * a.n_q + min(tok, a.n_q - 1)) * PN_H + h) * PD_V;
+  // token block j of this wave: tokens i0 + 32 (F_TB wave + j) + n32 (the
+  // column of S^T this lane holds); lanes past the workgroup's tokens take
+  // its last token and store nothing
+  int tok[F_TB], pos[F_TB], bfirst[F_TB];
+  bool tok_ok[F_TB];
+#pragma unroll
+  for (int j = 0; j < F_TB; ++j) {
+    const int tw = 32 * (F_TB * wave + j);
+    tok[j] = i0 + tw + n32;
+    tok_ok[j] = tw + n32 < nq_wg;
+    pos[j] = len - a.n_q + min(tok[j], a.n_q - 1);
+    bfirst[j] = len - a.n_q + i0 + min(tw, nq_wg - 1);   // the block's first position
+  }
   if (!valid) {
-    if (tok_ok) {
-      for (int c = g; c < PD_V; c += 2) orow[c] = __builtin_nanf("");
-      if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok) * PN_H + h] = __builtin_nanf("");
-    }
+#pragma unroll
+    for (int j = 0; j < F_TB; ++j)
+      if (tok_ok[j]) {
+        float* orow = a.o + (((size_t)b * a.n_q + tok[j]) * PN_H + h) * PD_V;
+        for (int c = g; c < PD_V; c += 2) orow[c] = __builtin_nanf("");
+        if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok[j]) * PN_H + h] = __builtin_nanf("");
+      }
     if (tid == 0 && qb == 0 && h == 0 && a.err_flag) atomicOr(a.err_flag, MLA_DEVERR_LENS);
     return;
   }
   const int p_first = len - a.n_q + i0;           // position of the workgroup's first token
   const int p_last = p_first + nq_wg - 1;
-  const int pos = len - a.n_q + min(tok, a.n_q - 1);   // this lane's token position
   const int nblk = (p_last + 1 + F_KB - 1) / F_KB;     // key blocks any token sees
+  // the wave's last position; a wave without tokens only helps with the loads
+  const bool idle = 32 * F_TB * wave >= nq_wg;
+  const int wpos_last = p_first + min(32 * F_TB * wave + 32 * F_TB - 1, nq_wg - 1);
 
-  // Q^T fragments (B operand): token n32 of this wave, features 16 kk + 8 g,
-  // in fp16.  Rope feature r = 16 (kk - 8) + 8 g + j pairs with r + 32: the
+  // Q^T fragments (B operand) of block j: token n32, features 16 kk + 8 g,
+  // in fp16.  Rope feature r = 16 (kk - 8) + 8 g + e pairs with r + 32: the
   // lane holds both (kk = 8 with 10, 9 with 11) and rotates them with the
   // angle of frequency r (rotate-half).
-  halfx8 q[PQK / 16];
-  {
-    const size_t t = (size_t)b * a.n_q + min(tok, a.n_q - 1);
+  halfx8 q[F_TB][PQK / 16];
+#pragma unroll
+  for (int j = 0; j < F_TB; ++j) {
+    const size_t t = (size_t)b * a.n_q + min(tok[j], a.n_q - 1);
     const __bf16* qr = a.q + (t * PN_H + h) * PQK;
     bf16x8 raw[PQK / 16];
 #pragma unroll
@@ -291,26 +328,26 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
 #pragma unroll
     for (int kk = 0; kk < PD_H / 16; ++kk)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[kk][j] = (_Float16)(float)raw[kk][j];
+      for (int e = 0; e < 8; ++e) q[j][kk][e] = (_Float16)(float)raw[kk][e];
     const float2* rt = a.rope + t * (PD_R / 2);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {          // kk = 8 + hh pairs with 10 + hh
       const int kl = PD_H / 16 + hh, khi = kl + 2;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float2 cs = rt[16 * hh + 8 * g + j];
-        const float lo = (float)raw[kl][j], hi = (float)raw[khi][j];
-        q[kl][j] = (_Float16)(lo * cs.x - hi * cs.y);
-        q[khi][j] = (_Float16)(hi * cs.x + lo * cs.y);
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = rt[16 * hh + 8 * g + e];
+        const float lo = (float)raw[kl][e], hi = (float)raw[khi][e];
+        q[j][kl][e] = (_Float16)(lo * cs.x - hi * cs.y);
+        q[j][khi][e] = (_Float16)(hi * cs.x + lo * cs.y);
       }
     }
   }
 
   const char* kvb = (const char*)(a.kv + (size_t)h * KVW);     // row r at kvb + r * n_h * 512
   const size_t kv_row = (size_t)PN_H * KVW * 2;
-  // DMA k of this wave for key block kb: stage chunk p = 64 (10 wave + k) + lane;
-  // p < 1536: K row p / 24, physical chunk p % 24 holding logical chunk
-  // (p % 24) ^ ksw(row) (logical < 16: K^C from kv, else k^R);
+  // DMA k of this wave for key block kb: stage chunk p = 64 (F_DPW wave + k)
+  // + lane; p < 1536: K row p / 24, physical chunk p % 24 holding logical
+  // chunk (p % 24) ^ ksw(row) (logical < 16: K^C from kv, else k^R);
   // else V row (p - 1536) / 16, logical chunk ((p - 1536) % 16) ^ vsw(row).
   auto dma_block = [&](int kb, int stage) {
 #pragma unroll
@@ -332,13 +369,19 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
     }
   };
 
-  floatx16 O[PD_V / 32];
+  floatx16 O[F_TB][PD_V / 32];
 #pragma unroll
-  for (int cb = 0; cb < PD_V / 32; ++cb)
+  for (int j = 0; j < F_TB; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) O[cb][e] = 0.f;
-  float m_run = -INFINITY;   // running max of this lane's token (log2 units)
-  float l_run = 0.f;         // this lane's share of the weight sum
+    for (int cb = 0; cb < PD_V / 32; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[j][cb][e] = 0.f;
+  float m_run[F_TB], l_run[F_TB];   // running max (log2 units) and this lane's share of the sum
+#pragma unroll
+  for (int j = 0; j < F_TB; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
 
   // transpose-read bases for V^T fragments: group G = lane / 16, i = lane % 16
   // reads 8 bytes of key row 16 kk2 + 8 rd + rr (rr = 4 g + i / 4) at value
@@ -346,76 +389,87 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
   const int Gq = lane >> 4, i16 = lane & 15;
   const int rr = 4 * g + (i16 >> 2);
 
-  dma_block(0, 0);
+  // Block kb + F_NST - 1 goes into the stage of block kb - 1, which every
+  // wave has finished (the barrier at the end of its step); indices past
+  // the last block repeat it into the free stage, so the wait count is
+  // constant.
+#pragma unroll
+  for (int k = 0; k < F_NST - 1; ++k) dma_block(min(k, nblk - 1), k);
   for (int kb = 0; kb < nblk; ++kb) {
-    if (kb + 1 < nblk) {
-      dma_block(kb + 1, (kb + 1) & 1);
-      vm_wait_barrier<F_DPW>();
-    } else {
-      vm_wait_barrier<0>();
-    }
-    const MLA_LDS char* Ks = (const MLA_LDS char*)lds + (kb & 1) * F_STAGE;
+    dma_block(min(kb + F_NST - 1, nblk - 1), (kb + F_NST - 1) % F_NST);
+    vm_wait_barrier<(F_NST - 1) * F_DPW>();   // block kb has landed
+    const MLA_LDS char* Ks = (const MLA_LDS char*)lds + (kb % F_NST) * F_STAGE;
     const MLA_LDS char* Vs = Ks + F_KB_BYTES;
     // The block's two 32-key halves are taken one after the other, each a
-    // step of the online softmax: S^T[32 keys x 32 tokens] = K Q^T, the
-    // causal mask, the running max (rescaling what was accumulated when it
-    // moves), the weights, O^T += V^T P^T.
+    // step of the online softmax for both token blocks: S^T[32 keys x 32
+    // tokens] = K Q^T, the causal mask, the running max (rescaling what was
+    // accumulated when it moves), the weights, O^T += V^T P^T.
 #pragma unroll 1
-    for (int t = 0; t < 2; ++t) {
-      floatx16 S;
+    for (int t = 0; t < F_KB / 32; ++t) {
+      const int kbase = kb * F_KB + 32 * t;
+      // every token of the wave precedes these keys: all weights are 0 and
+      // the running max stays, so the step changes nothing
+      if (idle || kbase > wpos_last) continue;
+      floatx16 S[F_TB];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) S[e] = 0.f;
+      for (int j = 0; j < F_TB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[j][e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < PQK / 16; ++kk) {
         const int kr = 32 * t + n32, c = 2 * kk + g;
         const halfx8 kf = *(const MLA_LDS halfx8*)(Ks + kr * F_KROWB + ((c ^ ksw(kr)) << 4));
-        S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[kk], S, 0, 0, 0);
-      }
-      // key of S[e] is 64 kb + 32 t + 8 (e / 4) + 4 g + e % 4.  Off the
-      // diagonal (every key of this half at or before the workgroup's first
-      // token) nothing is masked; on it, masked scores become -inf.  The max
-      // is taken on the raw scores (the scale is positive) and the scale is
-      // folded into the exponent's fma.
-      const int kbase = kb * F_KB + 32 * t;
-      if (kbase + 31 > p_first) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kbase + 8 * (e >> 2) + 4 * g + (e & 3);
-          S[e] = (key <= pos && key < len) ? S[e] : -INFINITY;
+        for (int j = 0; j < F_TB; ++j) S[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, q[j][kk], S[j], 0, 0, 0);
+      }
+      // weights as the PV operand: P[j][kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3}
+      halfx8 P[F_TB][2];
+#pragma unroll
+      for (int j = 0; j < F_TB; ++j) {
+        // key of S[e] is kbase + 8 (e / 4) + 4 g + e % 4.  Off the diagonal
+        // (every key of this half at or before the block's first token)
+        // nothing is masked; on it, masked scores become -inf.  The max is
+        // taken on the raw scores (the scale is positive) and the scale is
+        // folded into the exponent's fma.
+        if (kbase + 31 > bfirst[j]) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kbase + 8 * (e >> 2) + 4 * g + (e & 3);
+            S[j][e] = (key <= pos[j] && key < len) ? S[j][e] : -INFINITY;
+          }
         }
-      }
-      float bmax = fmaxf(S[0], S[1]);
+        float bmax = fmaxf(S[j][0], S[j][1]);
 #pragma unroll
-      for (int e = 2; e < 16; e += 2) bmax = fmaxf(bmax, fmaxf(S[e], S[e + 1]));
-      // the token's max over both lane halves, in log2 units
-      {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
-      }
-      // every token sees key 0 in the first half-block, so m_new is finite
-      const float m_new = fmaxf(m_run, bmax * a.scale_log2);
-      // rescale what was accumulated when the max moved
-      if (__any(m_new > m_run)) {
-        const float al = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf: 0
-        l_run *= al;
+        for (int e = 2; e < 16; e += 2) bmax = fmaxf(bmax, fmaxf(S[j][e], S[j][e + 1]));
+        // the token's max over both lane halves, in log2 units
+        {
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
+        }
+        // every token sees key 0 in its first step, so m_new is finite
+        // (a fully masked block of a later step keeps m_run)
+        const float m_new = fmaxf(m_run[j], bmax * a.scale_log2);
+        // rescale what was accumulated when the max moved
+        if (__any(m_new > m_run[j])) {
+          const float al = __builtin_amdgcn_exp2f(m_run[j] - m_new);   // m_run = -inf: 0
+          l_run[j] *= al;
 #pragma unroll
-        for (int cb = 0; cb < PD_V / 32; ++cb)
+          for (int cb = 0; cb < PD_V / 32; ++cb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) O[cb][e] *= al;
-      }
-      m_run = m_new;
-      // weights as the PV operand: P[kk2] holds keys 32 t + 16 kk2 + {4 g + 0..3, 8 + 4 g + 0..3};
-      // l sums the same fp16 weights, two per dot instruction
-      halfx8 P[2];
+            for (int e = 0; e < 16; ++e) O[j][cb][e] *= al;
+        }
+        m_run[j] = m_new;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        P[e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(S[e], a.scale_log2, -m_new));
-      const halfx2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        for (int e = 0; e < 16; ++e)
+          P[j][e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(S[j][e], a.scale_log2, -m_new));
+        // l sums the same fp16 weights, two per dot instruction
+        const halfx2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const halfx2 pr = {P[e >> 3][e & 7], P[e >> 3][(e & 7) + 1]};
-        l_run = __builtin_amdgcn_fdot2(pr, one2, l_run, false);
+        for (int e = 0; e < 16; e += 2) {
+          const halfx2 pr = {P[j][e >> 3][e & 7], P[j][e >> 3][(e & 7) + 1]};
+          l_run[j] = __builtin_amdgcn_fdot2(pr, one2, l_run[j], false);
+        }
       }
       // O^T[value cols x tokens] += V^T . P^T, four 32-column blocks
 #pragma unroll
@@ -432,28 +486,33 @@ __global__ void __launch_bounds__(256, 2) k_prefill(PrefillArgs a) {
           }
           const halfx8 vf = {part[0][0], part[0][1], part[0][2], part[0][3],
                              part[1][0], part[1][1], part[1][2], part[1][3]};
-          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[kk2], O[cb], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < F_TB; ++j)
+            O[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[j][kk2], O[j][cb], 0, 0, 0);
         }
     }
     asm volatile("s_barrier" ::: "memory");   // every wave is done with this stage
   }
-  // normalise and store: O[cb][e] is value column 32 cb + 8 (e / 4) + 4 g + e % 4
-  {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated last blocks land before the LDS is released
+  // normalise and store: O[j][cb][e] is value column 32 cb + 8 (e / 4) + 4 g + e % 4
+#pragma unroll
+  for (int j = 0; j < F_TB; ++j) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    l_run += __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(l_run)));
+    const float l = l_run[j] + __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(l_run[j])));
+    if (!tok_ok[j]) continue;
+    float* orow = a.o + (((size_t)b * a.n_q + tok[j]) * PN_H + h) * PD_V;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int cb = 0; cb < PD_V / 32; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 v = {O[j][cb][4 * q4] * inv, O[j][cb][4 * q4 + 1] * inv, O[j][cb][4 * q4 + 2] * inv,
+                           O[j][cb][4 * q4 + 3] * inv};
+        *(floatx4*)(orow + 32 * cb + 8 * q4 + 4 * g) = v;
+      }
+    if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok[j]) * PN_H + h] = (m_run[j] + log2f(l)) * kLn2;
   }
-  if (!tok_ok) return;
-  const float inv = 1.f / l_run;
-#pragma unroll
-  for (int cb = 0; cb < PD_V / 32; ++cb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const floatx4 v = {O[cb][4 * q4] * inv, O[cb][4 * q4 + 1] * inv, O[cb][4 * q4 + 2] * inv,
-                         O[cb][4 * q4 + 3] * inv};
-      *(floatx4*)(orow + 32 * cb + 8 * q4 + 4 * g) = v;
-    }
-  if (g == 0 && a.lse) a.lse[((size_t)b * a.n_q + tok) * PN_H + h] = (m_run + log2f(l_run)) * kLn2;
 }
 
 }  // namespace
@@ -504,7 +563,7 @@ hipError_t launch_prefill_v3(const Shape& s, int B, int n_q, const void* q, cons
   a.n_q = n_q;
   a.rows = (int)rows;
   a.scale_log2 = s.scale * kLog2e;
-  k_prefill<<<dim3((n_q + F_TQ - 1) / F_TQ, PN_H, B), 256, 0, st>>>(a);
+  k_prefill<<<dim3((n_q + F_TQ - 1) / F_TQ, PN_H, B), 64 * F_WAVES, 0, st>>>(a);
   return hipGetLastError();
 }
 
