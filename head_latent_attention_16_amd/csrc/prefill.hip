@@ -228,6 +228,8 @@ constexpr int F_TB = 1;                   // 32-token blocks per wave
 constexpr int F_TQ = F_WAVES * 32 * F_TB; // new tokens per workgroup (256)
 constexpr int F_KB = 64;                  // keys per block
 constexpr int F_NST = 3;                  // LDS stages: two blocks in flight
+constexpr float F_SLACK = 8.f;            // log2 headroom of the softmax reference
+constexpr float F_WMAX = 256.f;           // 2^F_SLACK: the largest weight kept
 constexpr int F_KROWB = PQK * 2;          // 384
 constexpr int F_VROWB = PD_V * 2;         // 256
 constexpr int F_KB_BYTES = F_KB * F_KROWB;   // 24576
@@ -349,7 +351,33 @@ __global__ void __launch_bounds__(64 * F_WAVES, 1) k_prefill(PrefillArgs a) {
   // + lane; p < 1536: K row p / 24, physical chunk p % 24 holding logical
   // chunk (p % 24) ^ ksw(row) (logical < 16: K^C from kv, else k^R);
   // else V row (p - 1536) / 16, logical chunk ((p - 1536) % 16) ^ vsw(row).
+  // A block whose rows all lie before the sequence's end takes each source
+  // as block 0's plus kb blocks of its stride (K^C and V rows are kv_row
+  // apart, k^R rows 128 B); the last block clamps its rows one by one.
+  const char* src0[F_DPW];
+  uint32_t bstep[F_DPW];
+#pragma unroll
+  for (int k = 0; k < F_DPW; ++k) {
+    const int p = 64 * (F_DPW * wave + k) + lane;
+    if (p < F_KB_BYTES / 16) {
+      const int kr = p / 24, pc = p - kr * 24, c = pc ^ ksw(kr);
+      const size_t row = (size_t)off + kr;
+      src0[k] = c < 16 ? kvb + row * kv_row + c * 16 : (const char*)(a.kr + row * PD_R) + (c - 16) * 16;
+      bstep[k] = c < 16 ? (uint32_t)(F_KB * kv_row) : (uint32_t)(F_KB * PD_R * 2);
+    } else {
+      const int pv = p - F_KB_BYTES / 16;
+      const int vr = pv >> 4, c = (pv & 15) ^ vsw(vr);
+      src0[k] = kvb + ((size_t)off + vr) * kv_row + PD_H * 2 + c * 16;
+      bstep[k] = (uint32_t)(F_KB * kv_row);
+    }
+  }
   auto dma_block = [&](int kb, int stage) {
+    if ((kb + 1) * F_KB <= len) {
+#pragma unroll
+      for (int k = 0; k < F_DPW; ++k)
+        dma16(lds0 + (uint32_t)(stage * F_STAGE + (F_DPW * wave + k) * 1024), src0[k] + (size_t)kb * bstep[k]);
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < F_DPW; ++k) {
       const int p = 64 * (F_DPW * wave + k) + lane;
@@ -431,38 +459,52 @@ __global__ void __launch_bounds__(64 * F_WAVES, 1) k_prefill(PrefillArgs a) {
         // nothing is masked; on it, masked scores become -inf.  The max is
         // taken on the raw scores (the scale is positive) and the scale is
         // folded into the exponent's fma.
+        // (pos <= len - 1, so key <= pos also keeps key < len)
         if (kbase + 31 > bfirst[j]) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kbase + 8 * (e >> 2) + 4 * g + (e & 3);
-            S[j][e] = (key <= pos[j] && key < len) ? S[j][e] : -INFINITY;
+            S[j][e] = key <= pos[j] ? S[j][e] : -INFINITY;
           }
         }
-        float bmax = fmaxf(S[j][0], S[j][1]);
+        // The weights against the reference m_run, in fp32.  The reference
+        // moves (rescaling what was accumulated) only when some token's
+        // weight would pass 2^F_SLACK: weights that large are exact enough in
+        // fp16 and their sums in fp32, and the rescale is then rare instead
+        // of happening in most steps.  The check takes the max of the
+        // exponentials (canonical results, one instruction per three of
+        // them); the token's max score over both lane halves is formed only
+        // when the reference moves, and the weights are then recomputed.
+        // Every token sees key 0 in its first step: before it m_run = -inf,
+        // its weight is +inf and the reference becomes finite (masked scores
+        // give NaN there, which the max ignores, and 0 after it).
+        float w[16];
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) bmax = fmaxf(bmax, fmaxf(S[j][e], S[j][e + 1]));
-        // the token's max over both lane halves, in log2 units
-        {
+        for (int e = 0; e < 16; ++e) w[e] = __builtin_amdgcn_exp2f(fmaf(S[j][e], a.scale_log2, -m_run[j]));
+        float wmax = fmaxf(fmaxf(w[0], w[1]), w[2]);
+#pragma unroll
+        for (int e = 3; e < 16; e += 2) wmax = fmaxf(wmax, fmaxf(w[e], w[e + 1]));
+        if (__any(wmax > F_WMAX)) {
+          float pmax = fmaxf(S[j][0], S[j][1]);
+#pragma unroll
+          for (int e = 2; e < 16; e += 2) pmax = fmaxf(pmax, fmaxf(S[j][e], S[j][e + 1]));
           int ln = lane;
           asm volatile("" : "+v"(ln));
-          bmax = fmaxf(bmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(bmax))));
-        }
-        // every token sees key 0 in its first step, so m_new is finite
-        // (a fully masked block of a later step keeps m_run)
-        const float m_new = fmaxf(m_run[j], bmax * a.scale_log2);
-        // rescale what was accumulated when the max moved
-        if (__any(m_new > m_run[j])) {
-          const float al = __builtin_amdgcn_exp2f(m_run[j] - m_new);   // m_run = -inf: 0
+          const float bmax =
+              fmaxf(pmax, __int_as_float(__builtin_amdgcn_ds_bpermute(((ln & 63) ^ 32) << 2, __float_as_int(pmax))));
+          const float m_new = fmaxf(m_run[j], bmax * a.scale_log2);
+          const float al = __builtin_amdgcn_exp2f(m_run[j] - m_new);
           l_run[j] *= al;
 #pragma unroll
           for (int cb = 0; cb < PD_V / 32; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) O[j][cb][e] *= al;
-        }
-        m_run[j] = m_new;
+          m_run[j] = m_new;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          P[j][e >> 3][e & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(S[j][e], a.scale_log2, -m_new));
+          for (int e = 0; e < 16; ++e) w[e] = __builtin_amdgcn_exp2f(fmaf(S[j][e], a.scale_log2, -m_new));
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) P[j][e >> 3][e & 7] = (_Float16)w[e];
         // l sums the same fp16 weights, two per dot instruction
         const halfx2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
