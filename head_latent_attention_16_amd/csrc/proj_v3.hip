@@ -202,110 +202,96 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
 }
 
 // ---------------------------------------------------------------------------
-// uv: one workgroup per (head, 32-row block of W_UV); it keeps its 32 x 512
-// weight block in registers and walks the batch in blocks of 32.  The four
-// waves split the 512-long contraction (wave w: columns 128 w .. +128) and
-// add their partial sums through LDS.
+// uv: one workgroup per (head, block of 32 batch rows).  Wave w owns the
+// head's value rows 32 w .. +32 over the whole 512-long contraction, with
+// its 32 x 512 block of W_UV in registers; the block's 32 o_lat rows are read
+// once by the workgroup (whole rows, 4 KiB per workgroup instruction), split
+// into bf16 hi and lo planes in LDS, and read by all four waves, so no
+// partial sums cross waves and each o_lat byte leaves L2 once.
 //   o^T[v x batch] = W_UV[h][v x c] . o_lat^T[c x batch]   (32x32x16)
 // o_lat is fp32; it enters the bf16 product as hi + lo with hi = bf16(x) and
 // lo = bf16(x - hi), two MFMAs per step, so the result keeps about 16
 // significant bits of o_lat instead of the 8 a single bf16 rounding leaves.
-// Each wave loads its 128 columns of the block's 32 o_lat rows with whole
-// 512-byte row pieces (two rows per wave instruction), splits them into hi
-// and lo planes in its own LDS region, and reads the MFMA fragments from
-// there; the next block's loads are in flight during the current block's
-// MFMAs.  Plane rows are 256 bytes, 16-byte chunk c of row r stored at
+// Plane rows are 1 KiB; the 16-byte chunk c of row r is stored at
 // c ^ (r % 16), so 16 rows at one chunk hit 16 distinct bank groups.
+// (The previous layout, four workgroups per head splitting W_UV's rows and
+// each reading every o_lat row of the head, took 12.9 us at B = 64: the
+// o_lat reads from L2 were four times the bytes.)
 // ---------------------------------------------------------------------------
-constexpr int UV_KS = DC / 16 / 4;   // 8 k-steps per wave
-constexpr int UV_COLS = DC / 4;      // 128 columns per wave
-constexpr int UV_ROWB = UV_COLS * 2; // 256 bytes per plane row
-constexpr int UV_PLANE = 32 * UV_ROWB;   // 8 KiB
+constexpr int UV_KS = DC / 16;            // 32 k-steps
+constexpr int UV_ROWB = DC * 2;           // 1024 bytes per plane row
+constexpr int UV_PLANE = 32 * UV_ROWB;    // 32 KiB
+constexpr int UV_SMALL_B = 32;   // batches up to this use two workgroups per head
 
-__global__ void __launch_bounds__(256) k_uv_v3(int B, const float* __restrict__ o_lat,
-                                               const __bf16* __restrict__ W_UV,
-                                               float* __restrict__ o, __bf16* __restrict__ ob) {
-  __shared__ floatx16 red[3][64];
-  __shared__ __attribute__((aligned(16))) char xs[4][2][UV_PLANE];   // [wave][hi, lo]
-  const int h = blockIdx.x, vb = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g32 = lane >> 5;
-  const int v = 32 * vb + (lane & 31);
-  const __bf16* wrow = W_UV + ((size_t)h * DV + v) * DC;
+template <int VW>   // waves per workgroup: value rows 32 VW (blockIdx.x % (4 / VW)) .. of head blockIdx.x / (4 / VW)
+__global__ void __launch_bounds__(64 * VW) k_uv_v3(int B, const float* __restrict__ o_lat,
+                                                   const __bf16* __restrict__ W_UV,
+                                                   float* __restrict__ o, __bf16* __restrict__ ob) {
+  constexpr int NT = 64 * VW, NL = 4096 / NT;   // threads, o_lat loads per thread
+  __shared__ __attribute__((aligned(16))) char xs[2][UV_PLANE];   // [hi, lo]
+  const int h = blockIdx.x / (4 / VW), b0 = 32 * blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5, n32 = lane & 31;
+  const int wave = (blockIdx.x % (4 / VW)) * VW + (tid >> 6);   // value rows 32 wave .. +32
+
+  // o_lat: load i of thread t is float4 number f = NT i + t of the block,
+  // row f / 128 (clamped to the last batch row), columns 4 (f % 128) .. +4
+  floatx4 xl[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int f = NT * i + tid;
+    const int bq = min(b0 + (f >> 7), B - 1);
+    xl[i] = *(const floatx4*)(o_lat + ((size_t)bq * NH + h) * DC + 4 * (f & 127));
+  }
+  // the wave's W_UV rows: lane n32 holds row 32 w + n32, k = 16 j + 8 g32 .. +8
+  const __bf16* wrow = W_UV + ((size_t)h * DV + 32 * wave + n32) * DC + 8 * g32;
   bf16x8 aw[UV_KS];
 #pragma unroll
-  for (int j = 0; j < UV_KS; ++j) aw[j] = *(const bf16x8*)(wrow + 16 * (wave * UV_KS + j) + 8 * g32);
+  for (int j = 0; j < UV_KS; ++j) aw[j] = *(const bf16x8*)(wrow + 16 * j);
 
-  // load i of a block: row 2 i + g32 of the block, columns 128 wave + 4 q .. +4
-  const int q = lane & 31;
-  floatx4 xl[16];
-  auto load_block = [&](int nb) {
+  MLA_LDS char* hp = (MLA_LDS char*)xs[0];
+  MLA_LDS char* lp = (MLA_LDS char*)xs[1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int bq = 32 * nb + 2 * i + g32;
-      xl[i] = bq < B ? *(const floatx4*)(o_lat + ((size_t)bq * NH + h) * DC + UV_COLS * wave + 4 * q)
-                     : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NL; ++i) {
+    const int f = NT * i + tid;
+    const int r = f >> 7, q = f & 127;   // columns 4 q .. +4: chunk q / 2, half q % 2
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (__bf16)xl[i][e];
+      lo[e] = (__bf16)(xl[i][e] - (float)hi[e]);
     }
-  };
-  MLA_LDS char* hp = (MLA_LDS char*)xs[wave][0];
-  MLA_LDS char* lp = (MLA_LDS char*)xs[wave][1];
-  auto stage_block = [&]() {
+    const int off = r * UV_ROWB + ((((q >> 1) ^ (r & 15)) << 4) | ((q & 1) << 3));
+    *(MLA_LDS bf16x4*)(hp + off) = hi;
+    *(MLA_LDS bf16x4*)(lp + off) = lo;
+  }
+  __syncthreads();
+
+  floatx16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 2 * i + g32;
-      bf16x4 hi, lo;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)xl[i][e];
-        lo[e] = (__bf16)(xl[i][e] - (float)hi[e]);
-      }
-      // columns 4 q .. +4: 16-byte chunk q / 2, half q % 2
-      const int off = r * UV_ROWB + ((((q >> 1) ^ (r & 15)) << 4) | ((q & 1) << 3));
-      *(MLA_LDS bf16x4*)(hp + off) = hi;
-      *(MLA_LDS bf16x4*)(lp + off) = lo;
-    }
-  };
-  load_block(0);
-  const int br = lane & 31;   // B-fragment row (batch row of the block)
-  for (int nb = 0; nb * 32 < B; ++nb) {
-    stage_block();   // the wave's own region: its previous fragment reads came first
-    if ((nb + 1) * 32 < B) load_block(nb + 1);
-    const int bq = 32 * nb + br;
-    floatx16 acc;
+  for (int j = 0; j < UV_KS; ++j) {
+    // B fragment: batch row n32 of the block, k = 16 j + 8 g32 .. +8 (chunk 2 j + g32)
+    const int off = n32 * UV_ROWB + (((2 * j + g32) ^ (n32 & 15)) << 4);
+    const bf16x8 hi = *(const MLA_LDS bf16x8*)(hp + off);
+    const bf16x8 lo = *(const MLA_LDS bf16x8*)(lp + off);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], lo, acc, 0, 0, 0);
+  }
+  // lane: batch row b0 + n32, value rows v = 32 w + 8 (i/4) + 4 g32 + i%4
+  const int bq = b0 + n32;
+  if (bq >= B) return;
+  const size_t at = ((size_t)bq * NH + h) * DV + 32 * wave + 4 * g32;
+  if (o) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(floatx4*)(o + at + 8 * q4) = floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+  }
+  if (ob) {
 #pragma unroll
-    for (int j = 0; j < UV_KS; ++j) {
-      // k = 16 j + 8 g32 .. +8 of the wave's columns: chunk 2 j + g32
-      const int off = br * UV_ROWB + (((2 * j + g32) ^ (br & 15)) << 4);
-      const bf16x8 hi = *(const MLA_LDS bf16x8*)(hp + off);
-      const bf16x8 lo = *(const MLA_LDS bf16x8*)(lp + off);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], hi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], lo, acc, 0, 0, 0);
-    }
-    if (wave > 0) red[wave - 1][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int w2 = 0; w2 < 3; ++w2) {
-        const floatx16 r = red[w2][lane];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += r[i];
-      }
-      // lane: batch bq, rows v = 32 vb + 8 (i/4) + 4 g32 + i%4
-      const size_t at = ((size_t)bq * NH + h) * DV + 32 * vb + 4 * g32;
-      if (bq < B && o) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(floatx4*)(o + at + 8 * q4) = floatx4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
-      }
-      if (bq < B && ob) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(bf16x4*)(ob + at + 8 * q4) = bf16x4{(__bf16)acc[4 * q4], (__bf16)acc[4 * q4 + 1],
-                                                (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
-      }
-    }
-    __syncthreads();
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(bf16x4*)(ob + at + 8 * q4) = bf16x4{(__bf16)acc[4 * q4], (__bf16)acc[4 * q4 + 1],
+                                            (__bf16)acc[4 * q4 + 2], (__bf16)acc[4 * q4 + 3]};
   }
 }
 
@@ -329,7 +315,10 @@ hipError_t launch_absorb_v3(const Shape& s, int B, const void* q, bool q_f32, co
 
 hipError_t launch_uv_v3(const Shape&, int B, const float* o_lat, const void* W_UV, float* o, void* ob,
                         hipStream_t st) {
-  k_uv_v3<<<dim3(NH, DV / 32), 256, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o, (__bf16*)ob);
+  if (B <= UV_SMALL_B)
+    k_uv_v3<2><<<dim3(2 * NH, (B + 31) / 32), 128, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o, (__bf16*)ob);
+  else
+    k_uv_v3<4><<<dim3(NH, (B + 31) / 32), 256, 0, st>>>(B, o_lat, (const __bf16*)W_UV, o, (__bf16*)ob);
   return hipGetLastError();
 }
 
