@@ -37,12 +37,11 @@ constexpr int ABS_THREADS = 256;
 constexpr int ABS_WPT = DH * ABS_COLS / 8 / ABS_THREADS;   // 16-byte weight pieces per thread
 constexpr int ABS_QROWB = DH * 2 + 16;                      // staged query row (bf16) + pad
 
-// cos and sin of pos * base^(-2i/d_r): the angle is formed in double and
-// reduced modulo 2 pi in double (2 pi as a sum of two doubles), and the
-// reduced angle, at most pi in magnitude, goes to single-precision sincos.
-__device__ __forceinline__ void rope_cs_reduced(int64_t pos, int i, int d_r, double log2_base, float* c,
-                                                float* s) {
-  const double theta = exp2(-2.0 * (double)i / (double)d_r * log2_base);
+// cos and sin of pos * theta, theta = base^(-2i/d_r): the angle is formed
+// in double and reduced modulo 2 pi in double (2 pi as a sum of two
+// doubles), and the reduced angle, at most pi in magnitude, goes to
+// single-precision sincos.
+__device__ __forceinline__ void rope_cs_reduced(int64_t pos, double theta, float* c, float* s) {
   const double ang = (double)pos * theta;
   const double k = rint(ang * 0.15915494309189535);   // 1 / (2 pi)
   double r = fma(-k, 6.283185307179586, ang);
@@ -124,24 +123,41 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
   load_q(0);
 
   // RoPE on the decoupled part: q_pe = rotate(q^R, pos[b]), pairs 8 qt .. +8.
+  // Item idx = (batch row idx / 8, pair 8 qt + idx % 8); a thread's items
+  // all have pair 8 qt + tid % 8, and the loads of RP items are issued
+  // before any of them is used (B = 64: 10.4 -> 10.0 us).
   {
-    const double log2_base = log2(rope_base);
-    for (int idx = tid; idx < B * 8; idx += ABS_THREADS) {
-      const int b = idx >> 3, i = 8 * qt + (idx & 7);
-      const size_t e0 = ((size_t)b * NH + h) * QW + DH;
-      float lo, hi;
-      if constexpr (QF32) {
-        lo = ((const float*)qv)[e0 + i];
-        hi = ((const float*)qv)[e0 + DR / 2 + i];
-      } else {
-        lo = (float)((const __bf16*)qv)[e0 + i];
-        hi = (float)((const __bf16*)qv)[e0 + DR / 2 + i];
+    static_assert(ABS_THREADS % 8 == 0, "one pair per thread");
+    constexpr int RP = 4;
+    const int i = 8 * qt + (tid & 7);
+    const double theta = exp2(-2.0 * (double)i / (double)DR * log2(rope_base));
+    for (int base = 0; base < B * 8; base += RP * ABS_THREADS) {
+      float lo[RP], hi[RP];
+      int64_t pb[RP];
+#pragma unroll
+      for (int u = 0; u < RP; ++u) {
+        const int idx = base + u * ABS_THREADS + tid;
+        const int b = min(idx >> 3, B - 1);
+        const size_t e0 = ((size_t)b * NH + h) * QW + DH;
+        if constexpr (QF32) {
+          lo[u] = ((const float*)qv)[e0 + i];
+          hi[u] = ((const float*)qv)[e0 + DR / 2 + i];
+        } else {
+          lo[u] = (float)((const __bf16*)qv)[e0 + i];
+          hi[u] = (float)((const __bf16*)qv)[e0 + DR / 2 + i];
+        }
+        pb[u] = pos[b];
       }
-      float cs, sn;
-      rope_cs_reduced(pos[b], i, DR, log2_base, &cs, &sn);
-      __bf16* out = q_pe + ((size_t)b * NH + h) * DR;
-      out[i] = (__bf16)(lo * cs - hi * sn);
-      out[DR / 2 + i] = (__bf16)(hi * cs + lo * sn);
+#pragma unroll
+      for (int u = 0; u < RP; ++u) {
+        const int idx = base + u * ABS_THREADS + tid;
+        if (idx >= B * 8) break;
+        float cs, sn;
+        rope_cs_reduced(pb[u], theta, &cs, &sn);
+        __bf16* out = q_pe + ((size_t)(idx >> 3) * NH + h) * DR;
+        out[i] = (__bf16)(lo[u] * cs - hi[u] * sn);
+        out[DR / 2 + i] = (__bf16)(hi[u] * cs + lo[u] * sn);
+      }
     }
   }
 
