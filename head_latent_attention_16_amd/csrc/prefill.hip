@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(256, 1) k_upproj(int rows, const __bf16* __res
 // Causal flash attention over the explicit keys and values.
 // Key block stage: K [64 x 192] (rows of 384 B, 24 chunks; chunk c of row r at
 // c ^ ((r >> 1) & 7)) then V [64 x 128] (rows of 256 B, 16 chunks; chunk c of
-// row r at c ^ (4 (r & 3))).  40 KiB = 10 DMAs per wave; two stages.
+// row r at c ^ (4 (r & 3))).  40 KiB = 5 DMAs per wave of eight; three stages.
 // ---------------------------------------------------------------------------
 constexpr int F_WAVES = 8;                // waves per workgroup
 constexpr int F_TB = 1;                   // 32-token blocks per wave
