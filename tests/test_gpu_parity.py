@@ -74,6 +74,25 @@ def test_v3_attention_small(lens):
                 norm_max=1e-2, norm_mean=2e-3)
 
 
+@pytest.mark.parametrize("B", [31, 32, 33, 65])
+def test_project_out_batch_blocks(B):
+    """W_UV at batch sizes around the up-projection kernel's switch from two
+    workgroups of two waves per head (B <= 32) to one of four waves per
+    32-row batch block, with a partial last block: o against the fp64
+    definition o[b,h] = W_UV[h] o_lat[b,h] for every (row, head)."""
+    w = small_v3([1] * B, seed=B)
+    u = Uploaded(w)
+    say(f"project_out: B={B}")
+    rng = np.random.default_rng(100 + B)
+    o_lat = rng.standard_normal((B, 128, 512)).astype(np.float32)
+    o = torch.empty(B, 128, 128, dtype=torch.float32, device="cuda")
+    L.project_out(u.dims, dev(o_lat), u.W["W_UV"], o=o)
+    torch.cuda.synchronize()
+    ref, _ = O.project_out(o_lat, w.f64(w.W["W_UV"]))
+    # o_lat enters as bf16 hi + lo (about 16 significant bits), fp32 sums
+    compare(host_f64(o), ref, f"B={B} o", max_abs=1e-3, mean_abs=1e-4, norm_max=1e-3, norm_mean=1e-4)
+
+
 def test_absorb_query_v3():
     """q_lat = W_UK^T q_C within one bf16 rounding; q_pe = RoPE(q_R, pos)."""
     w = small_v3([5, 9, 1000])
