@@ -1659,105 +1659,145 @@ __device__ void recompute_head(const CombineArgs& a, int b, int h, int len) {
 // own head itself: with the common max M of the pieces' m, piece i weighs
 // 2^(m_i - M) l_i.  Pieces over empty ranges carry m = -inf, l = 0 and zero
 // rows.  The result is transposed through LDS so that every head's 32
-// columns leave as one 128-byte store.  CPW > 1 (short sequences spanning
-// few pieces) gives each workgroup more loads in flight.
+// columns leave as one 128-byte store.  The combine is bound by the latency
+// of its partial loads, not by their bytes: a sequence of up to 16 pieces
+// has the loads of several column blocks (a "round", up to CMB_MAXLD
+// 8-byte loads per lane) issued together, and a round's results leave
+// through LDS behind one barrier.  Sequences of more than 16 pieces take a
+// grouped loop over the pieces instead (cmb_large).
 constexpr int CMB_HB = HPW;          // heads per block (one split-kernel wave)
 constexpr int CMB_CB = 32;           // columns per block (one accumulator tile)
 constexpr int CMB_NCB = DC / CMB_CB;
 constexpr size_t CMB_SLOT = (size_t)NH * DC;   // fp16 per slot
+constexpr size_t CMB_CHUNK = (size_t)CMB_HB * CMB_CB;   // fp16 per (piece, head block, column block)
+constexpr int CMB_MAXLD = 32;        // partial loads per lane in one round
+constexpr int CMB_MAXCG = 8;         // column blocks per round
+constexpr int CMB_ROW = CMB_MAXCG * CMB_CB + 1;   // LDS row of the transpose (odd: no bank conflicts)
 
-// Writes the normalised 32 x 32 block through LDS (lane t: head t / 8,
-// columns 4 (t % 8) ..+4 of the block).
-__device__ __forceinline__ void cmb_store(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb,
-                                          int cb, const float4& acc, float inv) {
+// Writes CG normalised 32 x 32 blocks (column blocks cb .. cb + CG - 1)
+// through LDS: lane t holds head t % 32, columns 8 (t / 64) + 4 ((t / 32) % 2)
+// ..+4 of each block; every head's CG 32 consecutive columns are written as
+// 16-byte pieces, eight lanes per 128 bytes.
+template <int CG>
+__device__ __forceinline__ void cmb_store(const CombineArgs& a, float (*s_out)[CMB_ROW], int b, int hb, int cb,
+                                          const float4 (&acc)[CG], float inv) {
   const int tid = threadIdx.x;
   const int n32 = tid & 31, cols = 8 * (tid >> 6) + 4 * ((tid >> 5) & 1);
-  s_out[n32][cols + 0] = acc.x * inv;
-  s_out[n32][cols + 1] = acc.y * inv;
-  s_out[n32][cols + 2] = acc.z * inv;
-  s_out[n32][cols + 3] = acc.w * inv;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    s_out[n32][CMB_CB * c + cols + 0] = acc[c].x * inv;
+    s_out[n32][CMB_CB * c + cols + 1] = acc[c].y * inv;
+    s_out[n32][CMB_CB * c + cols + 2] = acc[c].z * inv;
+    s_out[n32][CMB_CB * c + cols + 3] = acc[c].w * inv;
+  }
   __syncthreads();
   const int h_r = tid >> 3, c_r = (tid & 7) * 4;
-  float4* out = (float4*)(a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r);
-  *out = make_float4(s_out[h_r][c_r], s_out[h_r][c_r + 1], s_out[h_r][c_r + 2], s_out[h_r][c_r + 3]);
-  __syncthreads();   // s_out is reused by the next column block
+  float* row = a.o_lat + ((size_t)b * NH + hb * CMB_HB + h_r) * DC + cb * CMB_CB + c_r;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const float* sv = &s_out[h_r][CMB_CB * c + c_r];
+    *(float4*)(row + CMB_CB * c) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+  }
+  __syncthreads();   // s_out is reused by the next round
 }
 
-// Up to NP pieces: the (m, l) of all pieces and the entries of the first
-// column block are loaded together (cmb_small_load, issued before the
-// fallback flags are examined, so both share one round trip), the weights
-// are kept in registers (cmb_small_finish).
-template <int NP>
-struct SmallLoad {
-  float2 m2[NP];
-  halfx4 v[NP];
-};
+// Loads of one round: column blocks cb .. cb + CG - 1 of every piece (piece
+// indices past the last are clamped to it; their weight is 0).
+template <int NP, int CG>
+__device__ __forceinline__ void cmb_round_load(const _Float16* po, int cb, int npiece, halfx4 (&v)[CG][NP]) {
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int k = i < npiece ? i : npiece - 1;
+      v[c][i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)(cb + c) * CMB_CHUNK);
+    }
+}
 
-template <int NP>
-__device__ __forceinline__ void cmb_small_load(const CombineArgs& a, int hb, int cb0, int npiece,
-                                               size_t slot0, SmallLoad<NP>& d) {
+// Up to NP pieces, CG column blocks per round.  The (m, l) of all pieces and
+// the first round's partials are loaded before the fallback flags are
+// examined, so both share one round trip.  Returns 1 if the sequence must
+// take the fallback, 2 if one workgroup held it whole (the split kernel wrote
+// its result), else 0 with M, L of this lane's head.
+template <int NP, int CG>
+__device__ int cmb_small(const CombineArgs& a, float (*s_out)[CMB_ROW], int b, int hb, int cb0, int cpw,
+                         int npiece, size_t slot0, int flag, float& M, float& L) {
+  static_assert(NP * CG <= CMB_MAXLD && CG <= CMB_MAXCG, "round size");
   const int tid = threadIdx.x, n32 = tid & 31;
   const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
-  const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * (CMB_HB * CMB_CB) + 4 * tid;
+  const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * CMB_CHUNK + 4 * tid;
+  float2 m2[NP];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int k = i < npiece ? i : npiece - 1;   // clamped; weight 0 below
-    d.m2[i] = ml[(size_t)k * NH];
-    d.v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)cb0 * (CMB_HB * CMB_CB));
-  }
-}
-
-template <int NP>
-__device__ __forceinline__ void cmb_small_finish(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b,
-                                                 int hb, int cb0, int cpw, int npiece, size_t slot0,
-                                                 SmallLoad<NP>& d, float& M, float& L) {
-  const int tid = threadIdx.x;
-  const _Float16* po = a.part_o + slot0 * CMB_SLOT + (size_t)hb * CMB_NCB * (CMB_HB * CMB_CB) + 4 * tid;
+  for (int i = 0; i < NP; ++i) m2[i] = ml[(size_t)(i < npiece ? i : npiece - 1) * NH];
+  halfx4 v[CG][NP];
+  cmb_round_load<NP, CG>(po, cb0, npiece, v);
+  if (__syncthreads_or(flag)) return 1;
+  if (npiece == 1) return 2;
   float w[NP];
   M = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    if (i < npiece) M = fmaxf(M, d.m2[i].x);
+    if (i < npiece) M = fmaxf(M, m2[i].x);
   L = 0.f;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const bool use = i < npiece && d.m2[i].x != -INFINITY;
-    w[i] = use ? exp2f(d.m2[i].x - M) * d.m2[i].y : 0.f;   // 2^(m - M) l
+    const bool use = i < npiece && m2[i].x != -INFINITY;
+    w[i] = use ? exp2f(m2[i].x - M) * m2[i].y : 0.f;   // 2^(m - M) l
     L += w[i];
   }
   const float inv = 1.f / L;
-  for (int c = 0; c < cpw; ++c) {
-    if (c > 0) {
+  for (int r = 0; r < cpw; r += CG) {
+    if (r > 0) cmb_round_load<NP, CG>(po, cb0 + r, npiece, v);
+    float4 acc[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int k = i < npiece ? i : npiece - 1;
-        d.v[i] = *(const halfx4*)(po + (size_t)k * CMB_SLOT + (size_t)(cb0 + c) * (CMB_HB * CMB_CB));
+        acc[c].x += w[i] * (float)v[c][i][0];
+        acc[c].y += w[i] * (float)v[c][i][1];
+        acc[c].z += w[i] * (float)v[c][i][2];
+        acc[c].w += w[i] * (float)v[c][i][3];
       }
     }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      acc.x += w[i] * (float)d.v[i][0];
-      acc.y += w[i] * (float)d.v[i][1];
-      acc.z += w[i] * (float)d.v[i][2];
-      acc.w += w[i] * (float)d.v[i][3];
-    }
-    cmb_store(a, s_out, b, hb, cb0 + c, acc, inv);
+    cmb_store<CG>(a, s_out, b, hb, cb0 + r, acc, inv);
   }
+  return 0;
+}
+
+// The round size for NP pieces: as many of the workgroup's cpw column blocks
+// as CMB_MAXLD loads per lane allow, 16 for sequences of 9 to 16 pieces
+// (cpw and the round size are powers of two).  Measured per call (ragged
+// B = 64 / layer B = 128 / uniform B = 16, rounds of at most 16 or 32
+// loads): 16.7 / 18.1 / 8.7 and 15.4 / 17.1 / 9.1 us, against 19.0 / 22.7 /
+// 8.4 with one column block per round; more than 16 pieces (long B = 8)
+// went from 11.6 to 12.0 us in one round of 32 and take the grouped loop.
+template <int NP>
+__device__ int cmb_small_any(const CombineArgs& a, float (*s_out)[CMB_ROW], int b, int hb, int cb0, int cpw,
+                             int npiece, size_t slot0, int flag, float& M, float& L) {
+  constexpr int LD = NP >= 16 ? 16 : CMB_MAXLD;
+  constexpr int MAXCG = LD / NP < CMB_MAXCG ? LD / NP : CMB_MAXCG;
+  const int cg = cpw < MAXCG ? cpw : MAXCG;
+  if constexpr (MAXCG >= 8)
+    if (cg == 8) return cmb_small<NP, 8>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  if constexpr (MAXCG >= 4)
+    if (cg == 4) return cmb_small<NP, 4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  if constexpr (MAXCG >= 2)
+    if (cg == 2) return cmb_small<NP, 2>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  return cmb_small<NP, 1>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
 }
 
 // Any number of pieces: one pass per column block, 16 pieces at a time,
 // the running max M moving only between groups (rescaling what was
 // accumulated so far).
-__device__ void cmb_large(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int b, int hb, int cb0, int cpw,
+__device__ void cmb_large(const CombineArgs& a, float (*s_out)[CMB_ROW], int b, int hb, int cb0, int cpw,
                           int npiece, size_t slot0, float& M, float& L) {
   const int tid = threadIdx.x, n32 = tid & 31;
   const float2* ml = (const float2*)a.part_ml + slot0 * NH + hb * CMB_HB + n32;
   constexpr int GRP = 16;
   for (int c = 0; c < cpw; ++c) {
-    const _Float16* po =
-        a.part_o + slot0 * CMB_SLOT + ((size_t)hb * CMB_NCB + cb0 + c) * (CMB_HB * CMB_CB) + 4 * tid;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const _Float16* po = a.part_o + slot0 * CMB_SLOT + ((size_t)hb * CMB_NCB + cb0 + c) * CMB_CHUNK + 4 * tid;
+    float4 acc[1] = {make_float4(0.f, 0.f, 0.f, 0.f)};
     M = -INFINITY;
     L = 0.f;
     for (int i = 0; i < npiece; i += GRP) {
@@ -1775,10 +1815,10 @@ __device__ void cmb_large(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int 
         if (i + j < npiece) Mg = fmaxf(Mg, m2[j].x);
       if (Mg > M) {   // M = -inf only before any finite piece: nothing to rescale
         const float r = M == -INFINITY ? 0.f : exp2f(M - Mg);
-        acc.x *= r;
-        acc.y *= r;
-        acc.z *= r;
-        acc.w *= r;
+        acc[0].x *= r;
+        acc[0].y *= r;
+        acc[0].z *= r;
+        acc[0].w *= r;
         L *= r;
         M = Mg;
       }
@@ -1787,18 +1827,18 @@ __device__ void cmb_large(const CombineArgs& a, float (*s_out)[CMB_CB + 1], int 
         const bool use = i + j < npiece && m2[j].x != -INFINITY;
         const float w = use ? exp2f(m2[j].x - M) * m2[j].y : 0.f;   // 2^(m - M) l
         L += w;
-        acc.x += w * (float)v[j][0];
-        acc.y += w * (float)v[j][1];
-        acc.z += w * (float)v[j][2];
-        acc.w += w * (float)v[j][3];
+        acc[0].x += w * (float)v[j][0];
+        acc[0].y += w * (float)v[j][1];
+        acc[0].z += w * (float)v[j][2];
+        acc[0].w += w * (float)v[j][3];
       }
     }
-    cmb_store(a, s_out, b, hb, cb0 + c, acc, 1.f / L);
+    cmb_store<1>(a, s_out, b, hb, cb0 + c, acc, 1.f / L);
   }
 }
 
 __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
-  __shared__ float s_out[CMB_HB][CMB_CB + 1];
+  __shared__ float s_out[CMB_HB][CMB_ROW];
   const int cpw = a.cpw;
   const int ngrp = CMB_NCB / cpw;
   const int hb = blockIdx.x / ngrp, cb0 = (blockIdx.x % ngrp) * cpw, b = blockIdx.y;
@@ -1835,21 +1875,17 @@ __global__ void __launch_bounds__(CMB_THREADS) k_combine(CombineArgs a) {
     for (int k = blockIdx.x % ngrp; k < CMB_HB; k += ngrp) recompute_head(a, b, hb * CMB_HB + k, si.z);
   };
   float M, L;
-  if (npiece <= 4) {
-    SmallLoad<4> d;
-    cmb_small_load<4>(a, hb, cb0, npiece, slot0, d);
-    if (__syncthreads_or(flag)) return fallback();
-    if (npiece == 1) return;   // one workgroup held the whole sequence and wrote it
-    cmb_small_finish<4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, d, M, L);
-  } else if (npiece <= 16) {
-    SmallLoad<16> d;
-    cmb_small_load<16>(a, hb, cb0, npiece, slot0, d);
-    if (__syncthreads_or(flag)) return fallback();
-    cmb_small_finish<16>(a, s_out, b, hb, cb0, cpw, npiece, slot0, d, M, L);
-  } else {
-    if (__syncthreads_or(flag)) return fallback();
-    cmb_large(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
+  int r;
+  if (npiece <= 2) r = cmb_small_any<2>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  else if (npiece <= 4) r = cmb_small_any<4>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  else if (npiece <= 8) r = cmb_small_any<8>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  else if (npiece <= 16) r = cmb_small_any<16>(a, s_out, b, hb, cb0, cpw, npiece, slot0, flag, M, L);
+  else {
+    r = __syncthreads_or(flag) ? 1 : 0;
+    if (r == 0) cmb_large(a, s_out, b, hb, cb0, cpw, npiece, slot0, M, L);
   }
+  if (r == 1) return fallback();
+  if (r == 2) return;   // one workgroup held the whole sequence and wrote it
   if (cb0 == 0 && tid < CMB_HB && a.lse) {
     // lanes 0..31 hold heads 0..31 (n32 = tid); M, L are per head
     a.lse[(size_t)b * NH + hb * CMB_HB + tid] = (M + log2f(L)) * kLn2;
