@@ -12,7 +12,7 @@ import oracle as O
 from head_latent_attention_16_amd import _lib as L
 from head_latent_attention_16_amd import inputs as I
 
-from gpu_support import Uploaded, compare, dev, host_f64, oracle_seq, run_attention, say
+from gpu_support import Uploaded, canaried_workspace, compare, dev, host_f64, oracle_seq, run_attention, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,41 @@ def test_decode_latent_definition(hint):
         ref, lse = O.latent_attention(w.f64(q_lat[b]), w.f64(q_pe[b]), rows[:, :512], rows[:, 512:], scale)
         compare(got[b], ref, f"b={b} T={lens[b]} o_lat")
         compare(glse[b], lse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
+
+
+@pytest.mark.parametrize("hint_scale", [0.125, 1, 4])
+def test_decode_piece_counts(hint_scale):
+    """Sequences of 40 to 9000 rows under three row hints, so that the split
+    kernel cuts them into anything from one piece to a few dozen, and the
+    combine merges them with one to sixteen 32-column blocks per workgroup:
+    several rounds of partial loads at two, four and eight pieces, one and
+    several rounds at sixteen, and the grouped loop past sixteen.  Every head of
+    every sequence against the latent definition; the workspace canaries
+    stay intact."""
+    lens = [40, 700, 1500, 3000, 6000, 9000]
+    w = small_v3(lens, seed=21)
+    rng = np.random.default_rng(22)
+    q_lat = I.bf16_bits(rng.standard_normal((w.B, 128, 512)).astype(np.float32) * 0.05)
+    q_pe = I.bf16_bits(rng.standard_normal((w.B, 128, 64)).astype(np.float32))
+    hint = max(1, int(w.total_rows * hint_scale))
+    say(f"decode-only piece counts lens={lens} hint={hint}")
+    u = Uploaded(w)
+    o_lat = torch.empty(w.B, 128, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.B, 128, dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws, check_canary = canaried_workspace(L.decode_attn_workspace(u.dims, w.B, hint))
+    L.decode_attn(u.dims, dev(q_lat), dev(q_pe), u.cache, u.offsets, u.lens, o_lat, lse,
+                  total_rows_hint=hint, err_flag=err, ws=ws)
+    torch.cuda.synchronize()
+    check_canary()
+    assert int(err.item()) == 0
+    got, glse = host_f64(o_lat), host_f64(lse)
+    scale = 1 / math.sqrt(192)
+    for b in range(w.B):
+        rows = w.f64(w.seq_rows(b))
+        ref, rlse = O.latent_attention(w.f64(q_lat[b]), w.f64(q_pe[b]), rows[:, :512], rows[:, 512:], scale)
+        compare(got[b], ref, f"b={b} T={lens[b]} o_lat")
+        compare(glse[b], rlse, f"b={b} lse", max_abs=1e-2, mean_abs=1e-3, norm_max=1e-2, norm_mean=1e-3)
 
 
 def test_decode_more_workgroups_than_rows():
