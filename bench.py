@@ -8,9 +8,11 @@ the largest attention-only workload that fits one GPU.
 A step is one pass of the decode hot path over one batch:
   attention-only workloads (uniform, ragged, long):
       mla_absorb_q (q given) -> mla_decode_attn -> mla_project_out (o)
-  layer workload: mla_absorb_q (from h_t) -> mla_append_cache (from h_t)
-      -> mla_decode_attn -> mla_project_out (o and u); with --norms the
-      _normed variants of the first two (latent norms on c^Q and c^KV)
+  layer workload: mla_absorb_q (from h_t) and mla_append_cache (from h_t),
+      the append on a second stream beside the query path (--one-stream:
+      one after the other), -> mla_decode_attn -> mla_project_out (o and u);
+      with --norms the _normed variants of the first two (latent norms on
+      c^Q and c^KV)
   causal workload (--n-q new tokens per sequence, the cache's last rows):
       mla_absorb_q (B n_q queries) -> mla_decode_attn_causal -> mla_project_out (o)
 Warmup steps replay the same step graphs back to back right before the
@@ -70,6 +72,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch each kernel from the host")
+    p.add_argument("--one-stream", action="store_true",
+                   help="layer workload: run the append on the same stream as the query path")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="first run one plain device-to-device copy of MIB MiB (a reference "
                         "for the HBM byte counters of a profiler run)")
@@ -299,6 +303,7 @@ def main():
         base[k] = dev(v)
     if layer:
         base["h_t"] = dev(w.h_t)
+        base["pos"] = dev(w.lens)   # the query position of each step (lens before its append)
     else:
         base["q"] = dev(np.ascontiguousarray(np.concatenate([w.q_C, w.q_R], -1)))
     per_copy = sum(t.numel() * t.element_size() for t in base.values())
@@ -342,22 +347,45 @@ def main():
     ws_prj = torch.empty(max(1, lib.mla_project_out_workspace(ctypes.byref(dims), B, int(layer))),
                          dtype=torch.uint8, device="cuda")
 
+    # Layer step: the latent append (W^DKV|W^KR, the row write and the length
+    # increment) does not depend on the query path (W^DQ, W^UQ, absorption),
+    # so it runs on a second stream, forked after the query positions are
+    # copied from the lengths and joined before the attention call.
+    side = torch.cuda.Stream() if layer and not args.one_stream else None
+
+    def append(s):
+        if args.norms:
+            L.append_cache_normed(dims, s["cache"], s["offsets"], s["lens"], 1, s["h_t"], s["W_DKV"],
+                                  s["kv_norm_w"], s["W_KR"], ws=ws_app)
+        else:
+            L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
+                           W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
+
     def step(c):
         """One pass of the hot path over input copy c (launches only)."""
         s = sets[c]
         if layer:
-            # query position = current length: the absorb runs before the
-            # append on the stream, so it reads lens before the increment
+            # query position = the length before this step's append
+            s["pos"].copy_(s["lens"])
+            if side is not None:
+                main = torch.cuda.current_stream()
+                forked = torch.cuda.Event()
+                forked.record(main)
+                side.wait_event(forked)
+                with torch.cuda.stream(side):
+                    append(s)
+                appended = torch.cuda.Event()
+                appended.record(side)
             if args.norms:
-                L.absorb_q_normed(dims, q_lat, q_pe, s["W_UK"], s["lens"], s["h_t"], s["W_DQ"], s["q_norm_w"],
+                L.absorb_q_normed(dims, q_lat, q_pe, s["W_UK"], s["pos"], s["h_t"], s["W_DQ"], s["q_norm_w"],
                                   s["W_UQ"], ws=ws_abs)
-                L.append_cache_normed(dims, s["cache"], s["offsets"], s["lens"], 1, s["h_t"], s["W_DKV"],
-                                      s["kv_norm_w"], s["W_KR"], ws=ws_app)
             else:
-                L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["lens"], h_t=s["h_t"], W_DQ=s["W_DQ"],
+                L.absorb_q(dims, q_lat, q_pe, s["W_UK"], s["pos"], h_t=s["h_t"], W_DQ=s["W_DQ"],
                            W_UQ=s["W_UQ"], ws=ws_abs)
-                L.append_cache(dims, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"],
-                               W_DKV=s["W_DKV"], W_KR=s["W_KR"], ws=ws_app)
+            if side is not None:
+                main.wait_event(appended)
+            else:
+                append(s)
         else:
             L.absorb_q(dims, q_lat, q_pe, s["W_UK"], tok_pos if n_q > 1 else s["lens"], q=s["q"])
         attend(s)
@@ -466,7 +494,8 @@ def main():
                    else "absorb_q+decode_attn_fp8+project_out(o)" if fp8
                    else "absorb_q+decode_attn+project_out(o)",
                    "input_copies_rotated": copies,
-                   "launch": "host launches" if args.no_graph else "one HIP graph per input copy"},
+                   "launch": ("host launches" if args.no_graph else "one HIP graph per input copy")
+                   + (", the append on a second stream" if side is not None else "")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name if name != "causal" else f"causal_nq{n_q}"),
                      "kernel": ("mla_decode_attn_causal" if n_q > 1 else "mla_decode_attn_paged" if paged

@@ -61,15 +61,18 @@ def test_attention_step_graph_replays_match_eager():
             assert torch.equal(out[k], ref[k]), (rep, k)
 
 
-def test_layer_step_graph_replays_match_eager():
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_layer_step_graph_replays_match_eager(two_streams):
     """Full layer step (query path, append, attention, projections): the graph
     and an eager twin advance identical state copies; after every replay the
-    outputs, the appended rows and the lengths agree bit for bit."""
+    outputs, the appended rows and the lengths agree bit for bit.  With
+    two_streams the graph runs the append on a second stream beside the
+    query path while the eager twin runs everything on one stream."""
     w = I.layer(seed=7, B=4, lo=20, hi=200, spare=8)
     d = dims_of(w)
     dd = w.dims
     B, n_h = w.B, dd["n_h"]
-    say("graph: layer step B=4, 3 replays")
+    say(f"graph: layer step B=4, 3 replays, two streams {two_streams}")
 
     def state():
         return dict(cache=dev(w.cache), offsets=dev(w.offsets), lens=dev(w.lens),
@@ -90,21 +93,38 @@ def test_layer_step_graph_replays_match_eager():
         b["hint"] = hint
         return b
 
-    def step(s, b):
-        s["pos"].copy_(s["lens"])
-        L.absorb_q(d, b["q_lat"], b["q_pe"], s["W_UK"], s["pos"], h_t=s["h_t"], W_DQ=s["W_DQ"],
-                   W_UQ=s["W_UQ"], ws=b["ws_abs"])
+    def append(s, b):
         L.append_cache(d, s["cache"], s["offsets"], s["lens"], 1, h_t=s["h_t"], W_DKV=s["W_DKV"],
                        W_KR=s["W_KR"], ws=b["ws_app"])
+
+    def step(s, b, side=None):
+        s["pos"].copy_(s["lens"])
+        if side is not None:
+            # the append on a second stream, forked after the positions are
+            # copied and joined before the attention call (as the benchmark runs it)
+            main = torch.cuda.current_stream()
+            forked = torch.cuda.Event()
+            forked.record(main)
+            side.wait_event(forked)
+            with torch.cuda.stream(side):
+                append(s, b)
+            appended = torch.cuda.Event()
+            appended.record(side)
+        L.absorb_q(d, b["q_lat"], b["q_pe"], s["W_UK"], s["pos"], h_t=s["h_t"], W_DQ=s["W_DQ"],
+                   W_UQ=s["W_UQ"], ws=b["ws_abs"])
+        if side is not None:
+            main.wait_event(appended)
+        else:
+            append(s, b)
         L.decode_attn(d, b["q_lat"], b["q_pe"], s["cache"], s["offsets"], s["lens"], b["o_lat"],
                       b["lse"], total_rows_hint=b["hint"], ws=b["ws"])
         L.project_out(d, b["o_lat"], s["W_UV"], o=b["o"], u=b["u"], W_O=s["W_O"], ws=b["ws_prj"])
 
-    se, be = state(), bufs()     # eager twin
+    se, be = state(), bufs()     # eager twin, one stream
     sg, bg = state(), bufs()     # graph
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-        step(sg, bg)
+        step(sg, bg, side=torch.cuda.Stream() if two_streams else None)
     for rep in range(3):
         step(se, be)
         torch.cuda.synchronize()
