@@ -157,7 +157,9 @@ def cpu_baseline(w, budget_s):
         b += 1
     dt = time.perf_counter() - t0
     per_token_heads = done_tokens / d["n_h"]        # cache-tokens with all heads processed
-    return {"value": per_token_heads / dt, "unit": "cache-tokens/s", "cores": int(threads),
+    rate = per_token_heads / dt
+    return {"value": rate, "unit": "cache-tokens/s", "cores": int(threads),
+            "extrapolated_full_workload_s": float(w.total_rows) / rate if rate > 0 else None,
             "kind": "oracle", "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "blas": blas,
             "sample": f"fp64 explicit route, {heads_done} (sequence, head) pairs over "
