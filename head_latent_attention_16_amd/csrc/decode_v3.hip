@@ -1090,6 +1090,11 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
 #pragma unroll
       for (int j = 0; j < QK_PF; ++j)
         kf[j] = *(const MLA_LDS bf16x8*)(T + qk_off[j & 3] + (j >> 2) * 128);
+      // (MFMA, load) pairs in program order, pinned by scheduling barriers:
+      // the MFMAs are asm statements, which the scheduler's instruction
+      // groups do not recognise, and without the barriers it sank every
+      // fragment load to just before its MFMA behind a full LDS wait.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         if (kk == 0)
@@ -1099,18 +1104,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
         const int nk = kk + QK_PF;
         if (nk < KSTEPS)
           kf[kk % QK_PF] = *(const MLA_LDS bf16x8*)(T + qk_off[nk & 3] + (nk >> 2) * 128);
+        __builtin_amdgcn_sched_barrier(0);
       }
       mfma_drain(S);
-    };
-    // Schedule of one QK block: QK_PF fragment loads, then (MFMA, load)
-    // pairs, then the remaining MFMAs.
-    auto qk_schedule = [&]() {
-      __builtin_amdgcn_sched_group_barrier(0x100, QK_PF, 0);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (kk < KSTEPS - QK_PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
     };
 
     // ---- softmax of one tile: lane holds head n32, rows 8 (i/4) + 4 g32 + i%4 ----
@@ -1249,7 +1245,6 @@ __global__ void __launch_bounds__(THREADS, 1) k_split(SplitArgs a) {
       qk8(0, S_cur);
     } else {
       qk(0, S_cur);
-      qk_schedule();
     }
     {
       float mloc = -INFINITY;

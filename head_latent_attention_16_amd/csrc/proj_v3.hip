@@ -235,6 +235,7 @@ __global__ void __launch_bounds__(ABS_THREADS) k_absorb_v3(int B, double rope_ba
 // o_lat reads from L2 were four times the bytes.)
 // ---------------------------------------------------------------------------
 constexpr int UV_KS = DC / 16;            // 32 k-steps
+constexpr int UV_PF = 4;                  // fragment steps read ahead
 constexpr int UV_ROWB = DC * 2;           // 1024 bytes per plane row
 constexpr int UV_PLANE = 32 * UV_ROWB;    // 32 KiB
 constexpr int UV_SMALL_B = 32;   // batches up to this use two workgroups per head
@@ -285,14 +286,27 @@ __global__ void __launch_bounds__(64 * VW) k_uv_v3(int B, const float* __restric
   floatx16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  // B fragment of step j: batch row n32 of the block, k = 16 j + 8 g32 .. +8
+  // (chunk 2 j + g32), hi and lo planes, read UV_PF steps ahead of their
+  // MFMAs (the scheduling barriers keep that order; left to itself the
+  // compiler read most fragments just before their MFMA behind a full wait)
+  auto frag_off = [&](int j) { return n32 * UV_ROWB + (((2 * j + g32) ^ (n32 & 15)) << 4); };
+  bf16x8 fh[UV_PF], fl[UV_PF];
+#pragma unroll
+  for (int j = 0; j < UV_PF; ++j) {
+    fh[j] = *(const MLA_LDS bf16x8*)(hp + frag_off(j));
+    fl[j] = *(const MLA_LDS bf16x8*)(lp + frag_off(j));
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < UV_KS; ++j) {
-    // B fragment: batch row n32 of the block, k = 16 j + 8 g32 .. +8 (chunk 2 j + g32)
-    const int off = n32 * UV_ROWB + (((2 * j + g32) ^ (n32 & 15)) << 4);
-    const bf16x8 hi = *(const MLA_LDS bf16x8*)(hp + off);
-    const bf16x8 lo = *(const MLA_LDS bf16x8*)(lp + off);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], fh[j % UV_PF], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[j], fl[j % UV_PF], acc, 0, 0, 0);
+    if (j + UV_PF < UV_KS) {
+      fh[j % UV_PF] = *(const MLA_LDS bf16x8*)(hp + frag_off(j + UV_PF));
+      fl[j % UV_PF] = *(const MLA_LDS bf16x8*)(lp + frag_off(j + UV_PF));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   // lane: batch row b0 + n32, value rows v = 32 w + 8 (i/4) + 4 g32 + i%4
   const int bq = b0 + n32;
