@@ -1978,11 +1978,14 @@ hipError_t launch_decode_v3(const Shape& s, int B_seq, int n_q, const void* q_la
   c.scale_log2 = a.scale_log2;
   // about G / B pieces per sequence: fewer pieces, more column blocks per
   // workgroup (CPW * pieces loads in flight per lane), but not so many that
-  // large batches lose workgroups.  Measured best (median of 160 calls, CPW
-  // 1..16): ragged B=64 (G/B = 4) at 8, layer B=128 (2) at 4, uniform B=16
-  // (16) at 2, long B=8 (32) at 1; the rule below picks each of them.
+  // large batches lose workgroups, and at most four since the loads of a
+  // workgroup's blocks are issued in rounds.  Measured (mean of 300 calls,
+  // this rule against halved and doubled thresholds): ragged B=64 (G/B = 4)
+  // 16.4 us at 4 against 17.4 at 8 and 26.1 at 16; layer B=128 (2) 17.4 at 4
+  // against 19.7 at 8; uniform B=16 (16) 8.7 at 2 against 9.9 at 1 and 9.5 at
+  // 4; long B=8 (32) 11.6 at 1 against 13.5 at 2.
   int cpw = 1;
-  while (cpw < CMB_NCB && cpw * G < 32 * B && cpw * B < 512) cpw *= 2;
+  while (cpw < 4 && cpw * G < 32 * B && cpw * B < 512) cpw *= 2;
   c.cpw = cpw;
   k_combine<<<dim3((NH / CMB_HB) * (CMB_NCB / cpw), B), CMB_THREADS, 0, st>>>(c);
   return hipGetLastError();

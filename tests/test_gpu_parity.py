@@ -164,9 +164,9 @@ def test_decode_latent_definition(hint):
 def test_decode_piece_counts(hint_scale):
     """Sequences of 40 to 9000 rows under three row hints, so that the split
     kernel cuts them into anything from one piece to a few dozen, and the
-    combine merges them with one to sixteen 32-column blocks per workgroup:
-    several rounds of partial loads at two, four and eight pieces, one and
-    several rounds at sixteen, and the grouped loop past sixteen.  Every head of
+    combine merges them with one to four 32-column blocks per workgroup:
+    rounds of partial loads at two, four and eight pieces, one and several
+    rounds at sixteen, and the grouped loop past sixteen.  Every head of
     every sequence against the latent definition; the workspace canaries
     stay intact."""
     lens = [40, 700, 1500, 3000, 6000, 9000]
