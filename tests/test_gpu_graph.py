@@ -61,18 +61,21 @@ def test_attention_step_graph_replays_match_eager():
             assert torch.equal(out[k], ref[k]), (rep, k)
 
 
-@pytest.mark.parametrize("two_streams", [False, True])
-def test_layer_step_graph_replays_match_eager(two_streams):
+@pytest.mark.parametrize("two_streams,B,lo,hi", [(False, 4, 20, 200), (True, 4, 20, 200),
+                                                 (True, 128, 512, 8192)])
+def test_layer_step_graph_replays_match_eager(two_streams, B, lo, hi):
     """Full layer step (query path, append, attention, projections): the graph
     and an eager twin advance identical state copies; after every replay the
     outputs, the appended rows and the lengths agree bit for bit.  With
     two_streams the graph runs the append on a second stream beside the
-    query path while the eager twin runs everything on one stream."""
-    w = I.layer(seed=7, B=4, lo=20, hi=200, spare=8)
+    query path while the eager twin runs everything on one stream; the
+    last case is the full-size layer workload (B = 128, T_prior in [512,
+    8192]), as the benchmark runs it."""
+    w = I.layer(seed=7, B=B, lo=lo, hi=hi, spare=8)
     d = dims_of(w)
     dd = w.dims
     B, n_h = w.B, dd["n_h"]
-    say(f"graph: layer step B=4, 3 replays, two streams {two_streams}")
+    say(f"graph: layer step B={B} T_prior in [{lo}, {hi}], 3 replays, two streams {two_streams}")
 
     def state():
         return dict(cache=dev(w.cache), offsets=dev(w.offsets), lens=dev(w.lens),
