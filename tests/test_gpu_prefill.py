@@ -113,6 +113,25 @@ def test_prefill_long_prompt():
                 norm_mean=1e-3)
 
 
+def test_prefill_benchmark_configuration():
+    """The configuration the benchmark times: four fresh 4096-token prompts,
+    every token new (n_q = T = 4096).  Sampled tokens (first, tile and block
+    edges, last) and heads of the first and last prompt against the
+    explicit route."""
+    c = _case([4096] * 4, 4096, seed=44)
+    say("prefill: B=4 fresh prompts of 4096 tokens (n_q=4096)")
+    o, lse, err = _run(c)
+    assert err == 0
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    heads = [5, 100]
+    toks = [0, 1, 31, 32, 255, 256, 2047, 4095]
+    for b in (0, 3):
+        ro, rl = _oracle(c, b, toks, heads)
+        compare(o[b][toks][:, heads], ro, f"bench config b={b} o")
+        compare(lse[b][toks][:, heads], rl, f"bench config b={b} lse", max_abs=1e-2, mean_abs=1e-3,
+                norm_max=1e-2, norm_mean=1e-3)
+
+
 def test_prefill_invalid_lengths():
     c = _case([100, 50], 60, seed=3, caps=[100, 80])   # sequence 1 has fewer rows than tokens
     o, lse, err = _run(c)
